@@ -1,0 +1,211 @@
+/*
+ * pkv.h -- C ABI of libpkv, a PagedAttention library for AMD Instinct MI355X (gfx950).
+ *
+ * Pages this header cites (title, then where on the page):
+ *   [Shootout]         "LLM Serving Engine Shootout: vLLM vs TensorRT-LLM vs SGLang vs llama.cpp"
+ *                      (initnode.dev), sections 1.1, 2.1, 3.1, 3.2, 5.1.
+ *   [Serving Engines]  "Serving Engines" (inference.tusharamrit.in), part "How vLLM works".
+ *   [Inference Engines] "Inference Engines: vLLM, SGLang, TensorRT-LLM" (ragyfied.com),
+ *                      parts "PagedAttention" and "Prefix caching".
+ *   [VRAM black hole]  zhichai.net topic 178634546 (Chinese original), section 1, the ASCII
+ *                      figure of logical blocks, block table and physical blocks.
+ *
+ * What the library computes
+ * -------------------------
+ * The KV cache of every sequence lives in fixed-size physical blocks of `block_size` tokens
+ * (16 or 32) drawn from one pool shared by all sequences [Shootout 3.1; Serving Engines].
+ * A per-sequence block table maps logical block i (tokens i*B .. i*B+B-1) to a physical block
+ * anywhere in the pool [Shootout 3.1; Inference Engines "PagedAttention"]. Token j of a
+ * sequence therefore sits in physical block table[j / B] at offset j % B: the equation in
+ * [Shootout 3.1] gives the block index, the figure in [VRAM black hole section 1] (tokens 0-15
+ * in physical block #7, tokens 16-31 in #2) gives the offset. The attention kernels locate K and
+ * V through the block table; new tokens are placed by a per-token slot index [Serving Engines].
+ *
+ * Pool layout (fixed by this ABI; the pages leave it open)
+ * ---------------------------------------------------------
+ *   k_pool: [num_blocks][num_kv_heads][block_size][head_dim]   (token-major inside a tile)
+ *   v_pool: [num_blocks][num_kv_heads][head_dim][block_size]   (dim-major inside a tile)
+ * Both row-major, element type `dtype`. One (block, kv_head) tile of either pool is one
+ * contiguous run of block_size*head_dim elements. The element for token offset `o`, head `h`,
+ * dimension `d` of physical block `b` is at
+ *   k_pool[((b*Hkv + h)*B + o)*D + d]      v_pool[((b*Hkv + h)*D + d)*B + o]
+ * (index arithmetic is done in 64-bit). V is stored dim-major because the P*V product contracts
+ * over tokens, and a matrix-core operand wants its contraction index contiguous per lane.
+ *
+ * A slot is the flat token position blk*B + off in the pool.
+ *
+ * Conventions for every call
+ * --------------------------
+ *  - All array pointers are DEVICE pointers owned by the caller. The library allocates no
+ *    device memory, keeps no device state between calls and never synchronises; each call
+ *    enqueues its kernels on `stream` (a hipStream_t passed as void*; NULL = null stream) and
+ *    returns. Calls are thread-safe.
+ *  - Return value: a pkv_status. Arguments are validated on the host before any HIP call; a
+ *    failure returns without launching anything. PKV_ERR_HIP reports a launch failure.
+ *    pkv_last_error() returns a thread-local text for the last non-OK status of the thread.
+ *  - dtype PKV_F32 or PKV_BF16 (bf16 = IEEE binary32 truncated to the top 16 bits).
+ *    head_dim in {64, 128}; block_size in {16, 32}; num_q_heads % num_kv_heads == 0.
+ *    Anything else returns PKV_ERR_UNSUPPORTED.
+ *  - Query head h uses KV head h / (num_q_heads / num_kv_heads) (consecutive grouping, GQA
+ *    [Shootout 2.1]).
+ *  - Device-array preconditions the host cannot check without a synchronisation, and which
+ *    the caller must guarantee (a violation is undefined behaviour):
+ *      block ids in block_table[s][0 .. ceil(context_lens[s]/B)-1] lie in [0, num_blocks);
+ *      0 <= context_lens[s] <= max_blocks_per_seq*B, and <= max_context_len when one is given;
+ *      non-negative slots in slot_mapping are < num_blocks*B and pairwise distinct.
+ *    Block-table entries past ceil(context_lens[s]/B) are never read.
+ *  - Sharing: several block tables may name the same physical block (shared prefixes,
+ *    [Inference Engines "PagedAttention"; Serving Engines]). The attention calls only read the
+ *    pools; writing into a shared block is the caller's error (fork it first).
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, inconsistent sizes */
+  PKV_ERR_UNSUPPORTED = 2, /* dtype / head_dim / block_size / grouping not built */
+  PKV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  PKV_ERR_HIP = 4          /* a HIP runtime call failed; see pkv_last_error() */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+/* Library plumbing (not defined by the pages). */
+int pkv_abi_version(void);
+const char* pkv_status_string(int status);
+const char* pkv_last_error(void);
+
+/*
+ * pkv_kv_cache_write -- scatter new K/V rows into pool slots through a slot mapping.
+ * [Serving Engines, "How vLLM works": the kernel works from a block table and a slot mapping;
+ *  a sequence claims a new block only when its current one is full.]
+ * [Inference Engines, "PagedAttention": blocks are allocated as the sequence grows.]
+ *
+ *   k_new, v_new  [T][num_kv_heads][head_dim], dtype        (read)
+ *   k_pool        [num_blocks][num_kv_heads][block_size][head_dim]  (written in place)
+ *   v_pool        [num_blocks][num_kv_heads][head_dim][block_size]  (written in place)
+ *   slot_mapping  int32 [T]; token i goes to slot slot_mapping[i] = blk*B + off; a negative
+ *                 slot skips the token.
+ * For every i with slot >= 0 and every head h, dimension d:
+ *   k_pool[blk][h][off][d] = k_new[i][h][d],  v_pool[blk][h][d][off] = v_new[i][h][d].
+ * A pure bit copy: no rounding, NaN payloads preserved. Slots not named are left untouched.
+ * T == 0 is a no-op that returns PKV_OK.
+ */
+int pkv_kv_cache_write(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                       const int32_t* slot_mapping, int T, int num_kv_heads, int head_dim,
+                       int block_size, int num_blocks, int dtype, void* stream);
+
+/*
+ * pkv_decode_partition_size -- the partition size, in tokens, that pkv_paged_attention_decode
+ * uses for `partition_size` (0 selects the library default). Library plumbing.
+ * Returns -1 for a partition_size that is negative or not a multiple of 16.
+ */
+int pkv_decode_partition_size(int partition_size, int num_seqs, int num_kv_heads,
+                              int max_context_len);
+
+/*
+ * pkv_decode_workspace_size -- bytes of device workspace pkv_paged_attention_decode needs for
+ * these sizes (0 when a single partition covers max_context_len, so no partials are stored).
+ * Library plumbing.
+ */
+size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                 int max_context_len, int partition_size);
+
+/*
+ * pkv_paged_attention_decode -- one query token per sequence against its paged context.
+ * [Shootout 3.1, the displayed equation: score A_ij = q_i . k_j / sqrt(d_head) with k_j fetched
+ *  via BlockTable[floor(j / B_size)].] [Shootout 5.1: softmax of the scores, then the product
+ *  with V.] [Shootout 2.1: grouped-query attention, fewer KV heads than query heads.]
+ *
+ * For sequence s with n = context_lens[s] (the count of cached tokens, including the current
+ * one, whose K/V must already be written) and query head h with KV head g:
+ *   a_j = scale * sum_d q[s][h][d] * K_s[g][j][d],     j = 0 .. n-1
+ *   out[s][h][:] = sum_j softmax(a)_j * V_s[g][j][:]
+ * where K_s, V_s are the sequence's K/V gathered through block_table (see above).
+ * n == 0 writes zeros.
+ *
+ *   out           [num_seqs][num_q_heads][head_dim], out_dtype (written)
+ *   q             [num_seqs][num_q_heads][head_dim], dtype
+ *   k_pool/v_pool pool layout above, dtype
+ *   block_table   int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens  int32 [num_seqs]
+ *   scale         normally 1/sqrt(head_dim)
+ *   max_context_len  host bound on context_lens (0 = max_blocks_per_seq*block_size)
+ *   partition_size   tokens per partition, a multiple of 16; 0 = library default.
+ *                    Contexts longer than one partition are split: each partition computes
+ *                    (max, sum of exponentials, normalised output) and a second kernel merges
+ *                    them with log-sum-exp weights. The result is the same softmax up to
+ *                    floating-point rounding.
+ *   workspace     device buffer of at least pkv_decode_workspace_size(...) bytes (may be NULL
+ *                 when that size is 0); contents on entry are ignored.
+ * out_dtype may differ from dtype (e.g. bf16 inputs with an fp32 output); the bf16 output is
+ * rounded to nearest even from the fp32 result.
+ */
+int pkv_paged_attention_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* block_table, const int32_t* context_lens,
+                               int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                               int block_size, int max_blocks_per_seq, int num_blocks,
+                               float scale, int max_context_len, int partition_size,
+                               void* workspace, size_t workspace_bytes, int dtype, int out_dtype,
+                               void* stream);
+
+/*
+ * pkv_paged_attention_prefill_chunk -- a causal chunk of query tokens against the paged cache.
+ * [Serving Engines, "How vLLM works": chunked prefill slices a long prompt into pieces that run
+ *  interleaved with other sequences' decode steps.] [Shootout 3.1 equation, as for decode.]
+ * [Shootout 3.2; Serving Engines: shared-prefix blocks are read through the block table like
+ *  any other block.]
+ *
+ * Sequence s owns query rows cu_q_lens[s] .. cu_q_lens[s+1]-1 (chunk length c = the
+ * difference) and n = context_lens[s] cached tokens, which INCLUDE the chunk's own K/V
+ * (written beforehand with pkv_kv_cache_write). The chunk follows r = n - c earlier tokens,
+ * so chunk row i sits at absolute position r + i and attends to tokens 0 .. r + i (the causal
+ * mask is aligned to the end of the context). Requires 0 <= c <= n for every sequence.
+ *
+ *   out          [total_q][num_q_heads][head_dim], out_dtype (written)
+ *   q            [total_q][num_q_heads][head_dim], dtype; sequences packed in order
+ *   cu_q_lens    int32 [num_seqs+1], cu_q_lens[0] = 0, non-decreasing, cu_q_lens[S] = total_q
+ *   context_lens int32 [num_seqs]
+ *   max_q_len, max_context_len  host bounds on c and n (0 = total_q and
+ *                               max_blocks_per_seq*block_size)
+ */
+int pkv_paged_attention_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
+                                      const int32_t* context_lens, const void* k_pool,
+                                      const void* v_pool, const int32_t* block_table,
+                                      int num_seqs, int total_q, int num_q_heads,
+                                      int num_kv_heads, int head_dim, int block_size,
+                                      int max_blocks_per_seq, int num_blocks, float scale,
+                                      int max_q_len, int max_context_len, int dtype,
+                                      int out_dtype, void* stream);
+
+/*
+ * Kernel timing (library plumbing, for benchmarks). When enabled, the library records a HIP
+ * event pair around every kernel it launches, on the stream it launches that kernel on, and
+ * accumulates the elapsed time per kernel name. pkv_profile_read synchronises on the recorded
+ * events. Off by default; enabling, resetting and reading are not thread-safe against
+ * concurrent launches.
+ *   pkv_profile_enable(1) turns it on (and clears), 0 turns it off.
+ *   pkv_profile_read(name, &total_ms, &launches): totals for kernel `name` since the last
+ *   enable/reset; returns PKV_ERR_INVALID_ARG for an unknown name.
+ *   pkv_profile_kernel_names(): the known kernel names, comma-separated.
+ */
+int pkv_profile_enable(int on);
+int pkv_profile_reset(void);
+int pkv_profile_read(const char* kernel_name, double* total_ms, long long* launches);
+const char* pkv_profile_kernel_names(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

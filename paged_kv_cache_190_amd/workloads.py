@@ -1,0 +1,245 @@
+"""Seeded synthetic workloads for the paged-attention calls.
+
+This module only builds inputs: context lengths, a block allocation, block tables, slot
+mappings, and pools of N(0, 1) values. It does none of the attention arithmetic, so the tests and
+the benchmark can hand the same arrays both to the HIP library and to the CPU oracle.
+
+Shapes follow the workloads the pages describe: Llama-3-style grouped-query decode with mixed
+context lengths, shared system-prompt prefixes, and chunked prefill ("LLM Serving Engine
+Shootout" 2.1 and 3.1; "Inference Engines: vLLM, SGLang, TensorRT-LLM", "PagedAttention" and
+"Prefix caching"; "Serving Engines", "How vLLM works"). No dataset, token or weight is involved.
+
+Array conventions are those of the C ABI: k_pool [NB][Hkv][B][D], v_pool [NB][Hkv][D][B];
+"bf16" arrays are uint16 bit patterns, "f32" arrays are float32.
+
+Allocation recipe (shared by every builder):
+  * blocks needed by a sequence of n tokens: ceil(n / B); a shared prefix of P tokens (P a
+    multiple of B) is P / B physical blocks named by every table;
+  * pool size NB = ceil(1.1 * distinct blocks) unless given;
+  * physical ids are handed out in order from one seeded permutation of range(NB), shared
+    prefix first, then sequence by sequence in logical order;
+  * block-table entries past a sequence's last block are -1;
+  * every slot that holds no token of any sequence is NaN (so a read of a stale slot shows up),
+    including the slots the new tokens will be written to.
+Random draws, in order, from numpy.random.default_rng(seed): the lengths (by the config
+functions), the permutation, the K pool, the V pool, q, the new K rows, the new V rows.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+BF16_NAN = np.uint16(0x7FC0)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns, rounding to nearest, ties to even (IEEE 754 rounding of
+    the 24-bit significand to 8 bits). NaN maps to the canonical quiet NaN 0x7FC0."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+    r[np.isnan(x)] = BF16_NAN
+    return r
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float32 (exact)."""
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclass
+class Workload:
+    """Inputs of one decode step or one prefill chunk, as host arrays."""
+    kind: str                      # "decode" or "prefill"
+    dtype: str                     # "f32" or "bf16"
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    max_blocks_per_seq: int
+    scale: float
+    q: np.ndarray                  # [S][Hq][D] or [Tq][Hq][D]
+    k_pool: np.ndarray             # before the write of the new tokens
+    v_pool: np.ndarray
+    k_new: np.ndarray              # [T][Hkv][D] rows written by kv_cache_write
+    v_new: np.ndarray
+    slot_mapping: np.ndarray       # int32 [T]
+    block_table: np.ndarray        # int32 [S][MB]
+    context_lens: np.ndarray       # int32 [S], includes the new tokens
+    cu_q_lens: np.ndarray | None = None   # int32 [S+1] (prefill)
+    prefix_tokens: int = 0
+    shared_blocks: int = 0
+    name: str = ""
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) if self.num_seqs else 0
+
+    @property
+    def max_q_len(self) -> int:
+        if self.cu_q_lens is None:
+            return 1
+        return int(np.diff(self.cu_q_lens).max()) if self.num_seqs else 0
+
+    @property
+    def total_q(self) -> int:
+        return int(self.q.shape[0])
+
+
+def _allocate(rng, lens, block_size, prefix_tokens, num_blocks, max_blocks):
+    """Block tables for sequences of `lens` tokens sharing `prefix_tokens` leading tokens."""
+    assert prefix_tokens % block_size == 0
+    shared = prefix_tokens // block_size
+    per_seq = [max(0, -(-int(n) // block_size)) for n in lens]
+    for n in lens:
+        assert prefix_tokens == 0 or n > prefix_tokens
+    private = [nb - shared if prefix_tokens else nb for nb in per_seq]
+    distinct = (shared if len(lens) else 0) + sum(private)
+    if num_blocks is None:
+        num_blocks = max(1, math.ceil(1.1 * distinct))
+    assert num_blocks >= distinct, "pool too small"
+    if max_blocks is None:
+        max_blocks = max(per_seq) if per_seq else 1
+        max_blocks = max(max_blocks, 1)
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    bt = np.full((len(lens), max_blocks), -1, dtype=np.int32)
+    shared_ids = perm[:shared]
+    nxt = shared
+    for s, nb in enumerate(per_seq):
+        assert nb <= max_blocks
+        if prefix_tokens:
+            bt[s, :shared] = shared_ids
+            bt[s, shared:nb] = perm[nxt: nxt + nb - shared]
+            nxt += nb - shared
+        else:
+            bt[s, :nb] = perm[nxt: nxt + nb]
+            nxt += nb
+    return bt, num_blocks, max_blocks, shared
+
+
+def _fill_pools(rng, bt, lens, new_from, hkv, d, b, nb, dtype):
+    """Pools of N(0,1) where a token lives, NaN elsewhere. Token positions >= new_from[s] of
+    sequence s are the ones about to be written, so they start as NaN too."""
+    k = rng.standard_normal((nb, hkv, b, d), dtype=np.float32)
+    v = rng.standard_normal((nb, hkv, d, b), dtype=np.float32)
+    live = np.zeros((nb, b), dtype=bool)
+    for s, n in enumerate(lens):
+        upto = int(new_from[s])
+        for j in range(0, upto, b):
+            blk = int(bt[s, j // b])
+            live[blk, : min(b, upto - j)] = True
+    dead_k = ~live[:, None, :, None]
+    dead_v = ~live[:, None, None, :]
+    np.copyto(k, np.float32(np.nan), where=np.broadcast_to(dead_k, k.shape))
+    np.copyto(v, np.float32(np.nan), where=np.broadcast_to(dead_v, v.shape))
+    if dtype == "bf16":
+        return bf16_bits(k), bf16_bits(v)
+    return k, v
+
+
+def _values(rng, shape, dtype):
+    x = rng.standard_normal(shape, dtype=np.float32)
+    return bf16_bits(x) if dtype == "bf16" else x
+
+
+def _slots(bt, positions_per_seq, b):
+    out = []
+    for s, positions in enumerate(positions_per_seq):
+        for j in positions:
+            out.append(int(bt[s, j // b]) * b + j % b)
+    return np.asarray(out, dtype=np.int32)
+
+
+def build_decode(seed, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, lens,
+                 dtype="bf16", prefix_tokens=0, num_blocks=None, max_blocks=None, name="",
+                 rng=None):
+    """One decode step: sequence s has lens[s] tokens, the last of which is new (written by
+    kv_cache_write before attention). A zero length has no new token (slot -1)."""
+    rng = np.random.default_rng(seed) if rng is None else rng
+    lens = np.asarray(lens, dtype=np.int32)
+    assert len(lens) == num_seqs
+    bt, nb, mb, shared = _allocate(rng, lens, block_size, prefix_tokens, num_blocks, max_blocks)
+    new_from = np.maximum(lens - 1, 0)
+    k_pool, v_pool = _fill_pools(rng, bt, lens, new_from, num_kv_heads, head_dim, block_size,
+                                 nb, dtype)
+    q = _values(rng, (num_seqs, num_q_heads, head_dim), dtype)
+    k_new = _values(rng, (num_seqs, num_kv_heads, head_dim), dtype)
+    v_new = _values(rng, (num_seqs, num_kv_heads, head_dim), dtype)
+    slots = np.full(num_seqs, -1, dtype=np.int32)
+    for s, n in enumerate(lens):
+        if n > 0:
+            j = int(n) - 1
+            slots[s] = int(bt[s, j // block_size]) * block_size + j % block_size
+    return Workload("decode", dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                    nb, mb, 1.0 / math.sqrt(head_dim), q, k_pool, v_pool, k_new, v_new, slots,
+                    bt, lens, None, prefix_tokens, shared, name)
+
+
+def build_prefill(seed, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, prior_lens,
+                  chunk_lens, dtype="bf16", prefix_tokens=0, num_blocks=None, max_blocks=None,
+                  name="", rng=None):
+    """One chunked-prefill call: sequence s has prior_lens[s] cached tokens followed by a
+    chunk of chunk_lens[s] new tokens whose K/V kv_cache_write stores first."""
+    rng = np.random.default_rng(seed) if rng is None else rng
+    prior = np.asarray(prior_lens, dtype=np.int32)
+    chunk = np.asarray(chunk_lens, dtype=np.int32)
+    lens = prior + chunk
+    bt, nb, mb, shared = _allocate(rng, lens, block_size, prefix_tokens, num_blocks, max_blocks)
+    k_pool, v_pool = _fill_pools(rng, bt, lens, prior, num_kv_heads, head_dim, block_size, nb,
+                                 dtype)
+    tq = int(chunk.sum())
+    q = _values(rng, (tq, num_q_heads, head_dim), dtype)
+    k_new = _values(rng, (tq, num_kv_heads, head_dim), dtype)
+    v_new = _values(rng, (tq, num_kv_heads, head_dim), dtype)
+    slots = _slots(bt, [range(int(r), int(r) + int(c)) for r, c in zip(prior, chunk)],
+                   block_size)
+    cu = np.zeros(num_seqs + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(chunk)
+    return Workload("prefill", dtype, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                    block_size, nb, mb, 1.0 / math.sqrt(head_dim), q, k_pool, v_pool, k_new,
+                    v_new, slots, bt, lens, cu, prefix_tokens, shared, name,
+                    {"prior_lens": prior, "chunk_lens": chunk})
+
+
+# ------------------------------------------------------------------------ the five workloads
+
+CONFIG_NAMES = {
+    1: "tiny fp32 decode: 4 seqs, ctx {1,17,33,100}, 8/8 heads, D64, B16, pool 64",
+    2: "Llama-3-8B-shaped decode: 64 seqs, ctx U[512,4096], 32/8 heads, D128, B16, bf16",
+    3: "Llama-3-70B-shaped decode: 32 seqs, ctx logU[1024,32768], 64/8 heads, D128, B32, bf16",
+    4: "shared-prefix decode: 64 seqs, 2000-token shared prefix + U[16,512], 32/8, D128, B16",
+    5: "chunked prefill: 8 seqs, 512-token chunk after U[0,8192] cached, 32/8, D128, B16, bf16",
+}
+
+
+def make_config(k: int, seed: int | None = None) -> Workload:
+    """The five workloads, k = 1..5, seeded by default with seed = k."""
+    seed = k if seed is None else seed
+    rng = np.random.default_rng(seed)
+    if k == 1:
+        return build_decode(seed, 4, 8, 8, 64, 16, [1, 17, 33, 100], "f32", num_blocks=64,
+                            max_blocks=7, name="c1", rng=rng)
+    if k == 2:
+        lens = rng.integers(512, 4097, 64)
+        return build_decode(seed, 64, 32, 8, 128, 16, lens, "bf16", max_blocks=256, name="c2",
+                            rng=rng)
+    if k == 3:
+        lens = np.round(np.exp(rng.uniform(math.log(1024), math.log(32768), 32))).astype(int)
+        return build_decode(seed, 32, 64, 8, 128, 32, lens, "bf16", max_blocks=1024,
+                            name="c3", rng=rng)
+    if k == 4:
+        suffix = rng.integers(16, 513, 64)
+        return build_decode(seed, 64, 32, 8, 128, 16, 2000 + suffix, "bf16", prefix_tokens=2000,
+                            max_blocks=157, name="c4", rng=rng)
+    if k == 5:
+        prior = rng.integers(0, 8193, 8)
+        return build_prefill(seed, 8, 32, 8, 128, 16, prior, [512] * 8, "bf16", max_blocks=544,
+                             name="c5", rng=rng)
+    raise ValueError(f"no config {k}")

@@ -1,0 +1,378 @@
+"""Pins that tie the CPU oracle to facts outside itself.
+
+Each pin is a function of an oracle module (`orc`, with the API of oracle.paged_attention) and
+raises AssertionError when the oracle disagrees with:
+  * the block-table figure of the zhichai.net page (golden fixture),
+  * the IEEE definition of bf16 (fixed bit patterns),
+  * brute-force scalar loops on tiny inputs,
+  * closed forms (one token; equal V rows; equal keys; two tokens),
+  * invariances (physical block permutation; shared vs duplicated blocks; GQA vs repeated
+    heads),
+  * a library routine: torch's CPU float64 scaled_dot_product_attention on the contiguous K/V
+    the test scatters into the pool with its own index code.
+test_oracle.py runs every pin on the real oracle; test_oracle_mutations.py plants mistakes in a
+copy of the oracle and checks that some pin fails for each.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+from paged_kv_cache_190_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _assert_close(a, b, tol, what):
+    err = float(np.max(np.abs(np.asarray(a) - np.asarray(b)))) if np.size(a) else 0.0
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.1e}"
+
+
+def _scatter_contiguous(kc, vc, bt, b, nb, dtype_np, fill):
+    """Test-local paging: put contiguous K/V [S][Hkv][n][D] into pools through `bt`, using the
+    flat-index formulas of the ABI header written out here (not the oracle's code)."""
+    s_count, hkv, n, d = kc.shape
+    kf = np.full(nb * hkv * b * d, fill, dtype=dtype_np)
+    vf = np.full(nb * hkv * d * b, fill, dtype=dtype_np)
+    for s in range(s_count):
+        for j in range(n):
+            blk, off = int(bt[s][j // b]), j % b
+            for h in range(hkv):
+                base_k = ((blk * hkv + h) * b + off) * d
+                kf[base_k: base_k + d] = kc[s, h, j]
+                for x in range(d):
+                    vf[((blk * hkv + h) * d + x) * b + off] = vc[s, h, j, x]
+    return kf.reshape(nb, hkv, b, d), vf.reshape(nb, hkv, d, b)
+
+
+# --------------------------------------------------------------------------------- pins
+
+def pin_figure_block_table(orc):
+    """zhichai.net figure: tokens 0-15 come from physical block #7, tokens 16-31 from #2.
+    Every pool element holds a tag naming (block, offset); the gathered rows must carry the tags
+    of the figure's blocks, in token order."""
+    fx = json.load(open(os.path.join(GOLDEN, "block_table_figure.json")))
+    b, n, bt = fx["block_size"], fx["context_len"], np.asarray(fx["block_table"], np.int32)
+    nb, hkv, d = 10, 1, 2
+    k = np.zeros((nb, hkv, b, d), np.float32)
+    v = np.zeros((nb, hkv, d, b), np.float32)
+    for blk in range(nb):
+        for off in range(b):
+            k[blk, 0, off, :] = blk * 100 + off
+            v[blk, 0, :, off] = -(blk * 100 + off)
+    kg, vg = orc.gather(k, v, bt, n, b, "f32")
+    for lb in fx["logical_blocks"]:
+        for t in range(lb["first_token"], lb["last_token"] + 1):
+            blk = int(kg[0, t, 0]) // 100
+            assert blk == lb["physical_block"], f"token {t} read from block {blk}"
+            assert int(-vg[0, t, 0]) // 100 == lb["physical_block"]
+    offs = [int(kg[0, t, 0]) % 100 for t in range(n)]
+    assert offs == [t % b for t in range(n)], "tokens of a block must be in slot order"
+
+
+def pin_bf16_decoding(orc):
+    """IEEE bf16 = the high 16 bits of binary32: fixed patterns and their values."""
+    bits = np.asarray([0x3F80, 0xC000, 0x3FC0, 0x0001, 0x8000, 0x4049, 0x7F80, 0x3E80],
+                      np.uint16)
+    want = [1.0, -2.0, 1.5, 2.0 ** -133, -0.0, 3.140625, math.inf, 0.25]
+    got = orc.to_f64(bits, "bf16")
+    assert list(got) == want, got
+
+
+def pin_write_roundtrip(orc):
+    """kv_cache_write then gather gives back the written rows bit for bit; other slots keep
+    their words; negative slots are skipped; the V element lands where the header's flat index
+    formula says."""
+    rng = np.random.default_rng(7)
+    nb, hkv, b, d = 6, 2, 16, 8
+    k = np.full((nb, hkv, b, d), 0xFFFF, np.uint16)
+    v = np.full((nb, hkv, d, b), 0xFFFF, np.uint16)
+    bt = np.asarray([[4, 1, 5]], np.int32)
+    n = 40
+    kn = rng.integers(0, 0x7F00, (n + 1, hkv, d)).astype(np.uint16)
+    vn = rng.integers(0, 0x7F00, (n + 1, hkv, d)).astype(np.uint16)
+    slots = np.asarray([int(bt[0, j // b]) * b + j % b for j in range(n)] + [-1], np.int32)
+    k2, v2 = orc.kv_cache_write(k, v, kn, vn, slots, b)
+    assert (k == 0xFFFF).all(), "input pool was modified"
+    kg, vg = orc.gather(k2, v2, bt[0], n, b, "bf16")
+    kw = orc.to_f64(kn[:n], "bf16").transpose(1, 0, 2)
+    vw = orc.to_f64(vn[:n], "bf16").transpose(1, 0, 2)
+    assert np.array_equal(kg, kw) and np.array_equal(vg, vw)
+    touched = np.zeros((nb, b), bool)
+    for j in range(n):
+        touched[bt[0, j // b], j % b] = True
+    assert (k2.transpose(0, 2, 1, 3)[~touched] == 0xFFFF).all()
+    assert (v2.transpose(0, 3, 1, 2)[~touched] == 0xFFFF).all()
+    j, h, x = 37, 1, 5
+    flat = ((int(bt[0, j // b]) * hkv + h) * d + x) * b + j % b
+    assert v2.reshape(-1)[flat] == vn[j, h, x]
+    flat = ((int(bt[0, j // b]) * hkv + h) * b + j % b) * d + x
+    assert k2.reshape(-1)[flat] == kn[j, h, x]
+
+
+def _tiny_decode(seed, hq, hkv, d, b, lens, dtype):
+    return wl.build_decode(seed, len(lens), hq, hkv, d, b, lens, dtype)
+
+
+def _written(orc, w):
+    return orc.kv_cache_write(w.k_pool, w.v_pool, w.k_new, w.v_new, w.slot_mapping,
+                              w.block_size)
+
+
+def pin_decode_brute_force(orc):
+    """Decode equals scalar brute force on tiny inputs (fp32 and bf16, G = 1, 2, 4, B = 16
+    and 32, lengths across block boundaries)."""
+    cases = [(1, 4, 4, 8, 16, [1, 16, 17, 40], "f32"),
+             (2, 4, 2, 8, 16, [3, 33], "bf16"),
+             (3, 8, 2, 8, 32, [31, 32, 70], "bf16")]
+    for seed, hq, hkv, d, b, lens, dt in cases:
+        w = _tiny_decode(seed, hq, hkv, d, b, lens, dt)
+        kp, vp = _written(orc, w)
+        got = orc.decode(w.q, kp, vp, w.block_table, w.context_lens, w.scale, dt)
+        ref = orc.brute_force_decode(w.q, kp, vp, w.block_table, w.context_lens, w.scale, dt)
+        _assert_close(got, ref, 1e-12, f"decode vs brute force {dt} G={hq // hkv} B={b}")
+
+
+def pin_prefill_brute_force(orc):
+    """Chunked prefill equals scalar brute force (bottom-right causal) on tiny inputs."""
+    cases = [(4, 4, 2, 8, 16, [0, 5, 17], [3, 1, 20], "f32"),
+             (5, 4, 4, 8, 32, [40, 0], [7, 33], "bf16")]
+    for seed, hq, hkv, d, b, prior, chunk, dt in cases:
+        w = wl.build_prefill(seed, len(prior), hq, hkv, d, b, prior, chunk, dt)
+        kp, vp = _written(orc, w)
+        got = orc.prefill_chunk(w.q, w.cu_q_lens, w.context_lens, kp, vp, w.block_table,
+                                w.scale, dt)
+        ref = orc.brute_force_prefill(w.q, w.cu_q_lens, w.context_lens, kp, vp, w.block_table,
+                                      w.scale, dt)
+        _assert_close(got, ref, 1e-12, f"prefill vs brute force {dt}")
+
+
+def pin_single_token(orc):
+    """A one-token context gives out = v exactly (softmax of one score is 1)."""
+    w = _tiny_decode(11, 8, 8, 64, 16, [1, 1, 1], "f32")
+    kp, vp = _written(orc, w)
+    out = orc.decode(w.q, kp, vp, w.block_table, w.context_lens, w.scale, "f32")
+    want = np.repeat(w.v_new.astype(np.float64), 1, axis=1)
+    assert np.array_equal(out, want)
+    # prefill: first chunk row with no earlier tokens sees only itself
+    p = wl.build_prefill(12, 2, 4, 2, 16, 16, [0, 0], [5, 9], "bf16")
+    kp, vp = _written(orc, p)
+    out = orc.prefill_chunk(p.q, p.cu_q_lens, p.context_lens, kp, vp, p.block_table, p.scale,
+                            "bf16")
+    for s in range(2):
+        row = int(p.cu_q_lens[s])
+        for h in range(4):
+            assert np.array_equal(out[row, h], orc.to_f64(p.v_new[row, h // 2], "bf16"))
+
+
+def pin_zero_length(orc):
+    """Reading: an empty context yields a zero row."""
+    w = _tiny_decode(13, 4, 4, 8, 16, [0, 5], "f32")
+    kp, vp = _written(orc, w)
+    out = orc.decode(w.q, kp, vp, w.block_table, w.context_lens, w.scale, "f32")
+    assert np.array_equal(out[0], np.zeros_like(out[0]))
+    assert np.all(np.isfinite(out[1])) and np.any(out[1] != 0)
+
+
+def pin_closed_forms(orc):
+    """Equal V rows -> out = that row; equal keys or q = 0 -> out = mean of V;
+    two tokens -> out = v0 + sigmoid(a1 - a0) (v1 - v0) with a_j = q.k_j / sqrt(D)."""
+    rng = np.random.default_rng(5)
+    s_count, hkv, n, d, b = 1, 1, 37, 16, 16
+    nb = 4
+    bt = np.asarray([[2, 0, 3]], np.int32)
+    kc = rng.standard_normal((s_count, hkv, n, d))
+    row = rng.standard_normal(d)
+    vc = np.broadcast_to(row, (s_count, hkv, n, d)).copy()
+    kp, vp = _scatter_contiguous(kc, vc, bt, b, nb, np.float64, np.nan)
+    kp, vp = kp.astype(np.float32), vp.astype(np.float32)
+    q = rng.standard_normal((1, 1, d)).astype(np.float32)
+    lens = np.asarray([n], np.int32)
+    out = orc.decode(q, kp, vp, bt, lens, 1 / math.sqrt(d), "f32")
+    _assert_close(out[0, 0], row.astype(np.float32), 1e-12, "equal V rows")
+    # equal keys: softmax is uniform
+    kc2 = np.broadcast_to(rng.standard_normal(d), (1, 1, n, d)).copy()
+    vc2 = rng.standard_normal((1, 1, n, d))
+    kp2, vp2 = _scatter_contiguous(kc2, vc2, bt, b, nb, np.float64, np.nan)
+    out = orc.decode(q, kp2.astype(np.float32), vp2.astype(np.float32), bt, lens, 0.125, "f32")
+    _assert_close(out[0, 0], vc2[0, 0].astype(np.float32).astype(np.float64).mean(0), 1e-12,
+                  "equal keys")
+    # q = 0: uniform too
+    out = orc.decode(np.zeros_like(q), kp, vp2.astype(np.float32), bt, lens, 0.125, "f32")
+    _assert_close(out[0, 0], vc2[0, 0].astype(np.float32).astype(np.float64).mean(0), 1e-12,
+                  "q = 0")
+    # two tokens
+    kc3 = rng.standard_normal((1, 1, 2, d)).astype(np.float32).astype(np.float64)
+    vc3 = rng.standard_normal((1, 1, 2, d)).astype(np.float32).astype(np.float64)
+    kp3, vp3 = _scatter_contiguous(kc3, vc3, bt, b, nb, np.float64, np.nan)
+    q64 = q[0, 0].astype(np.float64)
+    a0 = float(q64 @ kc3[0, 0, 0]) / math.sqrt(d)
+    a1 = float(q64 @ kc3[0, 0, 1]) / math.sqrt(d)
+    sig = 1.0 / (1.0 + math.exp(-(a1 - a0)))
+    want = vc3[0, 0, 0] + sig * (vc3[0, 0, 1] - vc3[0, 0, 0])
+    out = orc.decode(q, kp3.astype(np.float32), vp3.astype(np.float32), bt,
+                     np.asarray([2], np.int32), 1 / math.sqrt(d), "f32")
+    _assert_close(out[0, 0], want, 1e-12, "two-token closed form")
+
+
+def pin_block_permutation(orc):
+    """Relabelling physical blocks (pool and tables remapped together) changes nothing,
+    bit for bit."""
+    w = _tiny_decode(21, 8, 2, 16, 16, [5, 48, 70], "bf16")
+    kp, vp = _written(orc, w)
+    ref = orc.decode(w.q, kp, vp, w.block_table, w.context_lens, w.scale, "bf16")
+    rng = np.random.default_rng(3)
+    perm = rng.permutation(w.num_blocks)          # new id of old block i is perm[i]
+    kq = np.empty_like(kp)
+    vq = np.empty_like(vp)
+    kq[perm] = kp
+    vq[perm] = vp
+    bt = np.where(w.block_table >= 0, perm[np.maximum(w.block_table, 0)], -1).astype(np.int32)
+    got = orc.decode(w.q, kq, vq, bt, w.context_lens, w.scale, "bf16")
+    assert np.array_equal(got, ref)
+    p = wl.build_prefill(22, 2, 4, 2, 16, 16, [20, 3], [9, 30], "bf16")
+    kp, vp = _written(orc, p)
+    ref = orc.prefill_chunk(p.q, p.cu_q_lens, p.context_lens, kp, vp, p.block_table, p.scale,
+                            "bf16")
+    perm = rng.permutation(p.num_blocks)
+    kq = np.empty_like(kp)
+    vq = np.empty_like(vp)
+    kq[perm] = kp
+    vq[perm] = vp
+    bt = np.where(p.block_table >= 0, perm[np.maximum(p.block_table, 0)], -1).astype(np.int32)
+    got = orc.prefill_chunk(p.q, p.cu_q_lens, p.context_lens, kq, vq, bt, p.scale, "bf16")
+    assert np.array_equal(got, ref)
+
+
+def pin_shared_equals_duplicated(orc):
+    """Tables pointing at one shared copy of a prefix equal tables with private duplicates of
+    it (the pages' copy-on-write sharing reads the same data), bit for bit."""
+    w = wl.build_decode(31, 3, 4, 2, 16, 16, [40, 33, 61], "bf16", prefix_tokens=32)
+    kp, vp = _written(orc, w)
+    shared = w.block_table[0, : w.shared_blocks].copy()
+    assert all((w.block_table[s, : w.shared_blocks] == shared).all() for s in range(3))
+    ref = orc.decode(w.q, kp, vp, w.block_table, w.context_lens, w.scale, "bf16")
+    # duplicate the shared blocks for sequences 1 and 2 at the end of the pool
+    extra = 2 * len(shared)
+    kq = np.concatenate([kp, np.zeros((extra,) + kp.shape[1:], kp.dtype)])
+    vq = np.concatenate([vp, np.zeros((extra,) + vp.shape[1:], vp.dtype)])
+    bt = w.block_table.copy()
+    nxt = w.num_blocks
+    for s in (1, 2):
+        for i, blk in enumerate(shared):
+            kq[nxt] = kp[blk]
+            vq[nxt] = vp[blk]
+            bt[s, i] = nxt
+            nxt += 1
+    got = orc.decode(w.q, kq, vq, bt, w.context_lens, w.scale, "bf16")
+    assert np.array_equal(got, ref)
+
+
+def pin_gqa_equals_repeated_mha(orc):
+    """G query heads on one KV head equal MHA with that KV head repeated G times."""
+    w = _tiny_decode(41, 8, 2, 16, 16, [9, 50], "f32")
+    kp, vp = _written(orc, w)
+    ref = orc.decode(w.q, kp, vp, w.block_table, w.context_lens, w.scale, "f32")
+    kr = np.repeat(kp, 4, axis=1)
+    vr = np.repeat(vp, 4, axis=1)
+    got = orc.decode(w.q, kr, vr, w.block_table, w.context_lens, w.scale, "f32")
+    assert np.array_equal(got, ref)
+
+
+def _sdpa(q, k, v, mask=None, causal=False):
+    import torch
+    f = torch.nn.functional.scaled_dot_product_attention
+    return f(torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=mask,
+             is_causal=causal).numpy()
+
+
+def pin_decode_sdpa(orc):
+    """With the contiguous K/V scattered into a shuffled pool by the test's own index code,
+    decode equals torch's float64 scaled_dot_product_attention (GQA via repeated KV heads)."""
+    rng = np.random.default_rng(51)
+    s_count, hq, hkv, n, d, b = 2, 8, 2, 45, 32, 16
+    nbk = -(-n // b)
+    nb = 8
+    perm = rng.permutation(nb)
+    bt = np.full((s_count, 4), -1, np.int32)
+    bt[0, :nbk] = perm[:nbk]
+    bt[1, :nbk] = perm[nbk: 2 * nbk]
+    kc = rng.standard_normal((s_count, hkv, n, d)).astype(np.float32)
+    vc = rng.standard_normal((s_count, hkv, n, d)).astype(np.float32)
+    q = rng.standard_normal((s_count, hq, d)).astype(np.float32)
+    kp, vp = _scatter_contiguous(kc, vc, bt, b, nb, np.float32, np.nan)
+    out = orc.decode(q, kp, vp, bt, np.asarray([n, n], np.int32), 1 / math.sqrt(d), "f32")
+    g = hq // hkv
+    ref = _sdpa(q.astype(np.float64)[:, :, None, :],
+                np.repeat(kc.astype(np.float64), g, axis=1),
+                np.repeat(vc.astype(np.float64), g, axis=1))[:, :, 0, :]
+    _assert_close(out, ref, 1e-12, "decode vs SDPA")
+
+
+def pin_prefill_sdpa(orc):
+    """Prefill vs torch SDPA: with no earlier tokens the chunk is plain causal self-attention
+    (is_causal is valid because query and key lengths agree); with r earlier tokens the mask is
+    built explicitly (row i sees keys <= r + i); and a one-row chunk equals decode."""
+    rng = np.random.default_rng(61)
+    hq, hkv, d, b = 4, 2, 16, 16
+    g = hq // hkv
+    for r, c in [(0, 23), (19, 14)]:
+        n = r + c
+        nbk = -(-n // b)
+        nb = nbk + 3
+        bt = np.full((1, nbk + 1), -1, np.int32)
+        bt[0, :nbk] = rng.permutation(nb)[:nbk]
+        kc = rng.standard_normal((1, hkv, n, d)).astype(np.float32)
+        vc = rng.standard_normal((1, hkv, n, d)).astype(np.float32)
+        q = rng.standard_normal((c, hq, d)).astype(np.float32)
+        kp, vp = _scatter_contiguous(kc, vc, bt, b, nb, np.float32, np.nan)
+        out = orc.prefill_chunk(q, np.asarray([0, c], np.int32), np.asarray([n], np.int32), kp,
+                                vp, bt, 1 / math.sqrt(d), "f32")
+        qq = q.astype(np.float64).transpose(1, 0, 2)[None]          # [1][Hq][c][D]
+        kk = np.repeat(kc.astype(np.float64), g, axis=1)
+        vv = np.repeat(vc.astype(np.float64), g, axis=1)
+        if r == 0:
+            ref = _sdpa(qq, kk, vv, causal=True)
+        else:
+            import torch
+            mask = torch.zeros((c, n), dtype=torch.bool)
+            for i in range(c):
+                mask[i, : r + i + 1] = True
+            ref = _sdpa(qq, kk, vv, mask=mask)
+        _assert_close(out, ref[0].transpose(1, 0, 2), 1e-12, f"prefill vs SDPA r={r}")
+    # one-row chunk == decode at n
+    w = wl.build_prefill(62, 2, 4, 2, 16, 16, [30, 7], [1, 1], "bf16")
+    kp, vp = _written(orc, w)
+    pre = orc.prefill_chunk(w.q, w.cu_q_lens, w.context_lens, kp, vp, w.block_table, w.scale,
+                            "bf16")
+    dec = orc.decode(w.q, kp, vp, w.block_table, w.context_lens, w.scale, "bf16")
+    assert np.array_equal(pre, dec)
+
+
+def pin_row_helpers(orc):
+    """The one-row helpers used for sampled checks agree with the full functions."""
+    w = _tiny_decode(71, 8, 2, 16, 16, [3, 40], "bf16")
+    kp, vp = _written(orc, w)
+    full = orc.decode(w.q, kp, vp, w.block_table, w.context_lens, w.scale, "bf16")
+    for s, h in [(0, 0), (1, 7), (1, 3)]:
+        assert np.array_equal(orc.decode_row(w.q, kp, vp, w.block_table, w.context_lens,
+                                             w.scale, "bf16", s, h), full[s, h])
+    p = wl.build_prefill(72, 2, 4, 2, 16, 16, [5, 0], [6, 4], "bf16")
+    kp, vp = _written(orc, p)
+    full = orc.prefill_chunk(p.q, p.cu_q_lens, p.context_lens, kp, vp, p.block_table, p.scale,
+                             "bf16")
+    rows = [(0, 1), (5, 3), (8, 0)]
+    part = orc.prefill_chunk(p.q, p.cu_q_lens, p.context_lens, kp, vp, p.block_table, p.scale,
+                             "bf16", rows=rows)
+    for t, h in rows:
+        assert np.array_equal(part[t, h], full[t, h])
+
+
+PINS = [pin_figure_block_table, pin_bf16_decoding, pin_write_roundtrip, pin_decode_brute_force,
+        pin_prefill_brute_force, pin_single_token, pin_zero_length, pin_closed_forms,
+        pin_block_permutation, pin_shared_equals_duplicated, pin_gqa_equals_repeated_mha,
+        pin_decode_sdpa, pin_prefill_sdpa, pin_row_helpers]

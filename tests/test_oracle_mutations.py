@@ -1,0 +1,60 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that every one of
+them makes at least one pin fail. This is what makes the pins worth trusting."""
+import inspect
+import types
+
+import pytest
+
+from oracle import paged_attention as orc
+from oracle_pins import PINS
+
+SOURCE = inspect.getsource(orc)
+
+# (name, text in the oracle, replacement). Each text must occur in the oracle exactly once.
+MUTANTS = [
+    ("gqa_mod_instead_of_div", "            g = h // group\n            out[s, h] = attend",
+     "            g = h % hkv\n            out[s, h] = attend"),
+    ("scale_dropped", "a = scale * (k @ qrow)", "a = (k @ qrow)"),
+    ("normalise_by_max", "return (p @ v) / p.sum()", "return (p @ v) / p.max()"),
+    ("causal_off_by_one", "k[g, : last + 1], v[g, : last + 1]", "k[g, : last], v[g, : last]"),
+    ("causal_top_left", "last = r + i  # keys", "last = i  # keys"),
+    ("table_order_ignored", "ids = [int(x) for x in bt_row[:nbk]]",
+     "ids = sorted(int(x) for x in bt_row[:nbk])"),
+    ("v_layout_not_transposed", "to_f64(v_pool[i], dtype).transpose(0, 2, 1)",
+     "to_f64(v_pool[i], dtype).transpose(0, 1, 2)"),
+    ("last_block_not_truncated", "return k[:, :n, :], v[:, :n, :]", "return k, v"),
+    ("write_k_into_v", "v_pool[blk, :, :, off] = v_new[i]", "v_pool[blk, :, :, off] = k_new[i]"),
+    ("write_offset_swapped", "blk, off = divmod(slot, b)", "off, blk = divmod(slot, b)"),
+    ("bf16_shift", "(a.astype(np.uint32) << np.uint32(16))",
+     "(a.astype(np.uint32) << np.uint32(15))"),
+    ("query_uses_kv_head", "out[s, h] = attend(qf[s, h], k[g], v[g], scale)",
+     "out[s, h] = attend(qf[s, g], k[g], v[g], scale)"),
+    ("context_len_excludes_current", "        n = int(context_lens[s])\n        if n == 0:\n            continue",
+     "        n = int(context_lens[s]) - 1\n        if n <= 0:\n            continue"),
+    ("brute_gqa", "            g = h * hkv // hq\n            qv", "            g = h % hkv\n            qv"),
+    ("brute_offset", "                off = j % b\n                acc = 0.0\n                for x in range(d):\n                    acc += qv[x]",
+     "                off = (j + 1) % b\n                acc = 0.0\n                for x in range(d):\n                    acc += qv[x]"),
+    ("row_helper_gqa", "    g = h // (hq // hkv)\n    return attend", "    g = h % hkv\n    return attend"),
+    ("prefill_rows_selection", "if wanted is not None and (lo + i, h) not in wanted:",
+     "if wanted is not None and (i, h) not in wanted:"),
+]
+
+
+def _mutant(old, new):
+    assert SOURCE.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(SOURCE.replace(old, new), "<oracle mutant>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new):
+    mod = _mutant(old, new)
+    caught = []
+    for pin in PINS:
+        try:
+            pin(mod)
+        except Exception as e:  # an assertion or a crash both count as caught
+            caught.append((pin.__name__, type(e).__name__))
+            break
+    assert caught, f"planted mistake {name!r} passed every pin"
