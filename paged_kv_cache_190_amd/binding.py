@@ -1,0 +1,196 @@
+"""Python binding of libpkv (ctypes). Argument marshalling only.
+
+The functions take torch device tensors, check shapes, dtypes and contiguity, and pass raw
+device pointers and the current HIP stream to the C ABI declared in include/pkv.h. Every step of
+the computation runs in the library's HIP kernels; torch only owns device memory and streams.
+The Python names drop the C prefix: kv_cache_write is pkv_kv_cache_write, and so on.
+
+The library must have been built (python -m paged_kv_cache_190_amd.build); loading fails loudly
+otherwise. There is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "lib", "libpkv.so")
+
+PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP = range(5)
+PKV_F32, PKV_BF16 = 0, 1
+
+_lib = None
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status} ({detail})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libpkv (loaded once)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m paged_kv_cache_190_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    L.pkv_abi_version.restype = i32
+    L.pkv_status_string.restype = ctypes.c_char_p
+    L.pkv_status_string.argtypes = [i32]
+    L.pkv_last_error.restype = ctypes.c_char_p
+    L.pkv_kv_cache_write.restype = i32
+    L.pkv_kv_cache_write.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    L.pkv_decode_partition_size.restype = i32
+    L.pkv_decode_partition_size.argtypes = [i32, i32, i32, i32]
+    L.pkv_decode_workspace_size.restype = sz
+    L.pkv_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.pkv_paged_attention_decode.restype = i32
+    L.pkv_paged_attention_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                             i32, i32, f32, i32, i32, vp, sz, i32, i32, vp]
+    L.pkv_paged_attention_prefill_chunk.restype = i32
+    L.pkv_paged_attention_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                                    i32, i32, i32, i32, i32, f32, i32, i32, i32,
+                                                    i32, vp]
+    L.pkv_profile_enable.restype = i32
+    L.pkv_profile_enable.argtypes = [i32]
+    L.pkv_profile_reset.restype = i32
+    L.pkv_profile_read.restype = i32
+    L.pkv_profile_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                   ctypes.POINTER(ctypes.c_longlong)]
+    L.pkv_profile_kernel_names.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status: int, where: str) -> None:
+    if status != PKV_OK:
+        L = lib()
+        raise PkvError(status, where, L.pkv_last_error().decode())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    if t.dtype == torch.float32:
+        return PKV_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _dev(t, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _i32(t, name: str):
+    import torch
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+    return _dev(t, name)
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def kv_cache_write(k_new, v_new, k_pool, v_pool, slot_mapping, stream=None) -> None:
+    """Scatter k_new/v_new [T][Hkv][D] into k_pool [NB][Hkv][B][D] / v_pool [NB][Hkv][D][B]
+    at slot_mapping [T] (int32, slot = block * B + offset, negative = skip). In place."""
+    T, hkv, d = k_new.shape
+    nb, hkv2, b, d2 = k_pool.shape
+    if (hkv, d) != (hkv2, d2) or v_pool.shape != (nb, hkv, d, b) or v_new.shape != k_new.shape:
+        raise ValueError("inconsistent shapes")
+    if not (k_new.dtype == v_new.dtype == k_pool.dtype == v_pool.dtype):
+        raise TypeError("k/v and pools must share a dtype")
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [T]")
+    _check(lib().pkv_kv_cache_write(_dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                                    _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                                    _i32(slot_mapping, "slot_mapping"), T, hkv, d, b, nb,
+                                    _dtype_code(k_pool), _stream(stream)), "kv_cache_write")
+
+
+def decode_partition_size(partition_size, num_seqs, num_kv_heads, max_context_len) -> int:
+    return lib().pkv_decode_partition_size(partition_size, num_seqs, num_kv_heads,
+                                           max_context_len)
+
+
+def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                          partition_size=0) -> int:
+    return lib().pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                           max_context_len, partition_size)
+
+
+def paged_attention_decode(out, q, k_pool, v_pool, block_table, context_lens, scale,
+                           max_context_len=0, partition_size=0, workspace=None, stream=None):
+    """out [S][Hq][D] = softmax(scale * q K^T) V over each sequence's paged context.
+    A workspace (uint8 device tensor) is allocated when needed and not given."""
+    import torch
+    S, hq, d = q.shape
+    nb, hkv, b, d2 = k_pool.shape
+    if d2 != d or v_pool.shape != (nb, hkv, d, b) or out.shape != q.shape:
+        raise ValueError("inconsistent shapes")
+    if block_table.dim() != 2 or block_table.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_table must be [S][MB], context_lens [S]")
+    mb = block_table.shape[1]
+    ctx = max_context_len if max_context_len else mb * b
+    need = decode_workspace_size(S, hq, hkv, d, ctx, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().pkv_paged_attention_decode(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _i32(block_table, "block_table"), _i32(context_lens, "context_lens"), S, hq, hkv, d, b,
+        mb, nb, float(scale), int(max_context_len), int(partition_size), ws_ptr, ws_bytes,
+        _dtype_code(q), _dtype_code(out), _stream(stream)), "paged_attention_decode")
+    return out
+
+
+def paged_attention_prefill_chunk(out, q, cu_q_lens, context_lens, k_pool, v_pool, block_table,
+                                  scale, max_q_len=0, max_context_len=0, stream=None):
+    """out [Tq][Hq][D]: causal attention of each sequence's chunk rows over its paged context
+    (row i of a c-row chunk after r cached tokens sees keys 0 .. r + i)."""
+    tq, hq, d = q.shape
+    nb, hkv, b, d2 = k_pool.shape
+    S = context_lens.shape[0]
+    if d2 != d or v_pool.shape != (nb, hkv, d, b) or out.shape != q.shape:
+        raise ValueError("inconsistent shapes")
+    if cu_q_lens.shape != (S + 1,) or block_table.dim() != 2 or block_table.shape[0] != S:
+        raise ValueError("cu_q_lens must be [S+1], block_table [S][MB]")
+    _check(lib().pkv_paged_attention_prefill_chunk(
+        _dev(out, "out"), _dev(q, "q"), _i32(cu_q_lens, "cu_q_lens"),
+        _i32(context_lens, "context_lens"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _i32(block_table, "block_table"), S, tq, hq, hkv, d, b, block_table.shape[1], nb,
+        float(scale), int(max_q_len), int(max_context_len), _dtype_code(q), _dtype_code(out),
+        _stream(stream)), "paged_attention_prefill_chunk")
+    return out
+
+
+# ------------------------------------------------------------------------------ timing
+
+def profile_enable(on: bool = True) -> None:
+    _check(lib().pkv_profile_enable(1 if on else 0), "profile_enable")
+
+
+def profile_reset() -> None:
+    _check(lib().pkv_profile_reset(), "profile_reset")
+
+
+def profile_read(kernel: str):
+    """(total milliseconds, launches) of `kernel` since the last enable/reset."""
+    ms = ctypes.c_double()
+    n = ctypes.c_longlong()
+    _check(lib().pkv_profile_read(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)),
+           "profile_read")
+    return ms.value, n.value

@@ -1,0 +1,362 @@
+// C ABI of libpkv: argument validation, partition sizing, kernel timing, error reporting.
+// Declarations and the meaning of every argument are in include/pkv.h.
+#include "../../include/pkv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PKV_OK;
+  return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool supported_dtype(int d) { return d == PKV_F32 || d == PKV_BF16; }
+int elem_bytes(int d) { return d == PKV_BF16 ? 2 : 4; }
+
+constexpr int kMaxGridYZ = 65535;
+
+// ------------------------------------------------------------------ kernel timing registry
+struct TimingRecord {
+  int id;
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+
+std::mutex g_timing_mu;
+bool g_timing_on = false;
+std::vector<TimingRecord> g_pending;
+std::vector<hipEvent_t> g_event_pool;
+double g_total_ms[pkv::K_COUNT];
+long long g_launches[pkv::K_COUNT];
+thread_local hipEvent_t t_open_start = nullptr;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void drain_locked() {
+  for (const TimingRecord& r : g_pending) {
+    float ms = 0.f;
+    if (r.stop && hipEventSynchronize(r.stop) == hipSuccess &&
+        hipEventElapsedTime(&ms, r.start, r.stop) == hipSuccess) {
+      g_total_ms[r.id] += ms;
+      g_launches[r.id] += 1;
+    }
+    if (r.start) g_event_pool.push_back(r.start);
+    if (r.stop) g_event_pool.push_back(r.stop);
+  }
+  g_pending.clear();
+}
+
+}  // namespace
+
+namespace pkv {
+
+const char* kernel_name(int id) {
+  switch (id) {
+    case K_KV_WRITE: return "kv_cache_write";
+    case K_DECODE_PARTITION: return "decode_partition";
+    case K_DECODE_REDUCE: return "decode_reduce";
+    case K_PREFILL: return "prefill_chunk";
+    default: return "?";
+  }
+}
+
+void timing_begin(int, hipStream_t stream) {
+  if (!g_timing_on) return;
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  t_open_start = take_event();
+  if (t_open_start) hipEventRecord(t_open_start, stream);
+}
+
+void timing_end(int id, hipStream_t stream) {
+  if (!g_timing_on) return;
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  if (!t_open_start) return;
+  hipEvent_t stop = take_event();
+  if (stop) hipEventRecord(stop, stream);
+  g_pending.push_back({id, t_open_start, stop});
+  t_open_start = nullptr;
+}
+
+}  // namespace pkv
+
+namespace {
+
+// Default partition size: 512 tokens, halved (down to 64) while the launch would have fewer than
+// 2048 (sequence, KV head, partition) work units, i.e. about eight per compute unit.
+int resolve_partition(int partition_size, int num_seqs, int num_kv_heads, int max_ctx) {
+  if (partition_size < 0 || partition_size % 16 != 0) return -1;
+  if (partition_size > 0) return partition_size;
+  int p = 512;
+  while (p > 64) {
+    const long long parts = (max_ctx + p - 1) / p;
+    if (static_cast<long long>(num_seqs) * num_kv_heads * parts >= 2048) break;
+    p /= 2;
+  }
+  return p;
+}
+
+int num_partitions(int max_ctx, int p) { return max_ctx <= 0 ? 1 : (max_ctx + p - 1) / p; }
+
+size_t workspace_bytes_for(int S, int Hq, int D, int NP) {
+  if (NP <= 1) return 0;
+  const size_t rows = static_cast<size_t>(S) * Hq * NP;
+  return rows * D * sizeof(float) + 2 * rows * sizeof(float);
+}
+
+int check_common(int Hq, int Hkv, int D, int B, int dtype, int out_dtype) {
+  if (Hq <= 0 || Hkv <= 0) return fail(PKV_ERR_INVALID_ARG, "head counts must be positive");
+  if (Hq % Hkv != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "num_q_heads %d is not a multiple of num_kv_heads %d", Hq,
+                Hkv);
+  if (D != 64 && D != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", D);
+  if (B != 16 && B != 32) return fail(PKV_ERR_UNSUPPORTED, "block_size %d not in {16, 32}", B);
+  if (!supported_dtype(dtype) || !supported_dtype(out_dtype))
+    return fail(PKV_ERR_UNSUPPORTED, "dtype %d / out_dtype %d not supported", dtype, out_dtype);
+  if (Hq > kMaxGridYZ) return fail(PKV_ERR_UNSUPPORTED, "num_q_heads %d too large", Hq);
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARG: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+int pkv_kv_cache_write(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                       const int32_t* slot_mapping, int T, int num_kv_heads, int head_dim,
+                       int block_size, int num_blocks, int dtype, void* stream) {
+  if (T < 0) return fail(PKV_ERR_INVALID_ARG, "T = %d is negative", T);
+  if (T == 0) return PKV_OK;
+  if (!k_new || !v_new || !k_pool || !v_pool || !slot_mapping)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (num_kv_heads <= 0 || num_blocks <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_kv_heads and num_blocks must be positive");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", head_dim);
+  if (block_size != 16 && block_size != 32)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %d not in {16, 32}", block_size);
+  if (!supported_dtype(dtype)) return fail(PKV_ERR_UNSUPPORTED, "dtype %d not supported", dtype);
+  if (static_cast<long long>(num_blocks) * block_size > 0x7fffffffLL)
+    return fail(PKV_ERR_UNSUPPORTED, "pool of %d blocks exceeds int32 slot numbers", num_blocks);
+  pkv::KvWriteArgs a{k_new, v_new, k_pool, v_pool, slot_mapping, T, num_kv_heads, head_dim,
+                     block_size, num_blocks, elem_bytes(dtype)};
+  return hip_status(pkv::launch_kv_write(a, static_cast<hipStream_t>(stream)), "kv_cache_write");
+}
+
+int pkv_decode_partition_size(int partition_size, int num_seqs, int num_kv_heads,
+                              int max_context_len) {
+  return resolve_partition(partition_size, num_seqs, num_kv_heads, max_context_len);
+}
+
+size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                 int max_context_len, int partition_size) {
+  const int p = resolve_partition(partition_size, num_seqs, num_kv_heads, max_context_len);
+  if (p <= 0 || num_seqs <= 0 || num_q_heads <= 0) return 0;
+  return workspace_bytes_for(num_seqs, num_q_heads, head_dim,
+                             num_partitions(max_context_len, p));
+}
+
+int pkv_paged_attention_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* block_table, const int32_t* context_lens,
+                               int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                               int block_size, int max_blocks_per_seq, int num_blocks,
+                               float scale, int max_context_len, int partition_size,
+                               void* workspace, size_t workspace_bytes, int dtype, int out_dtype,
+                               void* stream) {
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs = %d is negative", num_seqs);
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_table || !context_lens)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  int st = check_common(num_q_heads, num_kv_heads, head_dim, block_size, dtype, out_dtype);
+  if (st != PKV_OK) return st;
+  if (max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq and num_blocks must be positive");
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
+  const long long cap = static_cast<long long>(max_blocks_per_seq) * block_size;
+  if (cap > 0x7fffffffLL) return fail(PKV_ERR_UNSUPPORTED, "max_blocks_per_seq too large");
+  if (max_context_len < 0 || max_context_len > cap)
+    return fail(PKV_ERR_INVALID_ARG, "max_context_len %d outside [0, %lld]", max_context_len,
+                cap);
+  if (num_seqs > kMaxGridYZ) return fail(PKV_ERR_UNSUPPORTED, "num_seqs %d too large", num_seqs);
+  const int max_ctx = max_context_len > 0 ? max_context_len : static_cast<int>(cap);
+  if (partition_size < 0 || partition_size % 16 != 0 || partition_size % block_size != 0)
+    return fail(PKV_ERR_INVALID_ARG,
+                "partition_size %d must be a non-negative multiple of 16 and of block_size",
+                partition_size);
+  const int P = resolve_partition(partition_size, num_seqs, num_kv_heads, max_ctx);
+  if (P % block_size != 0)
+    return fail(PKV_ERR_INVALID_ARG, "partition size %d not a multiple of block_size", P);
+  const int NP = num_partitions(max_ctx, P);
+  const size_t need = workspace_bytes_for(num_seqs, num_q_heads, head_dim, NP);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : static_cast<size_t>(0));
+  pkv::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.S = num_seqs;
+  a.Hq = num_q_heads;
+  a.Hkv = num_kv_heads;
+  a.D = head_dim;
+  a.B = block_size;
+  a.MB = max_blocks_per_seq;
+  a.NB = num_blocks;
+  a.scale = scale;
+  a.max_ctx = max_ctx;
+  a.P = P;
+  a.NP = NP;
+  if (NP > 1) {
+    const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * NP;
+    float* base = static_cast<float*>(workspace);
+    a.part_o = base;
+    a.part_m = base + rows * head_dim;
+    a.part_l = a.part_m + rows;
+  }
+  a.bf16_in = dtype == PKV_BF16;
+  a.bf16_out = out_dtype == PKV_BF16;
+  return hip_status(pkv::launch_decode(a, static_cast<hipStream_t>(stream)),
+                    "paged_attention_decode");
+}
+
+int pkv_paged_attention_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
+                                      const int32_t* context_lens, const void* k_pool,
+                                      const void* v_pool, const int32_t* block_table,
+                                      int num_seqs, int total_q, int num_q_heads,
+                                      int num_kv_heads, int head_dim, int block_size,
+                                      int max_blocks_per_seq, int num_blocks, float scale,
+                                      int max_q_len, int max_context_len, int dtype,
+                                      int out_dtype, void* stream) {
+  if (num_seqs < 0 || total_q < 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_seqs and total_q must be non-negative");
+  if (num_seqs == 0 || total_q == 0) return PKV_OK;
+  if (!out || !q || !cu_q_lens || !context_lens || !k_pool || !v_pool || !block_table)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  int st = check_common(num_q_heads, num_kv_heads, head_dim, block_size, dtype, out_dtype);
+  if (st != PKV_OK) return st;
+  if (max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq and num_blocks must be positive");
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
+  const long long cap = static_cast<long long>(max_blocks_per_seq) * block_size;
+  if (cap > 0x7fffffffLL) return fail(PKV_ERR_UNSUPPORTED, "max_blocks_per_seq too large");
+  if (max_context_len < 0 || max_context_len > cap)
+    return fail(PKV_ERR_INVALID_ARG, "max_context_len %d outside [0, %lld]", max_context_len,
+                cap);
+  if (max_q_len < 0 || max_q_len > total_q)
+    return fail(PKV_ERR_INVALID_ARG, "max_q_len %d outside [0, total_q = %d]", max_q_len,
+                total_q);
+  if (num_seqs > kMaxGridYZ) return fail(PKV_ERR_UNSUPPORTED, "num_seqs %d too large", num_seqs);
+  const long long gy = static_cast<long long>(num_q_heads);  // upper bound on grid y
+  if (gy > kMaxGridYZ) return fail(PKV_ERR_UNSUPPORTED, "too many heads");
+  pkv::PrefillArgs a{};
+  a.out = out;
+  a.q = q;
+  a.cu_q_lens = cu_q_lens;
+  a.context_lens = context_lens;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.S = num_seqs;
+  a.total_q = total_q;
+  a.Hq = num_q_heads;
+  a.Hkv = num_kv_heads;
+  a.D = head_dim;
+  a.B = block_size;
+  a.MB = max_blocks_per_seq;
+  a.NB = num_blocks;
+  a.scale = scale;
+  a.max_q_len = max_q_len > 0 ? max_q_len : total_q;
+  a.max_ctx = max_context_len > 0 ? max_context_len : static_cast<int>(cap);
+  a.bf16_in = dtype == PKV_BF16;
+  a.bf16_out = out_dtype == PKV_BF16;
+  return hip_status(pkv::launch_prefill(a, static_cast<hipStream_t>(stream)),
+                    "paged_attention_prefill_chunk");
+}
+
+int pkv_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  drain_locked();
+  for (int i = 0; i < pkv::K_COUNT; ++i) {
+    g_total_ms[i] = 0.0;
+    g_launches[i] = 0;
+  }
+  g_timing_on = on != 0;
+  return PKV_OK;
+}
+
+int pkv_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  drain_locked();
+  for (int i = 0; i < pkv::K_COUNT; ++i) {
+    g_total_ms[i] = 0.0;
+    g_launches[i] = 0;
+  }
+  return PKV_OK;
+}
+
+int pkv_profile_read(const char* kernel_name, double* total_ms, long long* launches) {
+  if (!kernel_name) return fail(PKV_ERR_INVALID_ARG, "null kernel name");
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  drain_locked();
+  for (int i = 0; i < pkv::K_COUNT; ++i) {
+    if (std::string(kernel_name) == pkv::kernel_name(i)) {
+      if (total_ms) *total_ms = g_total_ms[i];
+      if (launches) *launches = g_launches[i];
+      return PKV_OK;
+    }
+  }
+  return fail(PKV_ERR_INVALID_ARG, "unknown kernel name '%s'", kernel_name);
+}
+
+const char* pkv_profile_kernel_names(void) {
+  return "kv_cache_write,decode_partition,decode_reduce,prefill_chunk";
+}
+
+}  // extern "C"
