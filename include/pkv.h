@@ -106,20 +106,21 @@ int pkv_kv_cache_write(const void* k_new, const void* v_new, void* k_pool, void*
                        int block_size, int num_blocks, int dtype, void* stream);
 
 /*
- * pkv_decode_partition_size -- the partition size, in tokens, that pkv_paged_attention_decode
- * uses for `partition_size` (0 selects the library default). Library plumbing.
+ * pkv_decode_partition_size -- the fixed partition size, in tokens, that
+ * pkv_paged_attention_decode uses for these arguments; 0 when it uses the balanced split
+ * (partition_size == 0 with bf16 inputs). Library plumbing.
  * Returns -1 for a partition_size that is negative or not a multiple of 16.
  */
 int pkv_decode_partition_size(int partition_size, int num_seqs, int num_kv_heads,
-                              int max_context_len);
+                              int max_context_len, int dtype);
 
 /*
  * pkv_decode_workspace_size -- bytes of device workspace pkv_paged_attention_decode needs for
- * these sizes (0 when a single partition covers max_context_len, so no partials are stored).
+ * these sizes (0 when fixed partitions leave a single partition, so no partials are stored).
  * Library plumbing.
  */
 size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                                 int max_context_len, int partition_size);
+                                 int max_context_len, int partition_size, int dtype);
 
 /*
  * pkv_paged_attention_decode -- one query token per sequence against its paged context.
@@ -141,11 +142,20 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads
  *   context_lens  int32 [num_seqs]
  *   scale         normally 1/sqrt(head_dim)
  *   max_context_len  host bound on context_lens (0 = max_blocks_per_seq*block_size)
- *   partition_size   tokens per partition, a multiple of 16; 0 = library default.
- *                    Contexts longer than one partition are split: each partition computes
- *                    (max, sum of exponentials, normalised output) and a second kernel merges
- *                    them with log-sum-exp weights. The result is the same softmax up to
- *                    floating-point rounding.
+ *   partition_size   how the contexts are split over the GPU's waves (split-context):
+ *                    > 0: fixed partitions of that many tokens (a multiple of 16 and of
+ *                         block_size); each partition of each (sequence, KV head) is one work
+ *                         unit.
+ *                    0:   bf16 inputs: balanced split -- the batch's 32-token tiles, in
+ *                         (sequence, KV head, position) order, are dealt in equal contiguous
+ *                         shares to a fixed number of waves (1024 by default; the environment
+ *                         variable PKV_DECODE_WAVES overrides it), so every wave does the same
+ *                         work whatever the mix of context lengths. fp32 inputs: fixed
+ *                         partitions of a default size.
+ *                    A context cut into several pieces is merged by a second kernel: each piece
+ *                    leaves (max, sum of exponentials, normalised output) and the merge weighs
+ *                    them by log-sum-exp. The result is the same softmax up to floating-point
+ *                    rounding.
  *   workspace     device buffer of at least pkv_decode_workspace_size(...) bytes (may be NULL
  *                 when that size is 0); contents on entry are ignored.
  * out_dtype may differ from dtype (e.g. bf16 inputs with an fp32 output); the bf16 output is
@@ -189,17 +199,19 @@ int pkv_paged_attention_prefill_chunk(void* out, const void* q, const int32_t* c
                                       int out_dtype, void* stream);
 
 /*
- * Kernel timing (library plumbing, for benchmarks). When enabled, the library records a HIP
- * event pair around every kernel it launches, on the stream it launches that kernel on, and
- * accumulates the elapsed time per kernel name. pkv_profile_read synchronises on the recorded
- * events. Off by default; enabling, resetting and reading are not thread-safe against
+ * Kernel timing (library plumbing, for benchmarks). For every kernel selected by the mask, the
+ * library passes a pair of HIP events to the kernel launch itself (hipExtLaunchKernel), so the
+ * events bracket exactly that kernel on the stream it runs on and add nothing between kernels;
+ * the elapsed times are accumulated per kernel name. pkv_profile_read synchronises on the
+ * recorded events. Off by default; enabling, resetting and reading are not thread-safe against
  * concurrent launches.
- *   pkv_profile_enable(1) turns it on (and clears), 0 turns it off.
+ *   pkv_profile_enable(mask): bit k selects the k-th name of pkv_profile_kernel_names()
+ *   (0 turns timing off); also clears the totals.
  *   pkv_profile_read(name, &total_ms, &launches): totals for kernel `name` since the last
  *   enable/reset; returns PKV_ERR_INVALID_ARG for an unknown name.
- *   pkv_profile_kernel_names(): the known kernel names, comma-separated.
+ *   pkv_profile_kernel_names(): the kernel names, comma-separated, in bit order.
  */
-int pkv_profile_enable(int on);
+int pkv_profile_enable(int kernel_mask);
 int pkv_profile_reset(void);
 int pkv_profile_read(const char* kernel_name, double* total_ms, long long* launches);
 const char* pkv_profile_kernel_names(void);

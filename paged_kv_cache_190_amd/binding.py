@@ -46,9 +46,9 @@ def lib() -> ctypes.CDLL:
     L.pkv_kv_cache_write.restype = i32
     L.pkv_kv_cache_write.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     L.pkv_decode_partition_size.restype = i32
-    L.pkv_decode_partition_size.argtypes = [i32, i32, i32, i32]
+    L.pkv_decode_partition_size.argtypes = [i32, i32, i32, i32, i32]
     L.pkv_decode_workspace_size.restype = sz
-    L.pkv_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.pkv_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     L.pkv_paged_attention_decode.restype = i32
     L.pkv_paged_attention_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                              i32, i32, f32, i32, i32, vp, sz, i32, i32, vp]
@@ -120,15 +120,17 @@ def kv_cache_write(k_new, v_new, k_pool, v_pool, slot_mapping, stream=None) -> N
                                     _dtype_code(k_pool), _stream(stream)), "kv_cache_write")
 
 
-def decode_partition_size(partition_size, num_seqs, num_kv_heads, max_context_len) -> int:
+def decode_partition_size(partition_size, num_seqs, num_kv_heads, max_context_len,
+                          dtype=PKV_BF16) -> int:
+    """Fixed partition size decode uses (0: the balanced split)."""
     return lib().pkv_decode_partition_size(partition_size, num_seqs, num_kv_heads,
-                                           max_context_len)
+                                           max_context_len, dtype)
 
 
 def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
-                          partition_size=0) -> int:
+                          partition_size=0, dtype=PKV_BF16) -> int:
     return lib().pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                           max_context_len, partition_size)
+                                           max_context_len, partition_size, dtype)
 
 
 def paged_attention_decode(out, q, k_pool, v_pool, block_table, context_lens, scale,
@@ -144,7 +146,7 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_table, context_lens, sc
         raise ValueError("block_table must be [S][MB], context_lens [S]")
     mb = block_table.shape[1]
     ctx = max_context_len if max_context_len else mb * b
-    need = decode_workspace_size(S, hq, hkv, d, ctx, partition_size)
+    need = decode_workspace_size(S, hq, hkv, d, ctx, partition_size, _dtype_code(q))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
@@ -179,8 +181,21 @@ def paged_attention_prefill_chunk(out, q, cu_q_lens, context_lens, k_pool, v_poo
 
 # ------------------------------------------------------------------------------ timing
 
-def profile_enable(on: bool = True) -> None:
-    _check(lib().pkv_profile_enable(1 if on else 0), "profile_enable")
+KERNEL_NAMES = ("kv_cache_write", "decode_partition", "decode_reduce", "prefill_chunk")
+
+
+def profile_enable(on: bool = True, kernels=None) -> None:
+    """Time the library's kernels (all of them, or only those named in `kernels`) with HIP
+    events recorded as part of each kernel dispatch; clears the totals."""
+    if not on:
+        mask = 0
+    elif kernels is None:
+        mask = (1 << len(KERNEL_NAMES)) - 1
+    else:
+        mask = 0
+        for k in kernels:
+            mask |= 1 << KERNEL_NAMES.index(k)
+    _check(lib().pkv_profile_enable(mask), "profile_enable")
 
 
 def profile_reset() -> None:

@@ -4,7 +4,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstdarg>
 #include <cstdio>
 #include <mutex>
@@ -45,12 +47,11 @@ struct TimingRecord {
 };
 
 std::mutex g_timing_mu;
-bool g_timing_on = false;
+unsigned g_timing_mask = 0;  // bit k: kernel id k is timed
 std::vector<TimingRecord> g_pending;
 std::vector<hipEvent_t> g_event_pool;
 double g_total_ms[pkv::K_COUNT];
 long long g_launches[pkv::K_COUNT];
-thread_local hipEvent_t t_open_start = nullptr;
 
 hipEvent_t take_event() {
   if (!g_event_pool.empty()) {
@@ -91,29 +92,29 @@ const char* kernel_name(int id) {
   }
 }
 
-void timing_begin(int, hipStream_t stream) {
-  if (!g_timing_on) return;
+TimingEvents timing_events(int id) {
+  TimingEvents ev;
+  if (!(g_timing_mask & (1u << id))) return ev;
   std::lock_guard<std::mutex> lk(g_timing_mu);
-  t_open_start = take_event();
-  if (t_open_start) hipEventRecord(t_open_start, stream);
-}
-
-void timing_end(int id, hipStream_t stream) {
-  if (!g_timing_on) return;
-  std::lock_guard<std::mutex> lk(g_timing_mu);
-  if (!t_open_start) return;
-  hipEvent_t stop = take_event();
-  if (stop) hipEventRecord(stop, stream);
-  g_pending.push_back({id, t_open_start, stop});
-  t_open_start = nullptr;
+  ev.start = take_event();
+  ev.stop = take_event();
+  if (ev.start && ev.stop) {
+    g_pending.push_back({id, ev.start, ev.stop});
+  } else {
+    if (ev.start) g_event_pool.push_back(ev.start);
+    if (ev.stop) g_event_pool.push_back(ev.stop);
+    ev = TimingEvents{};
+  }
+  return ev;
 }
 
 }  // namespace pkv
 
 namespace {
 
-// Default partition size: 512 tokens, halved (down to 64) while the launch would have fewer than
-// 2048 (sequence, KV head, partition) work units, i.e. about eight per compute unit.
+// Fixed-partition default (fp32 inputs, or callers that ask for fixed partitions): 512 tokens,
+// halved (down to 64) while the launch would have fewer than 2048 (sequence, KV head,
+// partition) work units, i.e. about eight per compute unit.
 int resolve_partition(int partition_size, int num_seqs, int num_kv_heads, int max_ctx) {
   if (partition_size < 0 || partition_size % 16 != 0) return -1;
   if (partition_size > 0) return partition_size;
@@ -128,10 +129,48 @@ int resolve_partition(int partition_size, int num_seqs, int num_kv_heads, int ma
 
 int num_partitions(int max_ctx, int p) { return max_ctx <= 0 ? 1 : (max_ctx + p - 1) / p; }
 
-size_t workspace_bytes_for(int S, int Hq, int D, int NP) {
+size_t fixed_workspace_bytes(int S, int Hq, int D, int NP) {
   if (NP <= 1) return 0;
   const size_t rows = static_cast<size_t>(S) * Hq * NP;
   return rows * D * sizeof(float) + 2 * rows * sizeof(float);
+}
+
+// Balanced split (bf16 inputs, partition_size == 0).
+constexpr int kMinTilesPerWave = 8;     // 256 tokens
+constexpr int kDefaultDecodeWaves = 1024;
+
+struct BalancedPlan {
+  int waves;
+  int kmax;
+  size_t o_off, m_off, l_off, cnt_off, bytes;
+};
+
+int decode_waves_setting() {
+  const char* e = std::getenv("PKV_DECODE_WAVES");
+  if (e) {
+    const int v = std::atoi(e);
+    if (v > 0) return v;
+  }
+  return kDefaultDecodeWaves;
+}
+
+BalancedPlan balanced_plan(int S, int Hq, int Hkv, int D, int max_ctx) {
+  BalancedPlan pl{};
+  const int G = Hq / Hkv;
+  const long long segs = static_cast<long long>(Hkv) * ((G + 15) / 16);
+  const long long seg_tiles = (std::max(max_ctx, 1) + 31) / 32;
+  const long long t_upper = static_cast<long long>(S) * segs * seg_tiles;
+  pl.waves = static_cast<int>(
+      std::max(1LL, std::min<long long>(decode_waves_setting(), t_upper / kMinTilesPerWave)));
+  pl.kmax = static_cast<int>((seg_tiles + kMinTilesPerWave - 1) / kMinTilesPerWave + 1);
+  const size_t rows = static_cast<size_t>(S) * Hq * pl.kmax;
+  auto align = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  pl.o_off = 0;
+  pl.m_off = align(rows * D * sizeof(float));
+  pl.l_off = pl.m_off + align(rows * sizeof(float));
+  pl.cnt_off = pl.l_off + align(rows * sizeof(float));
+  pl.bytes = pl.cnt_off + align(static_cast<size_t>(S) * segs * sizeof(int32_t));
+  return pl;
 }
 
 int check_common(int Hq, int Hkv, int D, int B, int dtype, int out_dtype) {
@@ -188,16 +227,22 @@ int pkv_kv_cache_write(const void* k_new, const void* v_new, void* k_pool, void*
 }
 
 int pkv_decode_partition_size(int partition_size, int num_seqs, int num_kv_heads,
-                              int max_context_len) {
+                              int max_context_len, int dtype) {
+  if (partition_size == 0 && dtype == PKV_BF16) return 0;  // balanced split
   return resolve_partition(partition_size, num_seqs, num_kv_heads, max_context_len);
 }
 
 size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                                 int max_context_len, int partition_size) {
+                                 int max_context_len, int partition_size, int dtype) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0)
+    return 0;
+  if (partition_size == 0 && dtype == PKV_BF16)
+    return balanced_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len).bytes;
   const int p = resolve_partition(partition_size, num_seqs, num_kv_heads, max_context_len);
-  if (p <= 0 || num_seqs <= 0 || num_q_heads <= 0) return 0;
-  return workspace_bytes_for(num_seqs, num_q_heads, head_dim,
-                             num_partitions(max_context_len, p));
+  if (p <= 0) return 0;
+  return fixed_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                               num_partitions(max_context_len, p));
 }
 
 int pkv_paged_attention_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
@@ -227,14 +272,6 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_pool, con
     return fail(PKV_ERR_INVALID_ARG,
                 "partition_size %d must be a non-negative multiple of 16 and of block_size",
                 partition_size);
-  const int P = resolve_partition(partition_size, num_seqs, num_kv_heads, max_ctx);
-  if (P % block_size != 0)
-    return fail(PKV_ERR_INVALID_ARG, "partition size %d not a multiple of block_size", P);
-  const int NP = num_partitions(max_ctx, P);
-  const size_t need = workspace_bytes_for(num_seqs, num_q_heads, head_dim, NP);
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
-                workspace ? workspace_bytes : static_cast<size_t>(0));
   pkv::DecodeArgs a{};
   a.out = out;
   a.q = q;
@@ -251,14 +288,40 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_pool, con
   a.NB = num_blocks;
   a.scale = scale;
   a.max_ctx = max_ctx;
-  a.P = P;
-  a.NP = NP;
-  if (NP > 1) {
-    const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * NP;
-    float* base = static_cast<float*>(workspace);
-    a.part_o = base;
-    a.part_m = base + rows * head_dim;
-    a.part_l = a.part_m + rows;
+  if (partition_size == 0 && dtype == PKV_BF16) {
+    const BalancedPlan pl = balanced_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_ctx);
+    if (!workspace || workspace_bytes < pl.bytes)
+      return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.bytes,
+                  workspace ? workspace_bytes : static_cast<size_t>(0));
+    char* base = static_cast<char*>(workspace);
+    a.balanced = 1;
+    a.waves = pl.waves;
+    a.min_tiles = kMinTilesPerWave;
+    a.KMAX = pl.kmax;
+    a.P = 32;
+    a.NP = 1;
+    a.part_o = reinterpret_cast<float*>(base + pl.o_off);
+    a.part_m = reinterpret_cast<float*>(base + pl.m_off);
+    a.part_l = reinterpret_cast<float*>(base + pl.l_off);
+    a.seg_count = reinterpret_cast<int32_t*>(base + pl.cnt_off);
+  } else {
+    const int P = resolve_partition(partition_size, num_seqs, num_kv_heads, max_ctx);
+    if (P % block_size != 0)
+      return fail(PKV_ERR_INVALID_ARG, "partition size %d not a multiple of block_size", P);
+    const int NP = num_partitions(max_ctx, P);
+    const size_t need = fixed_workspace_bytes(num_seqs, num_q_heads, head_dim, NP);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+      return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                  workspace ? workspace_bytes : static_cast<size_t>(0));
+    a.P = P;
+    a.NP = NP;
+    if (NP > 1) {
+      const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * NP;
+      float* base = static_cast<float*>(workspace);
+      a.part_o = base;
+      a.part_m = base + rows * head_dim;
+      a.part_l = a.part_m + rows;
+    }
   }
   a.bf16_in = dtype == PKV_BF16;
   a.bf16_out = out_dtype == PKV_BF16;
@@ -320,14 +383,14 @@ int pkv_paged_attention_prefill_chunk(void* out, const void* q, const int32_t* c
                     "paged_attention_prefill_chunk");
 }
 
-int pkv_profile_enable(int on) {
+int pkv_profile_enable(int kernel_mask) {
   std::lock_guard<std::mutex> lk(g_timing_mu);
   drain_locked();
   for (int i = 0; i < pkv::K_COUNT; ++i) {
     g_total_ms[i] = 0.0;
     g_launches[i] = 0;
   }
-  g_timing_on = on != 0;
+  g_timing_mask = static_cast<unsigned>(kernel_mask) & ((1u << pkv::K_COUNT) - 1u);
   return PKV_OK;
 }
 

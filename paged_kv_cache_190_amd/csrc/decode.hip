@@ -37,53 +37,48 @@ struct KvTile {
   u32x4 v[D / 16];
 };
 
-template <int D, int B, bool SPLIT, typename OutT>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_bf16_kernel(
-    OutT* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_m,
-    float* __restrict__ part_l, const uint16_t* __restrict__ q,
-    const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool,
-    const int32_t* __restrict__ block_table, const int32_t* __restrict__ context_lens, int Hq,
-    int Hkv, int G, int HG, int MB, int P, int NP, float scale_log2) {
+// Running online-softmax state of one wave: 16 head columns, D output dims per column.
+template <int D>
+struct WaveAttn {
+  f32x4 acc[D / 16];
+  float m;
+  float l;  // per lane: sum over the lane's own tokens; reduce over rows before use
+};
+
+template <int D>
+__device__ __forceinline__ void attn_init(WaveAttn<D>& st) {
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) st.acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+}
+
+// Q as the MFMA B operand: column = head, contraction slots d = 32*kk + 8*lg + e.
+template <int D>
+__device__ __forceinline__ void load_q(u32x4 (&qf)[D / 32], const uint16_t* qrow, bool hvalid,
+                                       int lg) {
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk)
+    qf[kk] = hvalid ? load16(qrow + 32 * kk + 8 * lg) : u32x4{0u, 0u, 0u, 0u};
+}
+
+// Attend the wave's 16 head columns (KV head g) to tokens [tok_begin, tok_end) of one
+// sequence with n tokens, walking 32-token tiles from tok_begin (a multiple of B).
+template <int D, int B>
+__device__ __forceinline__ void attend_tiles(WaveAttn<D>& st, const u32x4 (&qf)[D / 32],
+                                             const uint16_t* __restrict__ kpool,
+                                             const uint16_t* __restrict__ vpool,
+                                             const int32_t* __restrict__ bt, int n, int g,
+                                             int Hkv, int tok_begin, int tok_end,
+                                             float scale_log2) {
   constexpr int KK = D / 32;
   constexpr int DT = D / 16;
   constexpr int TILE = B * D;  // elements of one (block, head) tile
-
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int r16 = lane & 15;
   const int lg = lane >> 4;
-  const int p = blockIdx.x;
-  const int g = blockIdx.y / HG;
-  const int hgrp = blockIdx.y - g * HG;
-  const int s = blockIdx.z;
-  const int n = context_lens[s];
-  const int start = p * P;
-  const int hl = hgrp * 16 + r16;
-  const bool hvalid = hl < G;
-  const int h = g * G + (hvalid ? hl : 0);
-
-  if (start >= n) {
-    if (!SPLIT && p == 0 && hvalid) {  // empty context: zero row
-      OutT* o = out + (static_cast<int64_t>(s) * Hq + h) * D;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) store_out(o + 16 * dt + 4 * lg + e, 0.0f);
-    }
-    return;
-  }
-  const int end = min(start + P, n);
-  const int ntiles = (end - start + 31) >> 5;
+  const int ntiles = (tok_end - tok_begin + 31) >> 5;
   const int nblk = (n + B - 1) / B;
-  const int32_t* bt = block_table + static_cast<int64_t>(s) * MB;
-
-  // Q as the B operand: column = head, contraction slots d = 32*kk + 8*lg + e.
-  u32x4 qf[KK];
-  {
-    const uint16_t* qrow = q + (static_cast<int64_t>(s) * Hq + h) * D + 8 * lg;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      qf[kk] = hvalid ? load16(qrow + 32 * kk) : u32x4{0u, 0u, 0u, 0u};
-  }
 
   // K operand row r16 of half hf holds tile token 8*(r16/4) + 4*hf + r16%4.
   int koff[2];
@@ -98,14 +93,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const int vsel = (B == 16) ? (lg >> 1) : 0;
   const int vtok = (B == 16) ? 8 * (lg & 1) : 8 * lg;
   const int voff = r16 * B + vtok;
-
   const int64_t head_off = static_cast<int64_t>(g) * TILE;
   const int64_t blk_stride = static_cast<int64_t>(Hkv) * TILE;
 
+  // Block ids, one chunk of up to 64 logical blocks at a time: lane i holds the id of block
+  // chunk_lb + i (clamped to the last block that holds tokens). Tiles read them with readlane,
+  // so block addresses stay wave-uniform and the tile loop issues no other vector load.
+  int chunk_lb = 0;
+  int my_id = 0;
+  auto block_id = [&](int lb) -> int {
+    return __builtin_amdgcn_readlane(my_id, min(lb, nblk - 1) - chunk_lb);
+  };
   auto load_tile = [&](KvTile<D, B>& T, int t) {
-    const int lb0 = (start + 32 * t) / B;
-    const int id0 = bt[min(lb0, nblk - 1)];
-    const int id1 = (B == 16) ? bt[min(lb0 + 1, nblk - 1)] : id0;
+    const int lb0 = (tok_begin + 32 * t) / B;
+    const int id0 = block_id(lb0);
+    const int id1 = (B == 16) ? block_id(lb0 + 1) : id0;
     const uint16_t* kb = kpool + (ksel ? id1 : id0) * blk_stride + head_off;
     const uint16_t* vb = vpool + (vsel ? id1 : id0) * blk_stride + head_off;
 #pragma unroll
@@ -116,14 +118,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     for (int dt = 0; dt < DT; ++dt) T.v[dt] = load16(vb + voff + 16 * dt * B);
   };
 
-  f32x4 acc[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY;
-  float l = 0.f;
-
   auto compute = [&](KvTile<D, B>& T, int t) {
-    const int tok0 = start + 32 * t;
+    const int tok0 = tok_begin + 32 * t;
     f32x4 sc[2];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
@@ -132,7 +128,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       for (int kk = 0; kk < KK; ++kk) sc[hf] = mfma16x16x32(T.k[hf][kk], qf[kk], sc[hf]);
     }
     // lane: head column r16, tile tokens 8*lg + 4*hf + e
-    const int lim = end - tok0;
+    const int lim = tok_end - tok0;
     float x[8];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
@@ -144,11 +140,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     float tmax = x[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
-    tmax = wave_max_xor(tmax, 16);
-    tmax = wave_max_xor(tmax, 32);
-    const float mnew = fmaxf(m, tmax);
-    const float alpha = fast_exp2(m - mnew);
-    m = mnew;
+    tmax = xor32_max(xor16_max(tmax));
+    const float mnew = fmaxf(st.m, tmax);
+    const float alpha = fast_exp2(st.m - mnew);
+    st.m = mnew;
     float psum = 0.f;
     u32x4 pb;
 #pragma unroll
@@ -158,9 +153,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       psum += p0 + p1;
       pb[w] = pack_bf16x2(p0, p1);
     }
-    l = l * alpha + psum;
+    st.l = st.l * alpha + psum;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+    for (int dt = 0; dt < DT; ++dt) st.acc[dt] *= alpha;
     // Token slots at or past n may hold stale words (NaN) or come from a borrowed block:
     // their P is 0, but 0 * NaN is NaN, so clear the V words themselves.
     const int vlim = n - tok0;
@@ -175,40 +170,242 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       }
     }
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma16x16x32(T.v[dt], pb, acc[dt]);
+    for (int dt = 0; dt < DT; ++dt) st.acc[dt] = mfma16x16x32(T.v[dt], pb, st.acc[dt]);
   };
 
+  // Software pipeline: every compute of tile t runs while the loads of tile t+1 are in
+  // flight. Inside a chunk the loop body always issues exactly one tile of loads before each
+  // compute, so the wait before a compute leaves the next tile's loads outstanding.
+  constexpr int kChunkTiles = 64 * B / 32;  // tiles whose block ids fit one VGPR
   KvTile<D, B> ta, tb;
-  load_tile(ta, 0);
-  for (int t = 0; t < ntiles; t += 2) {
-    if (t + 1 < ntiles) load_tile(tb, t + 1);
-    compute(ta, t);
-    if (t + 1 >= ntiles) break;
-    if (t + 2 < ntiles) load_tile(ta, t + 2);
-    compute(tb, t + 1);
-  }
-
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  const float inv = 1.0f / l;
-  if (!hvalid) return;
-  const int64_t row = static_cast<int64_t>(s) * Hq + h;
-  if constexpr (!SPLIT) {
-    OutT* o = out + row * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) store_out(o + 16 * dt + 4 * lg + e, acc[dt][e] * inv);
-  } else {
-    const int64_t idx = row * NP + p;
-    if (lg == 0) {
-      part_m[idx] = m;
-      part_l[idx] = l;
+  for (int c0 = 0; c0 < ntiles; c0 += kChunkTiles) {
+    const int c1 = min(ntiles, c0 + kChunkTiles);
+    chunk_lb = (tok_begin + 32 * c0) / B;
+    my_id = bt[min(chunk_lb + lane, nblk - 1)];
+    load_tile(ta, c0);
+    int t = c0;
+    for (; t + 2 < c1; t += 2) {
+      load_tile(tb, t + 1);
+      compute(ta, t);
+      load_tile(ta, t + 2);
+      compute(tb, t + 1);
     }
-    float* o = part_o + idx * D;
+    if (t + 1 < c1) {
+      load_tile(tb, t + 1);
+      compute(ta, t);
+      compute(tb, t + 1);
+    } else {
+      compute(ta, t);
+    }
+  }
+}
+
+// Final output of a wave whose state covers a head's whole context: out = acc / l.
+template <int D, typename OutT>
+__device__ __forceinline__ void write_final(OutT* __restrict__ o, const WaveAttn<D>& st,
+                                            float l_total, int lg) {
+  const float inv = 1.0f / l_total;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<f32x4*>(o + 16 * dt + 4 * lg) = acc[dt] * inv;
+  for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_out(o + 16 * dt + 4 * lg + e, st.acc[dt][e] * inv);
+}
+
+// Partial result of part of a context: (m, l, acc / l) in fp32.
+template <int D>
+__device__ __forceinline__ void write_partial(float* __restrict__ part_o,
+                                              float* __restrict__ part_m,
+                                              float* __restrict__ part_l, int64_t idx,
+                                              const WaveAttn<D>& st, float l_total, int lg) {
+  const float inv = 1.0f / l_total;
+  if (lg == 0) {
+    part_m[idx] = st.m;
+    part_l[idx] = l_total;
+  }
+  float* o = part_o + idx * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt)
+    *reinterpret_cast<f32x4*>(o + 16 * dt + 4 * lg) = st.acc[dt] * inv;
+}
+
+template <int D, typename OutT>
+__device__ __forceinline__ void write_zero(OutT* __restrict__ o, int lg) {
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_out(o + 16 * dt + 4 * lg + e, 0.0f);
+}
+
+// Fixed partitions of P tokens: grid (KV head x head group, sequence, partition). The
+// partition index is the slowest, so the dispatcher hands out every sequence's first (full)
+// partitions before the shorter last ones, and the launch ends on small work units.
+template <int D, int B, bool SPLIT, typename OutT>
+__global__ __launch_bounds__(64) void decode_fixed_kernel(
+    OutT* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_m,
+    float* __restrict__ part_l, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ context_lens, int Hq,
+    int Hkv, int G, int HG, int MB, int P, int NP, float scale_log2) {
+  const int lane = threadIdx.x;
+  const int lg = lane >> 4;
+  const int g = blockIdx.x / HG;
+  const int hgrp = blockIdx.x - g * HG;
+  const int s = blockIdx.y;
+  const int p = blockIdx.z;
+  const int n = context_lens[s];
+  const int start = p * P;
+  const int hl = hgrp * 16 + (lane & 15);
+  const bool hvalid = hl < G;
+  const int h = g * G + (hvalid ? hl : 0);
+  const int64_t row = static_cast<int64_t>(s) * Hq + h;
+
+  if (start >= n) {
+    if (!SPLIT && p == 0 && hvalid) write_zero<D>(out + row * D, lg);  // empty context
+    return;
+  }
+  u32x4 qf[D / 32];
+  load_q<D>(qf, q + row * D, hvalid, lg);
+  WaveAttn<D> st;
+  attn_init(st);
+  attend_tiles<D, B>(st, qf, kpool, vpool, block_table + static_cast<int64_t>(s) * MB, n, g,
+                     Hkv, start, min(start + P, n), scale_log2);
+  const float l_total = xor32_sum(xor16_sum(st.l));
+  if (!hvalid) return;
+  if constexpr (!SPLIT) write_final<D>(out + row * D, st, l_total, lg);
+  else write_partial<D>(part_o, part_m, part_l, row * NP + p, st, l_total, lg);
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int mk = 32; mk >= 1; mk >>= 1) v += __shfl_xor(v, mk);
+  return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan_i(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+// Balanced split: the batch is a list of 32-token tiles ordered by (sequence, KV head x head
+// group, tile); wave w of W takes tiles [w*T/W, (w+1)*T/W). A (sequence, KV head) segment that
+// one wave covers whole is written as output directly; a segment shared by several waves gets
+// one partial per wave, merged by the reduce kernel. Every wave does the same number of tiles
+// (to within one), whatever the mix of context lengths. Wave 0 also records, per segment, how
+// many waves share it. W is lowered on the device so that each wave gets at least min_tiles
+// tiles, which bounds the partials per segment by ceil(ceil(max_ctx/32) / min_tiles) + 1 = KMAX.
+template <int D, int B, typename OutT>
+__global__ __launch_bounds__(64) void decode_balanced_kernel(
+    OutT* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_m,
+    float* __restrict__ part_l, int32_t* __restrict__ seg_count,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kpool,
+    const uint16_t* __restrict__ vpool, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ context_lens, int S, int Hq, int Hkv, int G, int HG, int MB,
+    int KMAX, int min_tiles, float scale_log2) {
+  const int lane = threadIdx.x;
+  const int lg = lane >> 4;
+  const int w = blockIdx.x;
+  const int segs = Hkv * HG;
+
+  int64_t T = 0;  // tiles of the whole batch
+  for (int base = 0; base < S; base += 64) {
+    const int s = base + lane;
+    const int ts = (s < S) ? (context_lens[s] + 31) >> 5 : 0;
+    T += wave_sum_i(ts);
+  }
+  T *= segs;
+  const int64_t Weff =
+      max<int64_t>(1, min<int64_t>(gridDim.x, T / max(1, min_tiles)));
+  // wave that owns tile x: the largest w with floor(w*T/Weff) <= x
+  auto wave_of = [&](int64_t x) -> int64_t { return (x * Weff + Weff - 1) / T; };
+
+  if (w == 0) {  // segment sharing counts, for the reduce
+    int64_t cum = 0;
+    for (int base = 0; base < S; base += 64) {
+      const int s = base + lane;
+      const int ts = (s < S) ? (context_lens[s] + 31) >> 5 : 0;
+      const int incl = wave_incl_scan_i(ts);
+      if (s < S) {
+        const int64_t seq0 = (cum + incl - ts) * segs;
+        for (int j = 0; j < segs; ++j) {
+          int cnt = 0;
+          if (ts > 0) {
+            const int64_t a = seq0 + static_cast<int64_t>(j) * ts;
+            cnt = static_cast<int>(wave_of(a + ts - 1) - wave_of(a) + 1);
+          }
+          seg_count[static_cast<int64_t>(s) * segs + j] = cnt;
+        }
+      }
+      cum += __shfl(incl, 63);
+    }
+  }
+  if (w >= Weff) return;
+  const int64_t x0 = (static_cast<int64_t>(w) * T) / Weff;
+  const int64_t x1 = (static_cast<int64_t>(w + 1) * T) / Weff;
+  if (x0 >= x1) return;
+
+  // Locate the sequence holding tile x0.
+  int s = -1;
+  int64_t sstart = 0;  // first tile of sequence s
+  {
+    int64_t cum = 0;
+    for (int base = 0; base < S && s < 0; base += 64) {
+      const int sl = base + lane;
+      const int ts = (sl < S) ? (context_lens[sl] + 31) >> 5 : 0;
+      const int incl = wave_incl_scan_i(ts);
+      const int64_t end_l = (cum + incl) * segs;
+      const uint64_t hit = __ballot(sl < S && end_l > x0);
+      if (hit) {
+        const int first = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+        s = base + first;
+        sstart = (cum + __shfl(incl - ts, first)) * segs;
+      }
+      cum += __shfl(incl, 63);
+    }
+  }
+  if (s < 0) return;
+  int n = context_lens[s];
+  int ts = (n + 31) >> 5;
+  int j = static_cast<int>((x0 - sstart) / ts);
+  int64_t x = x0;
+  while (x < x1) {
+    const int64_t a = sstart + static_cast<int64_t>(j) * ts;  // first tile of segment (s, j)
+    const int t_begin = static_cast<int>(x - a);
+    const int t_end = static_cast<int>(min<int64_t>(ts, x1 - a));
+    const int g = j / HG;
+    const int hgrp = j - g * HG;
+    const int hl = hgrp * 16 + (lane & 15);
+    const bool hvalid = hl < G;
+    const int h = g * G + (hvalid ? hl : 0);
+    const int64_t row = static_cast<int64_t>(s) * Hq + h;
+    u32x4 qf[D / 32];
+    load_q<D>(qf, q + row * D, hvalid, lg);
+    WaveAttn<D> st;
+    attn_init(st);
+    attend_tiles<D, B>(st, qf, kpool, vpool, block_table + static_cast<int64_t>(s) * MB, n, g,
+                       Hkv, 32 * t_begin, min(32 * t_end, n), scale_log2);
+    const float l_total = xor32_sum(xor16_sum(st.l));
+    const int64_t wf = wave_of(a);
+    if (hvalid) {
+      if (wf == wave_of(a + ts - 1)) write_final<D>(out + row * D, st, l_total, lg);
+      else if (w - wf < KMAX)  // always true when context_lens respect max_context_len
+        write_partial<D>(part_o, part_m, part_l, row * KMAX + (w - wf), st, l_total, lg);
+    }
+    x = a + t_end;
+    if (++j == segs) {  // next non-empty sequence
+      j = 0;
+      do {
+        sstart += static_cast<int64_t>(segs) * ts;
+        if (++s >= S) break;
+        n = context_lens[s];
+        ts = (n + 31) >> 5;
+      } while (ts == 0);
+      if (s >= S) break;
+    }
   }
 }
 
@@ -290,7 +487,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
     for (int j = 0; j < cnt; ++j) {
       const float pj = ps[j];
       const int64_t vb = vbase[j];
-      for (int i = 0; i < DPL; ++i) acc[i] += pj * vpool[vb + static_cast<int64_t>(lane + 64 * i) * B];
+      for (int i = 0; i < DPL; ++i)
+        acc[i] += pj * vpool[vb + static_cast<int64_t>(lane + 64 * i) * B];
     }
     __syncthreads();
   }
@@ -307,105 +505,141 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
   }
 }
 
-// Merge of the partitions: out = sum_p w_p o_p / sum_p w_p, w_p = l_p * 2^(m_p - max m).
+// Merge of partial results: out = sum_k w_k o_k / sum_k w_k, w_k = l_k * 2^(m_k - max m).
+// One workgroup per (sequence, query head). Fixed partitions (seg_count == nullptr): the row has
+// ceil(n / P) partials. Balanced split: seg_count gives the number of waves that shared the
+// row's segment; 1 means the output was written already, 0 an empty context.
 template <typename OutT>
 __global__ __launch_bounds__(64) void decode_reduce_kernel(
     OutT* __restrict__ out, const float* __restrict__ part_o, const float* __restrict__ part_m,
-    const float* __restrict__ part_l, const int32_t* __restrict__ context_lens, int Hq, int D,
-    int P, int NP) {
+    const float* __restrict__ part_l, const int32_t* __restrict__ context_lens,
+    const int32_t* __restrict__ seg_count, int Hq, int G, int HG, int D, int P, int KMAX) {
+  __shared__ float wts[64];
   const int h = blockIdx.x;
   const int s = blockIdx.y;
-  const int n = context_lens[s];
-  const int np = min((n + P - 1) / P, NP);  // NP bounds the workspace rows
+  const int tid = threadIdx.x;
   const int64_t row = static_cast<int64_t>(s) * Hq + h;
   OutT* o = out + row * D;
-  if (np <= 0) {
-    for (int d = threadIdx.x; d < D; d += 64) store_out(o + d, 0.0f);
+  int cnt;
+  if (seg_count) {
+    const int g = h / G;
+    const int j = g * HG + (h - g * G) / 16;
+    cnt = seg_count[static_cast<int64_t>(s) * (Hq / G) * HG + j];
+    if (cnt == 1) return;
+  } else {
+    cnt = (context_lens[s] + P - 1) / P;
+  }
+  cnt = min(cnt, KMAX);  // KMAX bounds the workspace rows
+  if (cnt <= 0) {
+    for (int d = tid; d < D; d += 64) store_out(o + d, 0.0f);
     return;
   }
-  const float* pm = part_m + row * NP;
-  const float* pl = part_l + row * NP;
+  const float* pm = part_m + row * KMAX;
+  const float* pl = part_l + row * KMAX;
+  const float* po = part_o + row * KMAX * D;
   float M = -INFINITY;
-  for (int i = 0; i < np; ++i) M = fmaxf(M, pm[i]);
-  float wsum = 0.f;
-  float acc0 = 0.f, acc1 = 0.f;
-  const float* po = part_o + row * NP * D;
-  const int d0 = threadIdx.x, d1 = threadIdx.x + 64;
-  for (int i = 0; i < np; ++i) {
-    const float w = pl[i] * fast_exp2(pm[i] - M);
-    wsum += w;
-    acc0 += w * po[static_cast<int64_t>(i) * D + d0];
-    if (d1 < D) acc1 += w * po[static_cast<int64_t>(i) * D + d1];
+  for (int k = tid; k < cnt; k += 64) M = fmaxf(M, pm[k]);
+#pragma unroll
+  for (int mk = 32; mk >= 1; mk >>= 1) M = fmaxf(M, __shfl_xor(M, mk));
+  float acc0 = 0.f, acc1 = 0.f, wsum = 0.f;
+  for (int k0 = 0; k0 < cnt; k0 += 64) {
+    const int k = k0 + tid;
+    const float wk = (k < cnt) ? pl[k] * fast_exp2(pm[k] - M) : 0.f;
+    wts[tid] = wk;
+    __syncthreads();
+    const int kn = min(64, cnt - k0);
+    for (int i = 0; i < kn; ++i) {
+      const float wi = wts[i];
+      wsum += wi;
+      const float* pi = po + static_cast<int64_t>(k0 + i) * D;
+      acc0 += wi * pi[tid];
+      if (tid + 64 < D) acc1 += wi * pi[tid + 64];
+    }
+    __syncthreads();
   }
   const float inv = 1.0f / wsum;
-  store_out(o + d0, acc0 * inv);
-  if (d1 < D) store_out(o + d1, acc1 * inv);
+  store_out(o + tid, acc0 * inv);
+  if (tid + 64 < D) store_out(o + tid + 64, acc1 * inv);
 }
 
 // ------------------------------------------------------------------------------ launchers
 
-template <int D, int B, bool SPLIT, typename OutT>
+template <int D, int B, typename OutT>
 static void launch_bf16(const DecodeArgs& a, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   const int HG = (G + 15) / 16;
-  dim3 grid(a.NP, a.Hkv * HG, a.S);
-  decode_bf16_kernel<D, B, SPLIT, OutT><<<grid, 64, 0, st>>>(
-      static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l,
-      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
-      static_cast<const uint16_t*>(a.v_pool), a.block_table, a.context_lens, a.Hq, a.Hkv, G, HG,
-      a.MB, a.P, a.NP, a.scale * kLog2e);
+  if (a.balanced) {
+    launch_kernel(K_DECODE_PARTITION, decode_balanced_kernel<D, B, OutT>, dim3(a.waves), dim3(64),
+        st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l, a.seg_count,
+        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
+        static_cast<const uint16_t*>(a.v_pool), a.block_table, a.context_lens, a.S, a.Hq, a.Hkv, G,
+        HG, a.MB, a.KMAX, a.min_tiles, a.scale * kLog2e);
+    return;
+  }
+  dim3 grid(a.Hkv * HG, a.S, a.NP);
+  if (a.NP > 1)
+    launch_kernel(K_DECODE_PARTITION, decode_fixed_kernel<D, B, true, OutT>, dim3(grid), dim3(64),
+        st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l,
+        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
+        static_cast<const uint16_t*>(a.v_pool), a.block_table, a.context_lens, a.Hq, a.Hkv, G, HG,
+        a.MB, a.P, a.NP, a.scale * kLog2e);
+  else
+    launch_kernel(K_DECODE_PARTITION, decode_fixed_kernel<D, B, false, OutT>, dim3(grid), dim3(64),
+        st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l,
+        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
+        static_cast<const uint16_t*>(a.v_pool), a.block_table, a.context_lens, a.Hq, a.Hkv, G, HG,
+        a.MB, a.P, a.NP, a.scale * kLog2e);
 }
 
 template <int D, int B, bool SPLIT, typename OutT>
 static void launch_f32(const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.S, a.Hq, a.NP);
-  attn_f32_kernel<D, B, SPLIT, false, OutT><<<grid, 64, 0, st>>>(
-      static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l, static_cast<const float*>(a.q),
+  launch_kernel(K_DECODE_PARTITION, attn_f32_kernel<D, B, SPLIT, false, OutT>, dim3(grid), dim3(64),
+      st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l, static_cast<const float*>(a.q),
       static_cast<const float*>(a.k_pool), static_cast<const float*>(a.v_pool), a.block_table,
       a.context_lens, nullptr, a.S, a.Hq, a.Hkv, a.MB, a.P, a.NP, a.scale * kLog2e);
 }
 
-template <int D, int B, bool SPLIT>
-static void dispatch_out(const DecodeArgs& a, hipStream_t st) {
+template <int D, int B, typename OutT>
+static void dispatch_out_t(const DecodeArgs& a, hipStream_t st) {
   if (a.bf16_in) {
-    if (a.bf16_out) launch_bf16<D, B, SPLIT, uint16_t>(a, st);
-    else launch_bf16<D, B, SPLIT, float>(a, st);
+    launch_bf16<D, B, OutT>(a, st);
   } else {
-    if (a.bf16_out) launch_f32<D, B, SPLIT, uint16_t>(a, st);
-    else launch_f32<D, B, SPLIT, float>(a, st);
+    if (a.NP > 1) launch_f32<D, B, true, OutT>(a, st);
+    else launch_f32<D, B, false, OutT>(a, st);
   }
 }
 
 template <int D, int B>
-static void dispatch_split(const DecodeArgs& a, hipStream_t st) {
-  if (a.NP > 1) dispatch_out<D, B, true>(a, st);
-  else dispatch_out<D, B, false>(a, st);
+static void dispatch_out(const DecodeArgs& a, hipStream_t st) {
+  if (a.bf16_out) dispatch_out_t<D, B, uint16_t>(a, st);
+  else dispatch_out_t<D, B, float>(a, st);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
-  timing_begin(K_DECODE_PARTITION, st);
   if (a.D == 128) {
-    if (a.B == 16) dispatch_split<128, 16>(a, st);
-    else dispatch_split<128, 32>(a, st);
+    if (a.B == 16) dispatch_out<128, 16>(a, st);
+    else dispatch_out<128, 32>(a, st);
   } else {
-    if (a.B == 16) dispatch_split<64, 16>(a, st);
-    else dispatch_split<64, 32>(a, st);
+    if (a.B == 16) dispatch_out<64, 16>(a, st);
+    else dispatch_out<64, 32>(a, st);
   }
   hipError_t e = hipGetLastError();
-  timing_end(K_DECODE_PARTITION, st);
-  if (e != hipSuccess || a.NP <= 1) return e;
-  timing_begin(K_DECODE_REDUCE, st);
+  if (e != hipSuccess || (!a.balanced && a.NP <= 1)) return e;
+  const int G = a.Hq / a.Hkv;
+  const int HG = (G + 15) / 16;
+  const int kmax = a.balanced ? a.KMAX : a.NP;
+  const int32_t* cnt = a.balanced ? a.seg_count : nullptr;
   dim3 grid(a.Hq, a.S);
   if (a.bf16_out)
-    decode_reduce_kernel<uint16_t><<<grid, 64, 0, st>>>(static_cast<uint16_t*>(a.out), a.part_o,
-                                                        a.part_m, a.part_l, a.context_lens,
-                                                        a.Hq, a.D, a.P, a.NP);
+    launch_kernel(K_DECODE_REDUCE, decode_reduce_kernel<uint16_t>, dim3(grid), dim3(64), st,
+        static_cast<uint16_t*>(a.out), a.part_o, a.part_m, a.part_l, a.context_lens, cnt, a.Hq, G,
+        HG, a.D, a.P, kmax);
   else
-    decode_reduce_kernel<float><<<grid, 64, 0, st>>>(static_cast<float*>(a.out), a.part_o,
-                                                     a.part_m, a.part_l, a.context_lens, a.Hq,
-                                                     a.D, a.P, a.NP);
+    launch_kernel(K_DECODE_REDUCE, decode_reduce_kernel<float>, dim3(grid), dim3(64), st,
+        static_cast<float*>(a.out), a.part_o, a.part_m, a.part_l, a.context_lens, cnt, a.Hq, G, HG,
+        a.D, a.P, kmax);
   e = hipGetLastError();
-  timing_end(K_DECODE_REDUCE, st);
   return e;
 }
 
@@ -416,7 +650,7 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st);
 template <int D, int B, typename OutT>
 static void launch_prefill_f32_t(const PrefillArgs& a, hipStream_t st) {
   dim3 grid(a.total_q, a.Hq, 1);
-  attn_f32_kernel<D, B, false, true, OutT><<<grid, 64, 0, st>>>(
+  launch_kernel(K_PREFILL, attn_f32_kernel<D, B, false, true, OutT>, dim3(grid), dim3(64), st,
       static_cast<OutT*>(a.out), nullptr, nullptr, nullptr, static_cast<const float*>(a.q),
       static_cast<const float*>(a.k_pool), static_cast<const float*>(a.v_pool), a.block_table,
       a.context_lens, a.cu_q_lens, a.S, a.Hq, a.Hkv, a.MB, 1 << 30, 1, a.scale * kLog2e);

@@ -48,20 +48,18 @@ hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream) {
   const int vec = 16 / a.elem_bytes;
   const int chunks = a.Hkv * (a.D / vec);
   const int threads = chunks >= 256 ? 256 : ((chunks + 63) / 64) * 64;
-  timing_begin(K_KV_WRITE, stream);
   if (a.elem_bytes == 2) {
-    kv_write_kernel<uint16_t><<<a.T, threads, 0, stream>>>(
+    launch_kernel(K_KV_WRITE, kv_write_kernel<uint16_t>, dim3(a.T), dim3(threads), stream,
         static_cast<const uint16_t*>(a.k_new), static_cast<const uint16_t*>(a.v_new),
-        static_cast<uint16_t*>(a.k_pool), static_cast<uint16_t*>(a.v_pool), a.slot_mapping,
-        a.Hkv, a.D, a.B);
-  } else {
-    kv_write_kernel<float><<<a.T, threads, 0, stream>>>(
-        static_cast<const float*>(a.k_new), static_cast<const float*>(a.v_new),
-        static_cast<float*>(a.k_pool), static_cast<float*>(a.v_pool), a.slot_mapping, a.Hkv,
+        static_cast<uint16_t*>(a.k_pool), static_cast<uint16_t*>(a.v_pool), a.slot_mapping, a.Hkv,
         a.D, a.B);
+  } else {
+    launch_kernel(K_KV_WRITE, kv_write_kernel<float>, dim3(a.T), dim3(threads), stream,
+        static_cast<const float*>(a.k_new), static_cast<const float*>(a.v_new),
+        static_cast<float*>(a.k_pool), static_cast<float*>(a.v_pool), a.slot_mapping, a.Hkv, a.D,
+        a.B);
   }
   hipError_t e = hipGetLastError();
-  timing_end(K_KV_WRITE, stream);
   return e;
 }
 

@@ -2,6 +2,7 @@
 // Arguments arrive validated; each launcher only computes its grid and launches.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -18,9 +19,24 @@ enum KernelId {
 };
 const char* kernel_name(int id);
 
-// Called by launchers around every kernel launch (no-ops unless timing is enabled).
-void timing_begin(int id, hipStream_t stream);
-void timing_end(int id, hipStream_t stream);
+// Timing: when kernel `id` is being timed, a pair of events (registered with the timing
+// registry) that the launch records as part of the kernel dispatch; otherwise nulls.
+struct TimingEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+TimingEvents timing_events(int id);
+
+// Every kernel of the library is launched through here: hipExtLaunchKernel takes the timing
+// events with the dispatch itself, so timing adds no packets between kernels.
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel(int id, void (*kernel)(KArgs...), dim3 grid, dim3 block,
+                         hipStream_t stream, Args... args) {
+  const TimingEvents ev = timing_events(id);
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev.start, ev.stop, 0,
+                        static_cast<KArgs>(args)...);
+  return hipGetLastError();
+}
 
 struct KvWriteArgs {
   const void* k_new;
@@ -42,11 +58,19 @@ struct DecodeArgs {
   int S, Hq, Hkv, D, B, MB, NB;
   float scale;
   int max_ctx;   // resolved host bound
-  int P;         // resolved partition size (tokens)
-  int NP;        // ceil(max_ctx / P); 1 => no partials
-  float* part_o; // [S][Hq][NP][D]
-  float* part_m; // [S][Hq][NP]
-  float* part_l; // [S][Hq][NP]
+  // Fixed partitions (balanced == 0): P tokens each, NP = ceil(max_ctx / P); NP == 1 stores no
+  // partials. Balanced split (balanced == 1): `waves` waves share the batch's 32-token tiles
+  // equally, each taking at least min_tiles; a row has at most KMAX partials.
+  int balanced;
+  int P;
+  int NP;
+  int waves;
+  int min_tiles;
+  int KMAX;
+  float* part_o;       // [S][Hq][NP or KMAX][D]
+  float* part_m;       // [S][Hq][NP or KMAX]
+  float* part_l;       // [S][Hq][NP or KMAX]
+  int32_t* seg_count;  // [S][Hkv][ceil(G/16)] (balanced)
   int bf16_in;
   int bf16_out;
 };

@@ -175,7 +175,7 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
     float rmax = x[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) rmax = fmaxf(rmax, x[i]);
-    rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+    rmax = xor32_max(rmax);
     const float mnew = fmaxf(m, rmax);
     const float alpha = fast_exp2(m - mnew);
     m = mnew;
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
   }
 
   if (!wave_active) return;
-  l += __shfl_xor(l, 32);
+  l = xor32_sum(l);
   if (!row_valid) return;
   const float inv = 1.0f / l;
   OutT* o = out + (static_cast<int64_t>(q0 + my_i) * Hq + head) * D + 4 * hb;
@@ -232,10 +232,10 @@ static void launch_t(const PrefillArgs& a, hipStream_t st) {
   const int n_tiles = (a.max_q_len + WGT - 1) / WGT;
   const int n_groups = G / HW;
   dim3 grid(n_tiles, a.Hkv * n_groups, a.S);
-  prefill_bf16_kernel<D, B, OutT><<<grid, 256, 0, st>>>(
+  launch_kernel(K_PREFILL, prefill_bf16_kernel<D, B, OutT>, dim3(grid), dim3(256), st,
       static_cast<OutT*>(a.out), static_cast<const uint16_t*>(a.q), a.cu_q_lens, a.context_lens,
-      static_cast<const uint16_t*>(a.k_pool), static_cast<const uint16_t*>(a.v_pool),
-      a.block_table, a.Hq, a.Hkv, G, HW, a.MB, n_tiles, n_groups, a.scale * kLog2eP);
+      static_cast<const uint16_t*>(a.k_pool), static_cast<const uint16_t*>(a.v_pool), a.block_table,
+      a.Hq, a.Hkv, G, HW, a.MB, n_tiles, n_groups, a.scale * kLog2eP);
 }
 
 template <int D, int B>
@@ -246,7 +246,6 @@ static void launch_out(const PrefillArgs& a, hipStream_t st) {
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   if (a.total_q == 0 || a.max_q_len == 0) return hipSuccess;
-  timing_begin(K_PREFILL, st);
   hipError_t e;
   if (!a.bf16_in) {
     e = launch_prefill_f32(a, st);
@@ -260,7 +259,6 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
     }
     e = hipGetLastError();
   }
-  timing_end(K_PREFILL, st);
   return e;
 }
 

@@ -65,6 +65,7 @@ def _decode(**kw):
     (dict(S=-1), bd.PKV_ERR_INVALID_ARG),
     (dict(MB=0), bd.PKV_ERR_INVALID_ARG),
     (dict(P=16), bd.PKV_ERR_WORKSPACE),                      # 8 partitions need partials
+    (dict(P=0), bd.PKV_ERR_WORKSPACE),                       # balanced split needs one too
     (dict(P=16, ws=FAKE, ws_bytes=10), bd.PKV_ERR_WORKSPACE),
     (dict(S=0, q=None), bd.PKV_OK),                          # empty batch: nothing to do
 ])
@@ -109,23 +110,30 @@ def test_prefill_validation():
 
 def test_partition_and_workspace_sizes():
     L = bd.lib()
+    BF16, F32 = bd.PKV_BF16, bd.PKV_F32
     # explicit partition sizes are kept; bad ones are refused
-    assert L.pkv_decode_partition_size(256, 64, 8, 4096) == 256
-    assert L.pkv_decode_partition_size(24, 64, 8, 4096) == -1
-    assert L.pkv_decode_partition_size(-16, 64, 8, 4096) == -1
-    # default: 512 when there is plenty of work, smaller for small batches
-    assert L.pkv_decode_partition_size(0, 64, 8, 4096) == 512
-    small = L.pkv_decode_partition_size(0, 1, 1, 4096)
+    assert L.pkv_decode_partition_size(256, 64, 8, 4096, BF16) == 256
+    assert L.pkv_decode_partition_size(24, 64, 8, 4096, BF16) == -1
+    assert L.pkv_decode_partition_size(-16, 64, 8, 4096, F32) == -1
+    # default: balanced split for bf16; fixed partitions for fp32
+    assert L.pkv_decode_partition_size(0, 64, 8, 4096, BF16) == 0
+    assert L.pkv_decode_partition_size(0, 64, 8, 4096, F32) == 512
+    small = L.pkv_decode_partition_size(0, 1, 1, 4096, F32)
     assert 64 <= small < 512 and small % 16 == 0
-    # one partition -> no workspace
-    assert L.pkv_decode_workspace_size(4, 8, 8, 64, 100, 512) == 0
-    # S * Hq * NP * (D + 2) floats
-    assert L.pkv_decode_workspace_size(4, 8, 8, 64, 100, 16) == 4 * 8 * 7 * (64 + 2) * 4
+    # fixed, one partition -> no workspace
+    assert L.pkv_decode_workspace_size(4, 8, 8, 64, 100, 512, F32) == 0
+    # fixed: S * Hq * NP * (D + 2) floats
+    assert L.pkv_decode_workspace_size(4, 8, 8, 64, 100, 16, F32) == 4 * 8 * 7 * (64 + 2) * 4
+    # balanced: partials for ceil(ceil(max_ctx/32)/8)+1 pieces per row, plus segment counts
+    kmax = -(-(-(-4096 // 32)) // 8) + 1
+    ws = L.pkv_decode_workspace_size(64, 32, 8, 128, 4096, 0, BF16)
+    assert ws >= 64 * 32 * kmax * (128 + 2) * 4 + 64 * 8 * 4
+    assert ws < 64 * 32 * kmax * (128 + 2) * 4 + 64 * 8 * 4 + 4 * 256
 
 
 def test_profile_registry_host_side():
     L = bd.lib()
-    assert L.pkv_profile_enable(1) == bd.PKV_OK
+    assert L.pkv_profile_enable(-1) == bd.PKV_OK
     names = L.pkv_profile_kernel_names().decode().split(",")
     assert "decode_partition" in names and "prefill_chunk" in names
     for n in names:
