@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+COPY_BYTES = 256 << 20          # calibration copy: reads and writes this many bytes
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 WORKLOADS = {
@@ -150,6 +151,14 @@ def run(args):
                                              max_q_len=w.max_q_len,
                                              max_context_len=w.max_context_len)
 
+    if args.calibrate_copy:
+        # A plain device copy of known size, for scaling rocprofv3's byte counters.
+        src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -306,6 +315,130 @@ def cpu_baseline(w, budget_s):
                           f"float64 NumPy, BLAS limited to 1 thread)"}
 
 
+# ------------------------------------------------------------------- rocprofv3 summaries
+
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/trace_{w} -o run -- "
+             "python3 bench.py --workload {w} --steps 20 --warmup 5 --no-cpu-baseline")
+PMC_CMD = ("rocprofv3 --pmc {c} -f csv -d gpurun_out/pmc_{c}_{w} -o run -- python3 bench.py "
+           "--workload {w} --steps 10 --warmup 2 --no-cpu-baseline --calibrate-copy")
+
+
+def _csv(path):
+    import csv
+    return list(csv.DictReader(open(path)))
+
+
+def _find(d, suffix):
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise FileNotFoundError(f"no *{suffix} under {d}")
+
+
+def _short(name):
+    return name.split("(")[0].replace("void ", "").replace("pkv::", "")
+
+
+def summarize_trace(d, workload):
+    rows = _csv(_find(d, "kernel_stats.csv"))
+    cmd = TRACE_CMD.format(w=workload)
+    out = [f"# Kernel durations, workload {workload}", "",
+           "rocprofv3 kernel trace of `bench.py` on one MI355X (gfx950).", "",
+           f"Command (from the repository root): `{cmd}`", "",
+           "| kernel | calls | average us | min us | max us | share of GPU time |",
+           "|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} "
+                   f"| {float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                   f"{float(r['Percentage']):.1f}% |")
+    out += ["", "`__amd_rocclr_copyBuffer` is the set-up copies of the inputs to the device "
+            "(not timed by the bench)."]
+    path = os.path.join(ROOT, "profiles", f"kernels_{workload}.md")
+    open(path, "w").write("\n".join(out) + "\n")
+    return path
+
+
+def _dispatches(path):
+    """{dispatch id: (kernel name, counter value)} from a rocprofv3 counter_collection.csv."""
+    return {int(r["Dispatch_Id"]): (_short(r["Kernel_Name"]), float(r["Counter_Value"]))
+            for r in _csv(path)}
+
+
+def summarize_pmc(fetch_dir, write_dir, workload, dominant):
+    """Both runs execute the same program, so dispatch ids match across them. The calibration
+    copies are the device copies whose WRITE_SIZE is the copy size."""
+    fetch = _dispatches(_find(fetch_dir, "counter_collection.csv"))
+    write = _dispatches(_find(write_dir, "counter_collection.csv"))
+    copy_kib = COPY_BYTES / 1024
+    calib = [i for i, (k, v) in write.items()
+             if "copy" in k.lower() and abs(v - copy_kib) < 1e-3 * copy_kib and i in fetch]
+    if not calib:
+        raise RuntimeError("no calibration copy found (run bench.py with --calibrate-copy)")
+    f_scale = copy_kib / (sum(fetch[i][1] for i in calib) / len(calib))
+    w_scale = copy_kib / (sum(write[i][1] for i in calib) / len(calib))
+    per = {}
+    for i, (k, fv) in fetch.items():
+        wv = write.get(i, (k, 0.0))[1]
+        per.setdefault(k, []).append((fv, wv))
+    out = [f"# HBM traffic per dispatch, workload {workload}", "",
+           "rocprofv3 counters on one MI355X (gfx950), one run per counter:", "",
+           f"- `{PMC_CMD.format(c='FETCH_SIZE', w=workload)}`",
+           f"- `{PMC_CMD.format(c='WRITE_SIZE', w=workload)}`", "",
+           f"Scale: the {len(calib)} calibration copies of {COPY_BYTES >> 20} MiB (device to "
+           f"device) read {copy_kib / f_scale:.0f} KiB and write {copy_kib / w_scale:.0f} KiB each "
+           f"by these counters, so FETCH_SIZE is multiplied by {f_scale:.4f} and WRITE_SIZE by "
+           f"{w_scale:.4f}.", "",
+           "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled bytes |",
+           "|---|---|---|---|---|"]
+    avg = {}
+    for k, v in per.items():
+        fv = sum(x for x, _ in v) / len(v)
+        wv = sum(y for _, y in v) / len(v)
+        avg[k] = (fv * f_scale + wv * w_scale) * 1024
+        out.append(f"| `{k}` | {len(v)} | {fv:.0f} | {wv:.0f} | {avg[k]:.4g} |")
+    dom = next(k for k in per if k.startswith(dominant))
+    out += ["", "(`__amd_rocclr_copyBuffer` rows mix the input set-up copies and the calibration "
+            "copies.)", "", f"dominant kernel: `{dom}`",
+            f"traffic_bytes_per_launch: {avg[dom]:.6g}",
+            f"kernel_sources_sha256: {kernel_sources_sha()}"]
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    open(path, "w").write("\n".join(out) + "\n")
+    return path
+
+
+MFMA_CMD = ("rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES "
+            "GRBM_GUI_ACTIVE -f csv -d gpurun_out/pmc_mfma_{w} -o run -- python3 bench.py "
+            "--workload {w} --steps 10 --warmup 2 --no-cpu-baseline")
+
+
+def summarize_mfma(d, workload):
+    """MFMA utilisation = busy cycles / (GUI-active cycles of one XCD x 1024 SIMDs); the
+    GRBM_GUI_ACTIVE value rocprofv3 reports is summed over the 8 XCDs."""
+    rows = _csv(_find(d, "counter_collection.csv"))
+    per = {}
+    for r in rows:
+        k = _short(r["Kernel_Name"])
+        per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    out = [f"# MFMA utilisation, workload {workload}", "",
+           f"Command (from the repository root): `{MFMA_CMD.format(w=workload)}`", "",
+           "| kernel | dispatches | MFMA bf16 MOPs (x512 flops) | busy cycles | GUI active "
+           "(sum of 8 XCDs) | MFMA busy % | bf16 flops per dispatch |",
+           "|---|---|---|---|---|---|---|"]
+    for k, c in per.items():
+        mops = sum(c["SQ_INSTS_VALU_MFMA_MOPS_BF16"]) / len(c["SQ_INSTS_VALU_MFMA_MOPS_BF16"])
+        if mops == 0:
+            continue
+        busy = sum(c["SQ_VALU_MFMA_BUSY_CYCLES"]) / len(c["SQ_VALU_MFMA_BUSY_CYCLES"])
+        gui = sum(c["GRBM_GUI_ACTIVE"]) / len(c["GRBM_GUI_ACTIVE"])
+        util = 100 * busy / ((gui / 8) * 1024)
+        out.append(f"| `{k}` | {len(c['GRBM_GUI_ACTIVE'])} | {mops:.4g} | {busy:.4g} | "
+                   f"{gui:.4g} | {util:.1f} | {mops * 512:.4g} |")
+    path = os.path.join(ROOT, "profiles", f"mfma_{workload}.md")
+    open(path, "w").write("\n".join(out) + "\n")
+    return path
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -317,7 +450,25 @@ def main():
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a 256 MiB device copy first (scale for rocprofv3 byte counters)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="write profiles/kernels_<workload>.md from a rocprofv3 kernel trace")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic_<workload>.md from FETCH_SIZE / WRITE_SIZE runs")
+    ap.add_argument("--summarize-mfma", metavar="DIR",
+                    help="write profiles/mfma_<workload>.md from an MFMA counter run")
     args = ap.parse_args()
+    if args.summarize_mfma:
+        print(summarize_mfma(args.summarize_mfma, args.workload))
+    if args.summarize_trace or args.summarize_pmc:
+        if args.summarize_trace:
+            print(summarize_trace(args.summarize_trace, args.workload))
+        if args.summarize_pmc:
+            dom = "prefill" if args.workload == "prefill-chunk" else "decode_balanced"
+            print(summarize_pmc(*args.summarize_pmc, args.workload, dom))
+    if args.summarize_trace or args.summarize_pmc or args.summarize_mfma:
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the paged-attention kernels shard by sequence or KV head without any exchange; "
