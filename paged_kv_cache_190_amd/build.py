@@ -26,7 +26,10 @@ SOURCES = ["api.cpp", "kv_write.hip", "decode.hip", "prefill.hip"]
 
 # Packed-fp32 VALU instructions are disabled for the device pass; hipcc -O3 would otherwise
 # form them from plain float code. The host pass warns that it does not know the feature.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# MFMA accumulators are kept in ordinary VGPRs: the softmax rescales them every few tiles, and
+# in AGPRs each rescale would cost a read, a multiply and a write per element.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include")]
 

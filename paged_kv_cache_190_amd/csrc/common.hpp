@@ -26,8 +26,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   __bf16 b = static_cast<__bf16>(x);
   return __builtin_bit_cast(uint16_t, b);
 }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// Two values in one v_cvt_pk_bf16_f32 (lo in bits 15:0).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

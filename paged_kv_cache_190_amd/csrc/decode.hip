@@ -569,7 +569,7 @@ static void launch_bf16(const DecodeArgs& a, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   const int HG = (G + 15) / 16;
   if (a.balanced) {
-    launch_kernel(K_DECODE_PARTITION, decode_balanced_kernel<D, B, OutT>, dim3(a.waves), dim3(64),
+    (void)launch_kernel(K_DECODE_PARTITION, decode_balanced_kernel<D, B, OutT>, dim3(a.waves), dim3(64),
         st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l, a.seg_count,
         static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
         static_cast<const uint16_t*>(a.v_pool), a.block_table, a.context_lens, a.S, a.Hq, a.Hkv, G,
@@ -578,13 +578,13 @@ static void launch_bf16(const DecodeArgs& a, hipStream_t st) {
   }
   dim3 grid(a.Hkv * HG, a.S, a.NP);
   if (a.NP > 1)
-    launch_kernel(K_DECODE_PARTITION, decode_fixed_kernel<D, B, true, OutT>, dim3(grid), dim3(64),
+    (void)launch_kernel(K_DECODE_PARTITION, decode_fixed_kernel<D, B, true, OutT>, dim3(grid), dim3(64),
         st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l,
         static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
         static_cast<const uint16_t*>(a.v_pool), a.block_table, a.context_lens, a.Hq, a.Hkv, G, HG,
         a.MB, a.P, a.NP, a.scale * kLog2e);
   else
-    launch_kernel(K_DECODE_PARTITION, decode_fixed_kernel<D, B, false, OutT>, dim3(grid), dim3(64),
+    (void)launch_kernel(K_DECODE_PARTITION, decode_fixed_kernel<D, B, false, OutT>, dim3(grid), dim3(64),
         st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l,
         static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
         static_cast<const uint16_t*>(a.v_pool), a.block_table, a.context_lens, a.Hq, a.Hkv, G, HG,
@@ -594,7 +594,7 @@ static void launch_bf16(const DecodeArgs& a, hipStream_t st) {
 template <int D, int B, bool SPLIT, typename OutT>
 static void launch_f32(const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.S, a.Hq, a.NP);
-  launch_kernel(K_DECODE_PARTITION, attn_f32_kernel<D, B, SPLIT, false, OutT>, dim3(grid), dim3(64),
+  (void)launch_kernel(K_DECODE_PARTITION, attn_f32_kernel<D, B, SPLIT, false, OutT>, dim3(grid), dim3(64),
       st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l, static_cast<const float*>(a.q),
       static_cast<const float*>(a.k_pool), static_cast<const float*>(a.v_pool), a.block_table,
       a.context_lens, nullptr, a.S, a.Hq, a.Hkv, a.MB, a.P, a.NP, a.scale * kLog2e);
@@ -632,11 +632,11 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   const int32_t* cnt = a.balanced ? a.seg_count : nullptr;
   dim3 grid(a.Hq, a.S);
   if (a.bf16_out)
-    launch_kernel(K_DECODE_REDUCE, decode_reduce_kernel<uint16_t>, dim3(grid), dim3(64), st,
+    (void)launch_kernel(K_DECODE_REDUCE, decode_reduce_kernel<uint16_t>, dim3(grid), dim3(64), st,
         static_cast<uint16_t*>(a.out), a.part_o, a.part_m, a.part_l, a.context_lens, cnt, a.Hq, G,
         HG, a.D, a.P, kmax);
   else
-    launch_kernel(K_DECODE_REDUCE, decode_reduce_kernel<float>, dim3(grid), dim3(64), st,
+    (void)launch_kernel(K_DECODE_REDUCE, decode_reduce_kernel<float>, dim3(grid), dim3(64), st,
         static_cast<float*>(a.out), a.part_o, a.part_m, a.part_l, a.context_lens, cnt, a.Hq, G, HG,
         a.D, a.P, kmax);
   e = hipGetLastError();
@@ -650,7 +650,7 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st);
 template <int D, int B, typename OutT>
 static void launch_prefill_f32_t(const PrefillArgs& a, hipStream_t st) {
   dim3 grid(a.total_q, a.Hq, 1);
-  launch_kernel(K_PREFILL, attn_f32_kernel<D, B, false, true, OutT>, dim3(grid), dim3(64), st,
+  (void)launch_kernel(K_PREFILL, attn_f32_kernel<D, B, false, true, OutT>, dim3(grid), dim3(64), st,
       static_cast<OutT*>(a.out), nullptr, nullptr, nullptr, static_cast<const float*>(a.q),
       static_cast<const float*>(a.k_pool), static_cast<const float*>(a.v_pool), a.block_table,
       a.context_lens, a.cu_q_lens, a.S, a.Hq, a.Hkv, a.MB, 1 << 30, 1, a.scale * kLog2e);

@@ -49,12 +49,12 @@ hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream) {
   const int chunks = a.Hkv * (a.D / vec);
   const int threads = chunks >= 256 ? 256 : ((chunks + 63) / 64) * 64;
   if (a.elem_bytes == 2) {
-    launch_kernel(K_KV_WRITE, kv_write_kernel<uint16_t>, dim3(a.T), dim3(threads), stream,
+    (void)launch_kernel(K_KV_WRITE, kv_write_kernel<uint16_t>, dim3(a.T), dim3(threads), stream,
         static_cast<const uint16_t*>(a.k_new), static_cast<const uint16_t*>(a.v_new),
         static_cast<uint16_t*>(a.k_pool), static_cast<uint16_t*>(a.v_pool), a.slot_mapping, a.Hkv,
         a.D, a.B);
   } else {
-    launch_kernel(K_KV_WRITE, kv_write_kernel<float>, dim3(a.T), dim3(threads), stream,
+    (void)launch_kernel(K_KV_WRITE, kv_write_kernel<float>, dim3(a.T), dim3(threads), stream,
         static_cast<const float*>(a.k_new), static_cast<const float*>(a.v_new),
         static_cast<float*>(a.k_pool), static_cast<float*>(a.v_pool), a.slot_mapping, a.Hkv, a.D,
         a.B);

@@ -35,19 +35,44 @@ __device__ __forceinline__ u32x4 lds16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations are outstanding and
+// leaves the other counters alone (gfx9 encoding: vmcnt split over bits 3:0 and 15:14).
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// XOR swizzles of the 16-byte chunks of the LDS tiles. The DMA writes each wave's 64 lanes to
+// 1 KiB of consecutive LDS, so rows cannot be padded; instead a row's chunks are permuted so
+// that the sixteen lanes a 128-bit LDS read serves together (64 banks x 4 bytes) hit sixteen
+// different 16-byte bank groups. K rows are read in the order krow(col) below, i.e. rows
+// {0..3, 16..19, 4..7, 20..23} for lanes 0..15 and {8..11, 24..27, 12..15, 28..31} for lanes
+// 16..31; V rows d in order.
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+  if constexpr (D == 128) return (row & 7) | ((row >> 1) & 8);       // 16 chunks per row
+  else return ((row >> 1) & 3) | ((row >> 2) & 4);                   // 8 chunks, 2 rows per line
+}
+__device__ __forceinline__ int vswz(int d) { return (d >> 2) & 3; }  // 4 chunks, 4 rows per line
+
 template <int D, int B, typename OutT>
 __global__ __launch_bounds__(256) void prefill_bf16_kernel(
     OutT* __restrict__ out, const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q_lens,
     const int32_t* __restrict__ context_lens, const uint16_t* __restrict__ kpool,
     const uint16_t* __restrict__ vpool, const int32_t* __restrict__ block_table, int Hq, int Hkv,
     int G, int HW, int MB, int n_tiles, int n_groups, float scale_log2) {
-  constexpr int KS = D + 8;    // LDS row pitch of the K tile (elements), padded
-  constexpr int VS = 32 + 8;   // LDS row pitch of the V^T tile
-  constexpr int KK = D / 16;   // QK MFMA steps
-  constexpr int DT = D / 32;   // PV output tiles
-  constexpr int CH = D / 64;   // 16-byte chunks per thread per tile (K and V each)
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][32 * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2][D * VS];
+  constexpr int KK = D / 16;             // QK MFMA steps
+  constexpr int DT = D / 32;             // PV output tiles
+  constexpr int NS = 4;                  // pipeline stages (prefetch distance NS - 1)
+  constexpr int KROW = 2 * D;            // bytes of one K row in LDS
+  constexpr int CPR = D / 8;             // 16-byte chunks per K row
+  constexpr int K_BYTES = 32 * KROW;     // K tile [32 keys][D]
+  constexpr int V_BYTES = D * 64;        // V tile [D][32 keys]
+  constexpr int STAGE = K_BYTES + V_BYTES;
+  constexpr int KI = K_BYTES / 4096;     // DMA instructions per thread for K (4 waves x 1 KiB)
+  constexpr int VI = V_BYTES / 4096;
+  constexpr int LPT = KI + VI;           // vector-memory operations per thread per tile
+  constexpr int kIdCap = 2048;           // block ids staged in LDS at a time
+  // One LDS object holds the stages and, after them, the block-id window.
+  __shared__ __attribute__((aligned(16))) unsigned char smem[NS * STAGE + 4 * kIdCap];
+  int32_t* ids = reinterpret_cast<int32_t*>(smem + NS * STAGE);
 
   // XCD-aware numbering (see header comment).
   const int total = n_tiles * gridDim.y * gridDim.z;
@@ -95,52 +120,63 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
       qf[kk] = row_valid ? load16(qrow + 16 * kk) : u32x4{0u, 0u, 0u, 0u};
   }
 
-  // Staging: thread tid copies CH 16-byte chunks of K ([32 keys][D]) and of V^T ([D][32 keys]).
-  u32x4 kreg[CH], vreg[CH];
-  auto stage_load = [&](int t) {
+  // Block ids are staged in LDS, a window of kIdCap logical blocks at a time, so the tile loop
+  // reads them from LDS and issues no vector load of its own (its waits count DMAs only).
+  // Tiles are issued in order; when one needs a block past the window, the window moves: the
+  // pipeline is drained, all waves pass a barrier, and the ids are reloaded.
+  int win = 0;
+  auto load_window = [&](int first) {
+    const int cnt = min(kIdCap, nblk - first);
+    int v[kIdCap / 256];
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const int cid = tid + 256 * j;
-      {  // K chunk: key cid / (D/8), dims 8*(cid % (D/8)) ..
-        const int key = cid / (D / 8);
-        const int dch = (cid % (D / 8)) * 8;
-        const int ka = 32 * t + key;
-        const int lb = min(ka / B, nblk - 1);
-        const int64_t id = bt[lb];
-        u32x4 v = load16(kg + id * blk_stride + (ka % B) * D + dch);
-        if (ka >= n) v = u32x4{0u, 0u, 0u, 0u};
-        kreg[j] = v;
-      }
-      {  // V chunk: dim cid / 4, keys 8*(cid % 4) .. +7
-        const int d = cid >> 2;
-        const int k8 = (cid & 3) * 8;
-        const int ka = 32 * t + k8;
-        const int lb = min(ka / B, nblk - 1);
-        const int64_t id = bt[lb];
-        u32x4 v = load16(vg + id * blk_stride + static_cast<int64_t>(d) * B + (ka % B));
-        const int valid = n - ka;  // keys ka .. ka+7: keep the first `valid`
-        if (valid < 8) {
+    for (int j = 0; j < kIdCap / 256; ++j)  // all loads in flight before any store
+      v[j] = (tid + 256 * j < cnt) ? bt[first + tid + 256 * j] : 0;
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const uint32_t keep =
-                (2 * w < valid ? 0x0000ffffu : 0u) | (2 * w + 1 < valid ? 0xffff0000u : 0u);
-            v[w] &= keep;
-          }
-        }
-        vreg[j] = v;
-      }
-    }
+    for (int j = 0; j < kIdCap / 256; ++j)
+      if (tid + 256 * j < cnt) ids[tid + 256 * j] = v[j];
   };
-  auto stage_store = [&](int buf) {
+  load_window(0);
+  // q and the first ids must have arrived before the tile DMAs start counting in the same
+  // counter; the barrier publishes the ids.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();
+  auto block_id = [&](int lb) -> int64_t { return ids[min(lb, nblk - 1) - win]; };
+
+  // DMA of key tile t into stage t % NS. K: wave instruction j covers physical rows
+  // 4*(KI*wave + j) .. (D = 128); V: 16 dims x 32 keys per instruction. Block ids are
+  // wave-uniform per tile (two candidates when B = 16).
+  auto issue = [&](int t) {
+    unsigned char* st = smem + (t % NS) * STAGE;
+    const int key0 = 32 * t;
+    const int lb0 = key0 / B;
+    if (min(lb0 + 1, nblk - 1) - win >= kIdCap) {  // uniform: every thread issues every tile
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      __syncthreads();
+      win = lb0;
+      load_window(win);
+      __syncthreads();
+    }
+    const int64_t id0 = block_id(lb0);
+    const int64_t id1 = (B == 16) ? block_id(lb0 + 1) : id0;
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const int cid = tid + 256 * j;
-      const int key = cid / (D / 8);
-      const int dch = (cid % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(&ks[buf][key * KS + dch]) = kreg[j];
-      const int d = cid >> 2;
-      const int k8 = (cid & 3) * 8;
-      *reinterpret_cast<u32x4*>(&vs[buf][d * VS + k8]) = vreg[j];
+    for (int j = 0; j < KI; ++j) {
+      const int gidx = KI * wave + j;                 // 1 KiB group within the K tile
+      const int prow = gidx * (64 / CPR) + lane / CPR;
+      const int chunk = (lane % CPR) ^ kswz<D>(prow);
+      const int key = key0 + prow;
+      const int64_t id = (B == 16 && prow >= 16) ? id1 : id0;
+      const uint16_t* src = kg + id * blk_stride + (key % B) * D + 8 * chunk;
+      __builtin_amdgcn_global_load_lds(src, st + gidx * 1024, 16, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < VI; ++j) {
+      const int gidx = VI * wave + j;
+      const int d = gidx * 16 + lane / 4;
+      const int chunk = (lane & 3) ^ vswz(d);        // keys 8*chunk .. 8*chunk+7
+      const int key = key0 + 8 * chunk;
+      const int64_t id = (B == 16 && chunk >= 2) ? id1 : id0;
+      const uint16_t* src = vg + id * blk_stride + static_cast<int64_t>(d) * B + (key % B);
+      __builtin_amdgcn_global_load_lds(src, st + K_BYTES + gidx * 1024, 16, 0, 0);
     }
   };
 
@@ -151,65 +187,102 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
   float m = -INFINITY;
   float l = 0.f;
-  const int qpos = r + my_i;          // this lane's query position
-  const int wq_lo = r + w_tok0;       // the wave's first query position
+  const int qpos = r + my_i;           // this lane's query position
+  const int wq_lo = r + w_tok0;        // the wave's first query position
+  const int klim = min(qpos, n - 1);   // last visible key of this row
   // MFMA row of the K operand -> key within the tile: lane half hb gets keys 16*hb + i.
   const int krow = 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3);
+  const int kbase = krow * KROW;
+  const int kx = kswz<D>(krow);
+  const int vx = vswz(col);
 
-  auto compute = [&](int buf, int t) {
+  auto compute = [&](int t) {
     const int key0 = 32 * t;
     if (!wave_active || key0 > wq_lo + 31) return;  // wholly above the diagonal
+    const unsigned char* st = smem + (t % NS) * STAGE;
     f32x16 sacc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-    const uint16_t* kt = &ks[buf][krow * KS + 8 * hb];
+    u32x4 ka[KK];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) sacc = mfma32x32x16(lds16(kt + 16 * kk), qf[kk], sacc);
+    for (int kk = 0; kk < KK; ++kk)
+      ka[kk] = *reinterpret_cast<const u32x4*>(st + kbase + 16 * ((2 * kk + hb) ^ kx));
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) sacc = mfma32x32x16(ka[kk], qf[kk], sacc);
     float x[16];
-    const bool diag = key0 + 31 > wq_lo;
+    const bool edge = key0 + 31 > wq_lo || key0 + 31 >= n;  // diagonal or past the context
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float v = sacc[i] * scale_log2;
-      x[i] = (diag && key0 + 16 * hb + i > qpos) ? -INFINITY : v;
+      x[i] = (edge && key0 + 16 * hb + i > klim) ? -INFINITY : v;
     }
     float rmax = x[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) rmax = fmaxf(rmax, x[i]);
     rmax = xor32_max(rmax);
-    const float mnew = fmaxf(m, rmax);
-    const float alpha = fast_exp2(m - mnew);
-    m = mnew;
+    // Lazy rescaling: keep the old reference max unless the row's max grows by more than 2^8,
+    // so exponentials stay <= 256 and the output is rescaled only rarely.
+    const bool grow = rmax > m + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float mnew = grow ? rmax : m;
+      const float alpha = fast_exp2(m - mnew);
+      m = mnew;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+    }
     float psum = 0.f;
     u32x4 pb[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float p0 = fast_exp2(x[8 * j + 2 * w] - mnew);
-        const float p1 = fast_exp2(x[8 * j + 2 * w + 1] - mnew);
+        const float p0 = fast_exp2(x[8 * j + 2 * w] - m);
+        const float p1 = fast_exp2(x[8 * j + 2 * w + 1] - m);
         psum += p0 + p1;
         pb[j][w] = pack_bf16x2(p0, p1);
       }
-    l = l * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+    l += psum;
+    u32x4 va[DT][2];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const uint16_t* vt = &vs[buf][(32 * dt + col) * VS + 16 * hb];
+      const unsigned char* vrow = st + K_BYTES + (32 * dt + col) * 64;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[dt] = mfma32x32x16(lds16(vt + 8 * j), pb[j], acc[dt]);
+      for (int j = 0; j < 2; ++j)
+        va[dt][j] = *reinterpret_cast<const u32x4*>(vrow + 16 * ((2 * hb + j) ^ vx));
     }
+    const int vlim = n - key0;  // keys at or past n may hold stale words: clear their V
+    if (vlim < 32) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int k0 = 16 * hb + 8 * j + 2 * w;
+          const uint32_t keep =
+              (k0 < vlim ? 0x0000ffffu : 0u) | (k0 + 1 < vlim ? 0xffff0000u : 0u);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) va[dt][j][w] &= keep;
+        }
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[dt] = mfma32x32x16(va[dt][j], pb[j], acc[dt]);
   };
 
-  stage_load(0);
-  stage_store(0);
-  __syncthreads();
+  // Pipeline: tiles t+1 .. t+NS-2 stay in flight while tile t is waited for; one barrier per
+  // tile both publishes tile t and frees the stage that tile t+NS-1 is then loaded into.
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < ntiles) issue(t);
   for (int t = 0; t < ntiles; ++t) {
-    const bool more = t + 1 < ntiles;
-    if (more) stage_load(t + 1);
-    compute(t & 1, t);
-    if (more) stage_store((t + 1) & 1);
-    __syncthreads();
+    const int ahead = min(NS - 2, ntiles - 1 - t);
+    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPT));
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPT));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_barrier();
+    if (t + NS - 1 < ntiles) issue(t + NS - 1);
+    compute(t);
   }
 
   if (!wave_active) return;
@@ -232,7 +305,7 @@ static void launch_t(const PrefillArgs& a, hipStream_t st) {
   const int n_tiles = (a.max_q_len + WGT - 1) / WGT;
   const int n_groups = G / HW;
   dim3 grid(n_tiles, a.Hkv * n_groups, a.S);
-  launch_kernel(K_PREFILL, prefill_bf16_kernel<D, B, OutT>, dim3(grid), dim3(256), st,
+  (void)launch_kernel(K_PREFILL, prefill_bf16_kernel<D, B, OutT>, dim3(grid), dim3(256), st,
       static_cast<OutT*>(a.out), static_cast<const uint16_t*>(a.q), a.cu_q_lens, a.context_lens,
       static_cast<const uint16_t*>(a.k_pool), static_cast<const uint16_t*>(a.v_pool), a.block_table,
       a.Hq, a.Hkv, G, HW, a.MB, n_tiles, n_groups, a.scale * kLog2eP);
