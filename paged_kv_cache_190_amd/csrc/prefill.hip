@@ -17,9 +17,9 @@
 // K/V tiles are double-buffered in LDS: the next tile is read from HBM into registers while the
 // current one is multiplied, then written to the other buffer. Tiles wholly above a wave's
 // causal diagonal are skipped; only diagonal tiles apply the mask.
-// Workgroups are numbered so that the row tiles of one (sequence, KV head) land on the same XCD
-// (the GPU deals consecutive workgroups round-robin to its eight XCDs, each with its own L2) and
-// the tiles with the most keys start first.
+// Workgroups are numbered so that the XCDs (the GPU deals consecutive workgroups round-robin to
+// its eight XCDs, each with its own L2) get equal shares of the work, with the row tiles of one
+// (sequence, KV head) on the same XCD and the tiles with the most keys first.
 //
 // fp32 prefill runs on the vector kernel in decode.hip.
 #include "common.hpp"
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
     OutT* __restrict__ out, const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q_lens,
     const int32_t* __restrict__ context_lens, const uint16_t* __restrict__ kpool,
     const uint16_t* __restrict__ vpool, const int32_t* __restrict__ block_table, int Hq, int Hkv,
-    int G, int HW, int MB, int n_tiles, int n_groups, float scale_log2) {
+    int G, int HW, int MB, int n_tiles, int n_groups, float scale_log2, int neg_scale) {
   constexpr int KK = D / 16;             // QK MFMA steps
   constexpr int DT = D / 32;             // PV output tiles
   constexpr int NS = 4;                  // pipeline stages (prefetch distance NS - 1)
@@ -74,13 +74,25 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char smem[NS * STAGE + 4 * kIdCap];
   int32_t* ids = reinterpret_cast<int32_t*>(smem + NS * STAGE);
 
-  // XCD-aware numbering (see header comment).
-  const int total = n_tiles * gridDim.y * gridDim.z;
-  int bid = blockIdx.x + n_tiles * (blockIdx.y + gridDim.y * blockIdx.z);
-  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
-  const int tile = n_tiles - 1 - bid % n_tiles;
-  const int gy = (bid / n_tiles) % gridDim.y;
-  const int s = bid / (n_tiles * gridDim.y);
+  // XCD-aware numbering. Workgroup b is dispatched to XCD b % 8, and each XCD works through its
+  // share in order. The (head group, sequence) pairs are dealt round-robin to the XCDs (with 8
+  // KV heads, XCD x takes KV head x of every sequence), so every XCD gets the same mix of
+  // context lengths; all row tiles of a pair stay on one XCD and share its L2; within a pair
+  // the tiles with the most keys start first.
+  const int pairs = gridDim.y * gridDim.z;
+  const int lin = blockIdx.x + n_tiles * (blockIdx.y + gridDim.y * blockIdx.z);
+  int pair, tix;
+  if ((pairs & 7) == 0) {
+    const int k = lin >> 3;
+    pair = (k / n_tiles) * 8 + (lin & 7);
+    tix = k % n_tiles;
+  } else {
+    pair = lin / n_tiles;
+    tix = lin % n_tiles;
+  }
+  const int tile = n_tiles - 1 - tix;
+  const int gy = pair % gridDim.y;
+  const int s = pair / gridDim.y;
 
   const int g = gy / n_groups;
   const int grp = gy - g * n_groups;
@@ -115,9 +127,12 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
     // rows past the chunk load nothing; their address is clamped into the chunk regardless
     const int qi = min(my_i, c - 1);
     const uint16_t* qrow = q + (static_cast<int64_t>(q0 + qi) * Hq + head) * D + 8 * hb;
+    // A negative scale is applied as |scale| on -q (bf16 negation flips the sign bits), so the
+    // scores' maximum can be taken on the raw MFMA results.
+    const uint32_t flip = neg_scale ? 0x80008000u : 0u;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      qf[kk] = row_valid ? load16(qrow + 16 * kk) : u32x4{0u, 0u, 0u, 0u};
+      qf[kk] = row_valid ? (load16(qrow + 16 * kk) ^ flip) : u32x4{0u, 0u, 0u, 0u};
   }
 
   // Block ids are staged in LDS, a window of kIdCap logical blocks at a time, so the tile loop
@@ -209,17 +224,18 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
       ka[kk] = *reinterpret_cast<const u32x4*>(st + kbase + 16 * ((2 * kk + hb) ^ kx));
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) sacc = mfma32x32x16(ka[kk], qf[kk], sacc);
-    float x[16];
+    // Scores stay in raw units until the exponential: the row max is taken on the raw values
+    // (scale_log2 >= 0 keeps the order) and p = 2^(raw * scale_log2 - m) is one fma.
     const bool edge = key0 + 31 > wq_lo || key0 + 31 >= n;  // diagonal or past the context
+    if (edge) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float v = sacc[i] * scale_log2;
-      x[i] = (edge && key0 + 16 * hb + i > klim) ? -INFINITY : v;
+      for (int i = 0; i < 16; ++i)
+        if (key0 + 16 * hb + i > klim) sacc[i] = -INFINITY;
     }
-    float rmax = x[0];
+    float rmax = sacc[0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) rmax = fmaxf(rmax, x[i]);
-    rmax = xor32_max(rmax);
+    for (int i = 1; i < 16; ++i) rmax = fmaxf(rmax, sacc[i]);
+    rmax = xor32_max(rmax) * scale_log2;
     // Lazy rescaling: keep the old reference max unless the row's max grows by more than 2^8,
     // so exponentials stay <= 256 and the output is rescaled only rarely.
     const bool grow = rmax > m + 8.0f;
@@ -237,8 +253,8 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float p0 = fast_exp2(x[8 * j + 2 * w] - m);
-        const float p1 = fast_exp2(x[8 * j + 2 * w + 1] - m);
+        const float p0 = fast_exp2(__builtin_fmaf(sacc[8 * j + 2 * w], scale_log2, -m));
+        const float p1 = fast_exp2(__builtin_fmaf(sacc[8 * j + 2 * w + 1], scale_log2, -m));
         psum += p0 + p1;
         pb[j][w] = pack_bf16x2(p0, p1);
       }
@@ -297,6 +313,8 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
       store_out(o + 32 * dt + 8 * (i >> 2) + (i & 3), acc[dt][i] * inv);
 }
 
+// The kernel takes a positive scale (a negative one flips q; zero becomes a tiny positive value,
+// which keeps masked scores at -inf and gives the uniform softmax of a zero scale).
 template <int D, int B, typename OutT>
 static void launch_t(const PrefillArgs& a, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
@@ -308,7 +326,8 @@ static void launch_t(const PrefillArgs& a, hipStream_t st) {
   (void)launch_kernel(K_PREFILL, prefill_bf16_kernel<D, B, OutT>, dim3(grid), dim3(256), st,
       static_cast<OutT*>(a.out), static_cast<const uint16_t*>(a.q), a.cu_q_lens, a.context_lens,
       static_cast<const uint16_t*>(a.k_pool), static_cast<const uint16_t*>(a.v_pool), a.block_table,
-      a.Hq, a.Hkv, G, HW, a.MB, n_tiles, n_groups, a.scale * kLog2eP);
+      a.Hq, a.Hkv, G, HW, a.MB, n_tiles, n_groups, fmaxf(fabsf(a.scale) * kLog2eP, 1e-30f),
+      a.scale < 0.f ? 1 : 0);
 }
 
 template <int D, int B>

@@ -342,3 +342,27 @@ def test_decode_balanced_wave_counts(waves, monkeypatch):
     d2 = Dev(w2)
     d2.write()
     assert_close(values(d2.decode()), ref2, TOL_BF16, f"balanced split G=16, {waves} waves")
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 1.7])
+def test_scale_variants(scale):
+    """Any finite scale: negative (softmax of the negated scores), zero (uniform weights) and a
+    large one, for decode (balanced and fixed partitions) and prefill."""
+    w = wl.build_decode(130, 3, 32, 8, 128, 16, [40, 700, 1], "bf16")
+    kp, vp = _oracle_written(w)
+    ref = orc.decode(w.q, kp, vp, w.block_table, w.context_lens, scale, "bf16")
+    d = Dev(w)
+    d.write()
+    d.w.scale = scale
+    for P in (0, 64):
+        assert_close(values(d.decode(out_dtype=_torch_dtype("f32"), partition_size=P)), ref,
+                     TOL_BF16, f"decode scale={scale} P={P}")
+    p = wl.build_prefill(131, 2, 32, 8, 128, 16, [70, 0], [45, 33], "bf16")
+    kp, vp = _oracle_written(p)
+    ref = orc.prefill_chunk(p.q, p.cu_q_lens, p.context_lens, kp, vp, p.block_table, scale,
+                            "bf16")
+    dp = Dev(p)
+    dp.write()
+    dp.w.scale = scale
+    assert_close(values(dp.prefill(out_dtype=_torch_dtype("f32"))), ref, TOL_BF16,
+                 f"prefill scale={scale}")
