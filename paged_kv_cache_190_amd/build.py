@@ -60,6 +60,13 @@ def build(verbose: bool = True) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}{res.stderr}")
+    # Load the result with every symbol resolved now, so an unresolved kernel stub fails the
+    # build rather than the first test (dlopen needs no GPU).
+    import ctypes
+    try:
+        ctypes.CDLL(tmp, mode=os.RTLD_NOW)
+    except OSError as e:
+        raise RuntimeError(f"built library does not load: {e}") from e
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
   const int g = gy / n_groups;
   const int grp = gy - g * n_groups;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
   const int lane = tid & 63;
   const int col = lane & 31;
   const int hb = lane >> 5;
@@ -159,11 +159,28 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
 
   // DMA of key tile t into stage t % NS. K: wave instruction j covers physical rows
   // 4*(KI*wave + j) .. (D = 128); V: 16 dims x 32 keys per instruction. Block ids are
-  // wave-uniform per tile (two candidates when B = 16).
+  // wave-uniform per tile (two candidates when B = 16); a lane's offset inside the block tile
+  // does not change from tile to tile (tiles start at multiples of 32, which B divides or
+  // equals), so it is computed once.
+  int koff[KI], voff[VI];
+  bool ksel[KI], vsel[VI];
+#pragma unroll
+  for (int j = 0; j < KI; ++j) {
+    const int prow = (KI * wave + j) * (64 / CPR) + lane / CPR;
+    const int chunk = (lane % CPR) ^ kswz<D>(prow);
+    koff[j] = (prow % B) * D + 8 * chunk;
+    ksel[j] = B == 16 && prow >= 16;
+  }
+#pragma unroll
+  for (int j = 0; j < VI; ++j) {
+    const int d = (VI * wave + j) * 16 + lane / 4;
+    const int chunk = (lane & 3) ^ vswz(d);  // keys 8*chunk .. 8*chunk+7
+    voff[j] = d * B + (8 * chunk) % B;
+    vsel[j] = B == 16 && chunk >= 2;
+  }
   auto issue = [&](int t) {
     unsigned char* st = smem + (t % NS) * STAGE;
-    const int key0 = 32 * t;
-    const int lb0 = key0 / B;
+    const int lb0 = (32 * t) / B;
     if (min(lb0 + 1, nblk - 1) - win >= kIdCap) {  // uniform: every thread issues every tile
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       __syncthreads();
@@ -171,27 +188,21 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
       load_window(win);
       __syncthreads();
     }
-    const int64_t id0 = block_id(lb0);
-    const int64_t id1 = (B == 16) ? block_id(lb0 + 1) : id0;
+    const uint16_t* kb0 = kg + block_id(lb0) * blk_stride;
+    const uint16_t* vb0 = vg + block_id(lb0) * blk_stride;
+    const uint16_t* kb1 = (B == 16) ? kg + block_id(lb0 + 1) * blk_stride : kb0;
+    const uint16_t* vb1 = (B == 16) ? vg + block_id(lb0 + 1) * blk_stride : vb0;
+    // (The source pointer is a named variable: given a conditional expression directly, the
+    // builtin makes clang drop this kernel's host-side launch stub without a diagnostic.)
 #pragma unroll
     for (int j = 0; j < KI; ++j) {
-      const int gidx = KI * wave + j;                 // 1 KiB group within the K tile
-      const int prow = gidx * (64 / CPR) + lane / CPR;
-      const int chunk = (lane % CPR) ^ kswz<D>(prow);
-      const int key = key0 + prow;
-      const int64_t id = (B == 16 && prow >= 16) ? id1 : id0;
-      const uint16_t* src = kg + id * blk_stride + (key % B) * D + 8 * chunk;
-      __builtin_amdgcn_global_load_lds(src, st + gidx * 1024, 16, 0, 0);
+      const uint16_t* src = (ksel[j] ? kb1 : kb0) + koff[j];
+      __builtin_amdgcn_global_load_lds(src, st + (KI * wave + j) * 1024, 16, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < VI; ++j) {
-      const int gidx = VI * wave + j;
-      const int d = gidx * 16 + lane / 4;
-      const int chunk = (lane & 3) ^ vswz(d);        // keys 8*chunk .. 8*chunk+7
-      const int key = key0 + 8 * chunk;
-      const int64_t id = (B == 16 && chunk >= 2) ? id1 : id0;
-      const uint16_t* src = vg + id * blk_stride + static_cast<int64_t>(d) * B + (key % B);
-      __builtin_amdgcn_global_load_lds(src, st + K_BYTES + gidx * 1024, 16, 0, 0);
+      const uint16_t* src = (vsel[j] ? vb1 : vb0) + voff[j];
+      __builtin_amdgcn_global_load_lds(src, st + K_BYTES + (VI * wave + j) * 1024, 16, 0, 0);
     }
   };
 
