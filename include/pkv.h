@@ -75,7 +75,8 @@ typedef enum {
   PKV_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, inconsistent sizes */
   PKV_ERR_UNSUPPORTED = 2, /* dtype / head_dim / block_size / grouping not built */
   PKV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
-  PKV_ERR_HIP = 4          /* a HIP runtime call failed; see pkv_last_error() */
+  PKV_ERR_HIP = 4,         /* a HIP runtime call failed; see pkv_last_error() */
+  PKV_ERR_OUT_OF_BLOCKS = 5 /* block manager: not enough free blocks (nothing was changed) */
 } pkv_status;
 
 typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
@@ -104,6 +105,66 @@ const char* pkv_last_error(void);
 int pkv_kv_cache_write(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
                        const int32_t* slot_mapping, int T, int num_kv_heads, int head_dim,
                        int block_size, int num_blocks, int dtype, void* stream);
+
+/*
+ * pkv_kv_cache_copy_blocks -- copy whole physical blocks between two pools (or inside one).
+ * ["Serving Engines", How vLLM works: copy-on-write -- when one of several sequences sharing a
+ *  block writes into it, only that block is copied and the block tables split there; swap
+ *  preemption moves a sequence's blocks to host memory and back.]
+ *
+ *   src_k, src_v   source pools, layout above (read)
+ *   dst_k, dst_v   destination pools, same layout and dtype (written); may equal the sources
+ *   block_pairs    int32 [n_pairs][2]: (source block, destination block), device-accessible
+ *   src_num_blocks, dst_num_blocks  pool sizes (for the caller's bookkeeping and validation)
+ * For each pair every KV head's K tile and V tile of the destination block becomes a bit copy
+ * of the source block's. Any of the four pools may be pinned host memory (hipHostMalloc):
+ * copying a device pool to a host pool and back is the swap-out / swap-in of preemption.
+ * Preconditions (unchecked, device data): ids within their pools; destination blocks pairwise
+ * distinct; within one pool, no destination is also a source. n_pairs == 0 is a no-op.
+ */
+int pkv_kv_cache_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                             const int32_t* block_pairs, int n_pairs, int num_kv_heads,
+                             int head_dim, int block_size, int src_num_blocks,
+                             int dst_num_blocks, int dtype, void* stream);
+
+/*
+ * Block manager -- host-side allocator of physical blocks with reference counts, for the
+ * bookkeeping around the kernels. ["Serving Engines", How vLLM works: a sequence claims a new
+ * block only when its current one fills; a reference count per block tracks sharing; a write
+ * into a shared block copies that block only. "Inference Engines", PagedAttention: blocks are
+ * freed when the sequence finishes.] Single-writer: not thread-safe.
+ *
+ *   pkv_bm_create(num_blocks, block_size, &bm)  all blocks free; ids handed out lowest first
+ *   pkv_bm_destroy(bm)
+ *   pkv_bm_num_free(bm)                         free blocks
+ *   pkv_bm_add(bm, seq)                         new empty sequence (PKV_ERR_INVALID_ARG if the
+ *                                               id exists)
+ *   pkv_bm_fork(bm, parent, child)              child shares every block of parent (counts+1)
+ *   pkv_bm_append(bm, seq, n, slots, copies, max_copies, &n_copies)
+ *       reserves slots for the next n tokens of seq: slots[i] = block * B + offset of token
+ *       len + i. If the last block is shared and partly filled, it is first copied to a fresh
+ *       block (copy-on-write): the pair (old, new) is written to copies[0..1] and n_copies = 1;
+ *       otherwise n_copies = 0. New blocks are claimed as positions cross block boundaries.
+ *       All or nothing: PKV_ERR_OUT_OF_BLOCKS if the pool cannot supply the blocks.
+ *   pkv_bm_free(bm, seq)                        drops seq; blocks whose count reaches 0 return
+ *                                               to the pool
+ *   pkv_bm_context_len(bm, seq, &len)
+ *   pkv_bm_block_table(bm, seq, table, capacity, &n_blocks)  copies up to capacity ids
+ *   pkv_bm_refcount(bm, block, &count)
+ */
+typedef struct pkv_block_manager pkv_block_manager;
+int pkv_bm_create(int num_blocks, int block_size, pkv_block_manager** out);
+void pkv_bm_destroy(pkv_block_manager* bm);
+int pkv_bm_num_free(const pkv_block_manager* bm);
+int pkv_bm_add(pkv_block_manager* bm, int64_t seq);
+int pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child);
+int pkv_bm_append(pkv_block_manager* bm, int64_t seq, int n_tokens, int32_t* slots,
+                  int32_t* copies, int max_copies, int* n_copies);
+int pkv_bm_free(pkv_block_manager* bm, int64_t seq);
+int pkv_bm_context_len(const pkv_block_manager* bm, int64_t seq, int* len);
+int pkv_bm_block_table(const pkv_block_manager* bm, int64_t seq, int32_t* table, int capacity,
+                       int* n_blocks);
+int pkv_bm_refcount(const pkv_block_manager* bm, int block, int* count);
 
 /*
  * pkv_decode_partition_size -- the fixed partition size, in tokens, that

@@ -86,6 +86,27 @@ def kv_cache_write(k_pool, v_pool, k_new, v_new, slot_mapping, block_size):
     return k_pool, v_pool
 
 
+def kv_cache_copy_blocks(src_k, src_v, dst_k, dst_v, pairs):
+    """Copy whole physical blocks (every KV head, K and V): dst[d] = src[s] for each (s, d).
+
+    ["Serving Engines", How vLLM works]: a copy-on-write fork copies exactly the one block being
+    written before the tables split; the same copy between a device pool and a host pool is the
+    data movement of swap preemption. Returns new (dst_k, dst_v); the inputs are untouched.
+    Source and destination may be the same pool; destinations must be distinct and must not be
+    sources of other pairs.
+    """
+    dst_k = dst_k.copy()
+    dst_v = dst_v.copy()
+    dsts = [int(d) for _, d in pairs]
+    assert len(set(dsts)) == len(dsts), "destination blocks must be distinct"
+    for s_blk, d_blk in pairs:
+        s_blk, d_blk = int(s_blk), int(d_blk)
+        assert 0 <= s_blk < src_k.shape[0] and 0 <= d_blk < dst_k.shape[0]
+        dst_k[d_blk] = src_k[s_blk]
+        dst_v[d_blk] = src_v[s_blk]
+    return dst_k, dst_v
+
+
 # ----------------------------------------------------------------------------- gather
 
 def gather(k_pool, v_pool, bt_row, n, block_size, dtype):

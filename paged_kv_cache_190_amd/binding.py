@@ -17,7 +17,8 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "lib", "libpkv.so")
 
-PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP = range(5)
+(PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP,
+ PKV_ERR_OUT_OF_BLOCKS) = range(6)
 PKV_F32, PKV_BF16 = 0, 1
 
 _lib = None
@@ -63,6 +64,30 @@ def lib() -> ctypes.CDLL:
     L.pkv_profile_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(ctypes.c_longlong)]
     L.pkv_profile_kernel_names.restype = ctypes.c_char_p
+    L.pkv_kv_cache_copy_blocks.restype = i32
+    L.pkv_kv_cache_copy_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                           vp]
+    i64, pi32 = ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)
+    pint = ctypes.POINTER(ctypes.c_int)
+    L.pkv_bm_create.restype = i32
+    L.pkv_bm_create.argtypes = [i32, i32, ctypes.POINTER(vp)]
+    L.pkv_bm_destroy.restype = None
+    L.pkv_bm_destroy.argtypes = [vp]
+    L.pkv_bm_num_free.restype = i32
+    L.pkv_bm_num_free.argtypes = [vp]
+    for name in ("pkv_bm_add", "pkv_bm_free"):
+        getattr(L, name).restype = i32
+        getattr(L, name).argtypes = [vp, i64]
+    L.pkv_bm_fork.restype = i32
+    L.pkv_bm_fork.argtypes = [vp, i64, i64]
+    L.pkv_bm_append.restype = i32
+    L.pkv_bm_append.argtypes = [vp, i64, i32, pi32, pi32, i32, pint]
+    L.pkv_bm_context_len.restype = i32
+    L.pkv_bm_context_len.argtypes = [vp, i64, pint]
+    L.pkv_bm_block_table.restype = i32
+    L.pkv_bm_block_table.argtypes = [vp, i64, pi32, i32, pint]
+    L.pkv_bm_refcount.restype = i32
+    L.pkv_bm_refcount.argtypes = [vp, i32, pint]
     _lib = L
     return L
 
@@ -179,9 +204,107 @@ def paged_attention_prefill_chunk(out, q, cu_q_lens, context_lens, k_pool, v_poo
     return out
 
 
+def _pool(t, name: str):
+    """A pool may live in device memory or in pinned host memory (a swap space)."""
+    if not (t.is_cuda or t.is_pinned()):
+        raise ValueError(f"{name} must be a device tensor or a pinned host tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def kv_cache_copy_blocks(src_k, src_v, dst_k, dst_v, block_pairs, stream=None) -> None:
+    """Copy whole blocks: for each row (s, d) of block_pairs [n][2] (int32, device), block s of
+    src_k/src_v to block d of dst_k/dst_v. Pools are [NB][Hkv][B][D] (K) and [NB][Hkv][D][B] (V)
+    in device memory or pinned host memory; source and destination may be the same pools."""
+    nbs, hkv, b, d = src_k.shape
+    nbd = dst_k.shape[0]
+    if (src_v.shape != (nbs, hkv, d, b) or dst_k.shape[1:] != (hkv, b, d)
+            or dst_v.shape != (nbd, hkv, d, b)):
+        raise ValueError("inconsistent pool shapes")
+    if not (src_k.dtype == src_v.dtype == dst_k.dtype == dst_v.dtype):
+        raise TypeError("pools must share a dtype")
+    if block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [n][2]")
+    n = block_pairs.shape[0]
+    _check(lib().pkv_kv_cache_copy_blocks(
+        _pool(src_k, "src_k"), _pool(src_v, "src_v"), _pool(dst_k, "dst_k"),
+        _pool(dst_v, "dst_v"), _i32(block_pairs, "block_pairs") if n else None, n, hkv, d, b,
+        nbs, nbd, _dtype_code(src_k), _stream(stream)), "kv_cache_copy_blocks")
+
+
+# ------------------------------------------------------------------------------ block manager
+
+class BlockManager:
+    """Host block manager in libpkv: reference-counted physical blocks, per-sequence block
+    tables, copy-on-write when a sequence appends into a shared, partly filled block."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        self._h = ctypes.c_void_p()
+        _check(lib().pkv_bm_create(num_blocks, block_size, ctypes.byref(self._h)),
+               "pkv_bm_create")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def close(self) -> None:
+        if self._h:
+            lib().pkv_bm_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def num_free(self) -> int:
+        return lib().pkv_bm_num_free(self._h)
+
+    def add(self, seq: int) -> None:
+        _check(lib().pkv_bm_add(self._h, seq), "pkv_bm_add")
+
+    def fork(self, parent: int, child: int) -> None:
+        _check(lib().pkv_bm_fork(self._h, parent, child), "pkv_bm_fork")
+
+    def append(self, seq: int, n_tokens: int):
+        """Slots (list of int) for the next n_tokens of seq, and the (src, dst) block copies the
+        caller must make before writing them."""
+        slots = (ctypes.c_int32 * max(n_tokens, 1))()
+        copies = (ctypes.c_int32 * 2)()
+        n_copies = ctypes.c_int()
+        _check(lib().pkv_bm_append(self._h, seq, n_tokens, slots, copies, 1,
+                                   ctypes.byref(n_copies)), "pkv_bm_append")
+        pairs = [(copies[0], copies[1])] if n_copies.value else []
+        return list(slots[:n_tokens]), pairs
+
+    def free(self, seq: int) -> None:
+        _check(lib().pkv_bm_free(self._h, seq), "pkv_bm_free")
+
+    def context_len(self, seq: int) -> int:
+        n = ctypes.c_int()
+        _check(lib().pkv_bm_context_len(self._h, seq, ctypes.byref(n)), "pkv_bm_context_len")
+        return n.value
+
+    def block_table(self, seq: int):
+        n = ctypes.c_int()
+        _check(lib().pkv_bm_block_table(self._h, seq, None, 0, ctypes.byref(n)),
+               "pkv_bm_block_table")
+        table = (ctypes.c_int32 * max(n.value, 1))()
+        _check(lib().pkv_bm_block_table(self._h, seq, table, n.value, ctypes.byref(n)),
+               "pkv_bm_block_table")
+        return list(table[:n.value])
+
+    def refcount(self, block: int) -> int:
+        c = ctypes.c_int()
+        _check(lib().pkv_bm_refcount(self._h, block, ctypes.byref(c)), "pkv_bm_refcount")
+        return c.value
+
+
 # ------------------------------------------------------------------------------ timing
 
-KERNEL_NAMES = ("kv_cache_write", "decode_partition", "decode_reduce", "prefill_chunk")
+KERNEL_NAMES = ("kv_cache_write", "decode_partition", "decode_reduce", "prefill_chunk",
+                "copy_blocks")
 
 
 def profile_enable(on: bool = True, kernels=None) -> None:

@@ -22,7 +22,8 @@ LIB = os.path.join(LIBDIR, "libpkv.so")
 OBJDIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "kv_write.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "block_manager.cpp", "kv_write.hip", "decode.hip", "prefill.hip",
+           "blocks.hip"]
 
 # Packed-fp32 VALU instructions are disabled for the device pass; hipcc -O3 would otherwise
 # form them from plain float code. The host pass warns that it does not know the feature.

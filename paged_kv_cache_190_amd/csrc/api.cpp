@@ -13,13 +13,14 @@
 #include <string>
 #include <vector>
 
+#include "errors.hpp"
 #include "launch.hpp"
 
 namespace {
-
 thread_local std::string g_last_error;
+}  // namespace
 
-int fail(int status, const char* fmt, ...) {
+int pkv::fail(int status, const char* fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -28,6 +29,10 @@ int fail(int status, const char* fmt, ...) {
   g_last_error = buf;
   return status;
 }
+
+namespace {
+
+using pkv::fail;
 
 int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return PKV_OK;
@@ -88,6 +93,7 @@ const char* kernel_name(int id) {
     case K_DECODE_PARTITION: return "decode_partition";
     case K_DECODE_REDUCE: return "decode_reduce";
     case K_PREFILL: return "prefill_chunk";
+    case K_COPY_BLOCKS: return "copy_blocks";
     default: return "?";
   }
 }
@@ -199,6 +205,7 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_HIP: return "HIP runtime error";
+    case PKV_ERR_OUT_OF_BLOCKS: return "not enough free blocks";
     default: return "unknown status";
   }
 }
@@ -224,6 +231,51 @@ int pkv_kv_cache_write(const void* k_new, const void* v_new, void* k_pool, void*
   pkv::KvWriteArgs a{k_new, v_new, k_pool, v_pool, slot_mapping, T, num_kv_heads, head_dim,
                      block_size, num_blocks, elem_bytes(dtype)};
   return hip_status(pkv::launch_kv_write(a, static_cast<hipStream_t>(stream)), "kv_cache_write");
+}
+
+namespace {
+// A pool handed to the copy kernel may be device memory or pinned host memory; anything else
+// (pageable host memory, a stale pointer) would fault in the kernel, so it is refused here.
+// Pinned memory is accepted only where the device sees it at the same address.
+int check_kernel_visible(const void* p, const char* name) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PKV_ERR_INVALID_ARG, "%s is not device or pinned host memory", name);
+  }
+  if (at.type == hipMemoryTypeHost && at.devicePointer != p)
+    return fail(PKV_ERR_INVALID_ARG, "%s: pinned host memory not mapped at the same address",
+                name);
+  if (at.type == hipMemoryTypeUnregistered)
+    return fail(PKV_ERR_INVALID_ARG, "%s is unregistered host memory", name);
+  return PKV_OK;
+}
+}  // namespace
+
+int pkv_kv_cache_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                             const int32_t* block_pairs, int n_pairs, int num_kv_heads,
+                             int head_dim, int block_size, int src_num_blocks,
+                             int dst_num_blocks, int dtype, void* stream) {
+  if (n_pairs < 0) return fail(PKV_ERR_INVALID_ARG, "n_pairs = %d is negative", n_pairs);
+  if (n_pairs == 0) return PKV_OK;
+  if (!src_k || !src_v || !dst_k || !dst_v || !block_pairs)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (num_kv_heads <= 0 || src_num_blocks <= 0 || dst_num_blocks <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_kv_heads and pool sizes must be positive");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", head_dim);
+  if (block_size != 16 && block_size != 32)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %d not in {16, 32}", block_size);
+  if (!supported_dtype(dtype)) return fail(PKV_ERR_UNSUPPORTED, "dtype %d not supported", dtype);
+  if (n_pairs > kMaxGridYZ) return fail(PKV_ERR_UNSUPPORTED, "n_pairs %d too large", n_pairs);
+  const void* ptrs[5] = {src_k, src_v, dst_k, dst_v, block_pairs};
+  const char* names[5] = {"src_k", "src_v", "dst_k", "dst_v", "block_pairs"};
+  for (int i = 0; i < 5; ++i)
+    if (int st = check_kernel_visible(ptrs[i], names[i])) return st;
+  pkv::CopyBlocksArgs a{src_k, src_v, dst_k, dst_v, block_pairs, n_pairs, num_kv_heads,
+                        head_dim, block_size, elem_bytes(dtype)};
+  return hip_status(pkv::launch_copy_blocks(a, static_cast<hipStream_t>(stream)),
+                    "kv_cache_copy_blocks");
 }
 
 int pkv_decode_partition_size(int partition_size, int num_seqs, int num_kv_heads,
@@ -419,7 +471,7 @@ int pkv_profile_read(const char* kernel_name, double* total_ms, long long* launc
 }
 
 const char* pkv_profile_kernel_names(void) {
-  return "kv_cache_write,decode_partition,decode_reduce,prefill_chunk";
+  return "kv_cache_write,decode_partition,decode_reduce,prefill_chunk,copy_blocks";
 }
 
 }  // extern "C"

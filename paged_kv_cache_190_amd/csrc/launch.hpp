@@ -15,7 +15,8 @@ enum KernelId {
   K_DECODE_PARTITION = 1,
   K_DECODE_REDUCE = 2,
   K_PREFILL = 3,
-  K_COUNT = 4
+  K_COPY_BLOCKS = 4,
+  K_COUNT = 5
 };
 const char* kernel_name(int id);
 
@@ -47,6 +48,16 @@ struct KvWriteArgs {
   int T, Hkv, D, B, NB, elem_bytes;
 };
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
+
+struct CopyBlocksArgs {
+  const void* src_k;
+  const void* src_v;
+  void* dst_k;
+  void* dst_v;
+  const int32_t* pairs;
+  int n_pairs, Hkv, D, B, elem_bytes;
+};
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 
 struct DecodeArgs {
   void* out;

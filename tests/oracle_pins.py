@@ -9,7 +9,8 @@ raises AssertionError when the oracle disagrees with:
   * invariances (physical block permutation; shared vs duplicated blocks; GQA vs repeated
     heads),
   * a library routine: torch's CPU float64 scaled_dot_product_attention on the contiguous K/V
-    the test scatters into the pool with its own index code.
+    the test scatters into the pool with its own index code,
+  * the flat-index formulas of the ABI header, for block copies between pools.
 test_oracle.py runs every pin on the real oracle; test_oracle_mutations.py plants mistakes in a
 copy of the oracle and checks that some pin fails for each.
 """
@@ -372,7 +373,48 @@ def pin_row_helpers(orc):
         assert np.array_equal(part[t, h], full[t, h])
 
 
+def pin_copy_blocks(orc):
+    """Block copies, checked word by word through the header's flat-index formulas: after
+    copying (s, d) pairs from one pool into another of a different size, the K word at
+    ((d*Hkv + h)*B + o)*D + x equals the source's at ((s*Hkv + h)*B + o)*D + x, the V word at
+    ((d*Hkv + h)*D + x)*B + o likewise, every other destination word is unchanged, the inputs
+    are untouched, and a copy out to a second pool and back restores the first."""
+    nbs, nbd, hkv, b, d = 5, 9, 2, 4, 3
+    ks = np.arange(nbs * hkv * b * d, dtype=np.float32).reshape(nbs, hkv, b, d)
+    vs = -1.0 - np.arange(nbs * hkv * d * b, dtype=np.float32).reshape(nbs, hkv, d, b)
+    kd = np.full((nbd, hkv, b, d), 7.5, np.float32)
+    vd = np.full((nbd, hkv, d, b), -7.5, np.float32)
+    pairs = [(3, 0), (1, 8), (3, 4)]
+    k2, v2 = orc.kv_cache_copy_blocks(ks, vs, kd, vd, np.asarray(pairs, np.int32))
+    assert (kd == 7.5).all() and (vd == -7.5).all(), "destination input was modified"
+    kf, vf, ksf, vsf = k2.reshape(-1), v2.reshape(-1), ks.reshape(-1), vs.reshape(-1)
+    written = set()
+    for s_blk, d_blk in pairs:
+        for h in range(hkv):
+            for o in range(b):
+                for x in range(d):
+                    dk = ((d_blk * hkv + h) * b + o) * d + x
+                    dv = ((d_blk * hkv + h) * d + x) * b + o
+                    assert kf[dk] == ksf[((s_blk * hkv + h) * b + o) * d + x]
+                    assert vf[dv] == vsf[((s_blk * hkv + h) * d + x) * b + o]
+                    written.add(dk)
+    rest = [i for i in range(kf.size) if i not in written]
+    assert (kf[rest] == 7.5).all() and (vf[rest] == -7.5).all(), "a block outside the pairs changed"
+    # copy-on-write inside one pool, then out to a host-side pool and back (swap)
+    kp, vp = orc.kv_cache_copy_blocks(ks, vs, ks, vs, np.asarray([[2, 0]], np.int32))
+    assert np.array_equal(kp[0], ks[2]) and np.array_equal(vp[1:], vs[1:])
+    hk = np.zeros((3, hkv, b, d), np.float32)
+    hv = np.zeros((3, hkv, d, b), np.float32)
+    out = np.asarray([[1, 2], [4, 0]], np.int32)
+    hk, hv = orc.kv_cache_copy_blocks(kp, vp, hk, hv, out)
+    wiped_k, wiped_v = kp.copy(), vp.copy()
+    wiped_k[[1, 4]] = 0
+    wiped_v[[1, 4]] = 0
+    bk, bv = orc.kv_cache_copy_blocks(hk, hv, wiped_k, wiped_v, out[:, ::-1].copy())
+    assert np.array_equal(bk, kp) and np.array_equal(bv, vp)
+
+
 PINS = [pin_figure_block_table, pin_bf16_decoding, pin_write_roundtrip, pin_decode_brute_force,
         pin_prefill_brute_force, pin_single_token, pin_zero_length, pin_closed_forms,
         pin_block_permutation, pin_shared_equals_duplicated, pin_gqa_equals_repeated_mha,
-        pin_decode_sdpa, pin_prefill_sdpa, pin_row_helpers]
+        pin_decode_sdpa, pin_prefill_sdpa, pin_row_helpers, pin_copy_blocks]

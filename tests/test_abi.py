@@ -31,8 +31,8 @@ def test_every_declared_symbol_is_exported():
 def test_version_and_strings():
     L = bd.lib()
     assert L.pkv_abi_version() == 1
-    for st in range(5):
-        assert L.pkv_status_string(st)
+    for st in range(6):
+        assert L.pkv_status_string(st) != b"unknown status"
     assert L.pkv_status_string(99) == b"unknown status"
 
 
@@ -85,6 +85,27 @@ def test_write_validation():
     assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 8, 64, 64, 4, 1, None) == bd.PKV_ERR_UNSUPPORTED
     assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 8, 64, 16, 4, 5, None) == bd.PKV_ERR_UNSUPPORTED
     assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 0, 64, 16, 4, 1, None) == bd.PKV_ERR_INVALID_ARG
+
+
+def test_copy_blocks_validation():
+    c = bd.lib().pkv_kv_cache_copy_blocks
+    ok = (FAKE, FAKE, FAKE, FAKE, FAKE, 3, 8, 128, 16, 10, 20, bd.PKV_BF16, None)
+
+    def call(i, x):
+        a = list(ok)
+        a[i] = x
+        return c(*a)
+
+    assert call(5, 0) == bd.PKV_OK                        # no pairs: nothing to do
+    assert call(5, -1) == bd.PKV_ERR_INVALID_ARG
+    assert call(4, None) == bd.PKV_ERR_INVALID_ARG
+    assert call(2, None) == bd.PKV_ERR_INVALID_ARG
+    assert call(6, 0) == bd.PKV_ERR_INVALID_ARG
+    assert call(9, 0) == bd.PKV_ERR_INVALID_ARG
+    assert call(7, 96) == bd.PKV_ERR_UNSUPPORTED
+    assert call(8, 8) == bd.PKV_ERR_UNSUPPORTED
+    assert call(11, 9) == bd.PKV_ERR_UNSUPPORTED
+    assert bd.lib().pkv_last_error()
 
 
 def test_prefill_validation():

@@ -35,6 +35,9 @@ MUTANTS = [
     ("brute_offset", "                off = j % b\n                acc = 0.0\n                for x in range(d):\n                    acc += qv[x]",
      "                off = (j + 1) % b\n                acc = 0.0\n                for x in range(d):\n                    acc += qv[x]"),
     ("row_helper_gqa", "    g = h // (hq // hkv)\n    return attend", "    g = h % hkv\n    return attend"),
+    ("copy_v_from_k", "dst_v[d_blk] = src_v[s_blk]", "dst_v[d_blk] = src_k[s_blk].reshape(dst_v[d_blk].shape)"),
+    ("copy_direction", "dst_k[d_blk] = src_k[s_blk]", "dst_k[s_blk % dst_k.shape[0]] = src_k[d_blk % src_k.shape[0]]"),
+    ("copy_k_skipped", "        dst_k[d_blk] = src_k[s_blk]\n", "        pass\n"),
     ("prefill_rows_selection", "if wanted is not None and (lo + i, h) not in wanted:",
      "if wanted is not None and (i, h) not in wanted:"),
 ]
