@@ -8,6 +8,7 @@ that batch: kv_cache_write of the 64 new tokens' K/V, then paged_attention_decod
 kernel, plus the reduce kernel when the context is split).
 
     python bench.py [--steps K] [--warmup W] [--workload decode-8b|decode-70b|shared-prefix|prefill-chunk]
+    python bench.py --workload cow-fork|block-copy|swap-out|swap-in      # block copies
 
 Prints ONE JSON line on stdout. Inputs are resident in HBM before timing starts. Steps rotate
 over --replicas copies of the pools (so no step re-reads what the previous step left in the
@@ -40,7 +41,15 @@ WORKLOADS = {
     "decode-70b": 3,
     "shared-prefix": 4,
     "prefill-chunk": 5,
+    # the same decode batches with E4M3 (one byte per element) pools, per-pool scale 1/16
+    "decode-8b-fp8": 2,
+    "decode-70b-fp8": 3,
 }
+# Block-copy workloads, all on the decode-8b pool: copy-on-write of one block per sequence (a
+# fork of every sequence), a device-to-device migration of the blocks of half the sequences,
+# and the swap-out / swap-in of those blocks to / from pinned host memory.
+BLOCK_WORKLOADS = ("cow-fork", "block-copy", "swap-out", "swap-in")
+PCIE_PEAK_GBS = 64.0           # PCIe 5.0 x16, one direction (32 GT/s x 16 lanes)
 
 
 def log(msg):
@@ -49,12 +58,16 @@ def log(msg):
 
 # ------------------------------------------------------------------------- algorithmic work
 
+def _pool_esz(w):
+    return {"fp8": 1, "bf16": 2, "f32": 4}[w.pool_dtype]
+
+
 def decode_bytes(w):
     """Bytes the decode method must move: every context token's K and V row for every KV head,
     q read, out written, one block id per (sequence, block), one context length per sequence."""
     esz = 2 if w.dtype == "bf16" else 4
     n = w.context_lens.astype("int64")
-    kv = int(n.sum()) * 2 * w.num_kv_heads * w.head_dim * esz
+    kv = int(n.sum()) * 2 * w.num_kv_heads * w.head_dim * _pool_esz(w)
     q = w.num_seqs * w.num_q_heads * w.head_dim * esz
     ids = int(((n + w.block_size - 1) // w.block_size).sum()) * 4
     return {"kv": kv, "q": q, "out": q, "ids": ids, "ctx": 4 * w.num_seqs}
@@ -62,18 +75,18 @@ def decode_bytes(w):
 
 def unique_decode_kv_bytes(w):
     """KV bytes counting the shared-prefix blocks once (what HBM must deliver at least)."""
-    esz = 2 if w.dtype == "bf16" else 4
     n = w.context_lens.astype("int64")
-    per_tok = 2 * w.num_kv_heads * w.head_dim * esz
+    per_tok = 2 * w.num_kv_heads * w.head_dim * _pool_esz(w)
     if not w.prefix_tokens:
         return int(n.sum()) * per_tok
     return (w.prefix_tokens + int((n - w.prefix_tokens).sum())) * per_tok
 
 
 def write_bytes(w):
+    """New rows read (input dtype) and written (pool dtype), K and V, plus the slot list."""
     esz = 2 if w.dtype == "bf16" else 4
     t = int((w.slot_mapping >= 0).sum())
-    return 2 * 2 * t * w.num_kv_heads * w.head_dim * esz + 4 * len(w.slot_mapping)
+    return 2 * t * w.num_kv_heads * w.head_dim * (esz + _pool_esz(w)) + 4 * len(w.slot_mapping)
 
 
 def prefill_flops(w):
@@ -94,6 +107,133 @@ def prefill_bytes(w):
 
 
 # ---------------------------------------------------------------------------- device side
+
+def run_blocks(args):
+    """Time kv_cache_copy_blocks on the decode-8b pool (see BLOCK_WORKLOADS)."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_190_amd import binding as bd
+    from paged_kv_cache_190_amd import workloads as wl
+
+    w = wl.make_config(WORKLOADS["decode-8b"])
+    dev = torch.device("cuda:0")
+    k0, v0 = to_dev(w.k_pool), to_dev(w.v_pool)
+    b = w.block_size
+    nblk = (w.context_lens.astype(np.int64) + b - 1) // b
+    if args.workload == "cow-fork":
+        # each sequence's last block (the one a forked child writes next) to a fresh block
+        src = np.asarray([w.block_table[s, nblk[s] - 1] for s in range(w.num_seqs)], np.int32)
+    else:
+        half = w.num_seqs // 2
+        src = np.concatenate([w.block_table[s, :nblk[s]] for s in range(half)]).astype(np.int32)
+    n = len(src)
+    block_bytes = 2 * w.num_kv_heads * b * w.head_dim * 2  # K and V of one block, bf16
+    host = args.workload in ("swap-out", "swap-in")
+    shape_k = (n, w.num_kv_heads, b, w.head_dim)
+    shape_v = (n, w.num_kv_heads, w.head_dim, b)
+    if args.workload == "cow-fork":
+        free = np.setdiff1d(np.arange(w.num_blocks), w.block_table[w.block_table >= 0])
+        pairs = np.stack([src, free[:n].astype(np.int32)], 1)
+        ends = (k0, v0, k0, v0)
+    else:
+        ok = torch.empty(shape_k, dtype=torch.bfloat16, device="cpu" if host else dev,
+                         pin_memory=host)
+        ov = torch.empty(shape_v, dtype=torch.bfloat16, device="cpu" if host else dev,
+                         pin_memory=host)
+        out_pairs = np.stack([src, np.arange(n, dtype=np.int32)], 1)
+        if args.workload == "swap-in":
+            bd.kv_cache_copy_blocks(k0, v0, ok, ov, to_dev(out_pairs))
+            pairs, ends = out_pairs[:, ::-1].copy(), (ok, ov, k0, v0)
+        else:
+            pairs, ends = out_pairs, (k0, v0, ok, ov)
+    tp = to_dev(np.ascontiguousarray(pairs))
+    log(f"workload {args.workload}: {n} blocks of {block_bytes} B ({n * block_bytes / 1e6:.1f} MB)")
+
+    def step():
+        bd.kv_cache_copy_blocks(*ends, tp)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    def timed(instrument):
+        bd.profile_enable(instrument)
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.steps):
+            step()
+        stop.record()
+        torch.cuda.synchronize()
+        ms, cnt = bd.profile_read("copy_blocks") if instrument else (0.0, 0)
+        bd.profile_enable(False)
+        return start.elapsed_time(stop) / args.steps, (1e3 * ms / cnt if cnt else None)
+
+    ms_per_step, _ = timed(False)
+    _, kern_us = timed(True)
+    moved = n * block_bytes
+    result = {"ms_per_step": round(ms_per_step, 4),
+              "kernels": {"copy_blocks": {"avg_us": round(kern_us, 2), "launches": args.steps}},
+              "blocks_per_step": n, "bytes_per_block": block_bytes}
+    if host:
+        # context: the DMA engines copying one contiguous buffer of the same size
+        dsrc = torch.empty(moved, dtype=torch.uint8, device=dev)
+        hbuf = torch.empty(moved, dtype=torch.uint8, pin_memory=True)
+        a, bb = (dsrc, hbuf) if args.workload == "swap-out" else (hbuf, dsrc)
+        bb.copy_(a, non_blocking=True)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(5):
+            bb.copy_(a, non_blocking=True)
+        t1.record()
+        torch.cuda.synchronize()
+        result["contiguous_dma_copy_GBs"] = round(5 * moved / (t0.elapsed_time(t1) * 1e-3) / 1e9, 1)
+        achieved = moved / (kern_us * 1e-6) / 1e9
+        result["roofline"] = {"bound": "pcie", "achieved": round(achieved, 1),
+                              "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                              "frac": round(achieved / PCIE_PEAK_GBS, 4), "traffic": None,
+                              "kernel": "copy_blocks", "avg_us": round(kern_us, 2),
+                              "algorithmic_bytes_per_launch": moved}
+        result.update(metric=f"{args.workload} of KV blocks over the host link, GB/s",
+                      value=round(moved / (ms_per_step * 1e-3) / 1e9, 2), unit="GB/s")
+    else:
+        hbm = 2 * moved + 8 * n  # read + write every block, plus the pair list
+        achieved = hbm / (kern_us * 1e-6) / 1e9
+        result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1),
+                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                              "kernel": "copy_blocks", "avg_us": round(kern_us, 2),
+                              "algorithmic_bytes_per_launch": hbm}
+        result.update(metric=f"{args.workload}: KV block copy HBM GB/s (read + write)",
+                      value=round(hbm / (ms_per_step * 1e-3) / 1e9, 1), unit="GB/s")
+    result["_w"] = w
+    result["_pairs"] = pairs
+    return result
+
+
+def cpu_baseline_blocks(w, pairs, budget_s):
+    """The oracle's block copy timed on the host, over growing prefixes of the same pairs."""
+    import numpy as np
+
+    from oracle import paged_attention as orc
+    dk = np.empty((len(pairs),) + w.k_pool.shape[1:], w.k_pool.dtype)
+    dv = np.empty((len(pairs),) + w.v_pool.shape[1:], w.v_pool.dtype)
+    local = np.stack([pairs[:, 0], np.arange(len(pairs), dtype=np.int32)], 1)
+    t0 = time.perf_counter()
+    done = 0
+    while done < len(local) and time.perf_counter() - t0 < budget_s:
+        orc.kv_cache_copy_blocks(w.k_pool, w.v_pool, dk, dv, local[done:done + 256])
+        done = min(done + 256, len(local))
+    dt = time.perf_counter() - t0
+    per = 2 * w.k_pool[0].nbytes
+    return {"value": round(done * per / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"oracle block copy of {done} of {len(pairs)} blocks in calls of 256 "
+                      f"({dt:.2f} s, NumPy); bytes of the blocks copied / time"}
 
 def to_dev(a):
     import numpy as np
@@ -117,7 +257,8 @@ def run(args):
     from paged_kv_cache_190_amd import workloads as wl
 
     cfg = WORKLOADS[args.workload]
-    w = wl.make_config(cfg)
+    fp8 = args.workload.endswith("-fp8")
+    w = wl.make_config(cfg, kv_dtype="fp8" if fp8 else "")
     log(f"workload {args.workload} ({wl.CONFIG_NAMES[cfg]}): S={w.num_seqs} "
         f"sum(n)={int(w.context_lens.sum())} NB={w.num_blocks}")
     dev = torch.device("cuda:0")
@@ -134,13 +275,22 @@ def run(args):
     P = args.partition_size
     if w.kind == "decode":
         code = bd.PKV_BF16 if w.dtype == "bf16" else bd.PKV_F32
+        if fp8:
+            code = bd.PKV_FP8_E4M3
         need = bd.decode_workspace_size(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
                                         w.max_context_len, P, code)
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-        P_eff = bd.decode_partition_size(P, w.num_seqs, w.num_kv_heads, w.max_context_len, code)
+        P_eff = 0 if fp8 else bd.decode_partition_size(P, w.num_seqs, w.num_kv_heads,
+                                                        w.max_context_len, code)
 
     def step(i):
         r = reps[i % replicas]
+        if fp8:
+            bd.kv_cache_write_fp8(k_new, v_new, r.k_pool, r.v_pool, slots, w.k_scale, w.v_scale)
+            bd.paged_attention_decode_fp8(out, q, r.k_pool, r.v_pool, bt, ctx, w.scale,
+                                          w.k_scale, w.v_scale,
+                                          max_context_len=w.max_context_len, workspace=ws)
+            return
         bd.kv_cache_write(k_new, v_new, r.k_pool, r.v_pool, slots)
         if w.kind == "decode":
             bd.paged_attention_decode(out, q, r.k_pool, r.v_pool, bt, ctx, w.scale,
@@ -207,8 +357,11 @@ def run(args):
                 "traffic": traffic_from_profile(args.workload, dom_bytes),
                 "kernel": dom, "avg_us": round(dom_us, 2),
                 "algorithmic_bytes_per_launch": dom_bytes}
+        shape = {"decode-8b": "8B-shaped", "decode-70b": "70B-shaped",
+                 "shared-prefix": "shared-prefix, 8B-shaped", "decode-8b-fp8": "8B-shaped, fp8 KV",
+                 "decode-70b-fp8": "70B-shaped, fp8 KV"}[args.workload]
         result.update(
-            metric="paged decode KV HBM GB/s (% of peak) and decode tokens/sec/GPU, 8B-shaped",
+            metric=f"paged decode KV HBM GB/s (% of peak) and decode tokens/sec/GPU, {shape}",
             value=round(value, 1), unit="GB/s", higher_is_better=True,
             pct_of_hbm_peak=round(100 * value / HBM_PEAK_GBS, 2),
             tokens_per_s_per_layer=round(w.num_seqs / (ms_per_step * 1e-3), 1),
@@ -273,18 +426,23 @@ def cpu_baseline(w, budget_s):
     from threadpoolctl import threadpool_limits
 
     from oracle import paged_attention as orc
-    kp, vp = orc.kv_cache_write(w.k_pool, w.v_pool, w.k_new, w.v_new, w.slot_mapping,
-                                w.block_size)
+    if w.pool_dtype == "fp8":
+        kp, vp = orc.kv_cache_write_fp8(w.k_pool, w.v_pool, w.k_new, w.v_new, w.slot_mapping,
+                                        w.block_size, w.dtype, w.k_scale, w.v_scale)
+    else:
+        kp, vp = orc.kv_cache_write(w.k_pool, w.v_pool, w.k_new, w.v_new, w.slot_mapping,
+                                    w.block_size)
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         done = 0
         if w.kind == "decode":
             work = 0
-            per_tok = 2 * w.num_kv_heads * w.head_dim * (2 if w.dtype == "bf16" else 4)
+            per_tok = 2 * w.num_kv_heads * w.head_dim * _pool_esz(w)
             while done < w.num_seqs and time.perf_counter() - t0 < budget_s:
                 s = done
                 orc.decode(w.q[s:s + 1], kp, vp, w.block_table[s:s + 1],
-                           w.context_lens[s:s + 1], w.scale, w.dtype)
+                           w.context_lens[s:s + 1], w.scale, w.dtype,
+                           kv_dtype=w.kv_dtype or None, k_scale=w.k_scale, v_scale=w.v_scale)
                 work += int(w.context_lens[s]) * per_tok
                 done += 1
             dt = time.perf_counter() - t0
@@ -444,7 +602,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="decode-8b")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS) + list(BLOCK_WORKLOADS),
+                    default="decode-8b")
     ap.add_argument("--replicas", type=int, default=0,
                     help="pool copies the steps rotate over (0: enough for 2 GB)")
     ap.add_argument("--partition-size", type=int, default=0)
@@ -479,22 +638,29 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    res = run(args)
+    from paged_kv_cache_190_amd.workloads import CONFIG_NAMES
+    blocks = args.workload in BLOCK_WORKLOADS
+    res = run_blocks(args) if blocks else run(args)
     w = res.pop("_w")
-    cfg = {"workload": f"{args.workload}: {__import__('paged_kv_cache_190_amd.workloads', fromlist=['x']).CONFIG_NAMES[WORKLOADS[args.workload]]}",
+    pairs = res.pop("_pairs", None)
+    base = "decode-8b" if blocks else args.workload
+    cfg = {"workload": f"{args.workload}: {CONFIG_NAMES[WORKLOADS[base]]}",
            "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
            "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
-           "sum_context_tokens": int(w.context_lens.sum()), "seed": WORKLOADS[args.workload]}
+           "sum_context_tokens": int(w.context_lens.sum()), "seed": WORKLOADS[base]}
     line = {"metric": res.pop("metric"), "value": res.pop("value"), "unit": res.pop("unit"),
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": res.pop("ms_per_step"), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": w.dtype, "data": "synthetic", "config": cfg}
+    if w.kv_dtype:
+        line["kv_dtype"] = w.kv_dtype
     line["roofline"] = res.pop("roofline")
     if args.no_cpu_baseline:
         line["cpu_baseline"] = None
     else:
         log("timing the oracle on the host ...")
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        line["cpu_baseline"] = (cpu_baseline_blocks(w, pairs, args.cpu_seconds) if blocks
+                                else cpu_baseline(w, args.cpu_seconds))
     line.update(res)
     print(json.dumps(line), flush=True)
 

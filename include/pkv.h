@@ -8,7 +8,8 @@
  *   [Inference Engines] "Inference Engines: vLLM, SGLang, TensorRT-LLM" (ragyfied.com),
  *                      parts "PagedAttention" and "Prefix caching".
  *   [VRAM black hole]  zhichai.net topic 178634546 (Chinese original), section 1, the ASCII
- *                      figure of logical blocks, block table and physical blocks.
+ *                      figure of logical blocks, block table and physical blocks; section 4,
+ *                      the KV-cache memory formula (FP8: one byte per element).
  *
  * What the library computes
  * -------------------------
@@ -79,7 +80,11 @@ typedef enum {
   PKV_ERR_OUT_OF_BLOCKS = 5 /* block manager: not enough free blocks (nothing was changed) */
 } pkv_status;
 
-typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+/* PKV_FP8_E4M3: pools only (pkv_kv_cache_write_fp8, pkv_paged_attention_decode_fp8,
+ * pkv_kv_cache_copy_blocks): one byte per element in the OCP 8-bit floating point E4M3 format
+ * (1 sign, 4 exponent bits with bias 7, 3 fraction bits; no infinity; S.1111.111 is NaN;
+ * largest finite 448). */
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 } pkv_dtype;
 
 /* Library plumbing (not defined by the pages). */
 int pkv_abi_version(void);
@@ -107,6 +112,26 @@ int pkv_kv_cache_write(const void* k_new, const void* v_new, void* k_pool, void*
                        int block_size, int num_blocks, int dtype, void* stream);
 
 /*
+ * pkv_kv_cache_write_fp8 -- pkv_kv_cache_write into E4M3 pools, quantising on the way.
+ * [VRAM black hole section 4: FP8 stores a cached element in one byte; Serving Engines "What
+ *  they all agree on": engines quantise the KV cache.] The pages give no scaling scheme; this
+ *  call takes one float32 scale per pool.
+ *
+ *   k_new, v_new   [T][num_kv_heads][head_dim], in_dtype PKV_BF16 or PKV_F32   (read)
+ *   k_pool, v_pool uint8 E4M3 codes, layout above                            (written in place)
+ *   k_scale, v_scale  finite, > 0
+ * Element x of k_new is stored as code(x / k_scale), v_new's with v_scale, where the quotient
+ * is the IEEE float32 quotient (correctly rounded) and code() picks the E4M3 value nearest to
+ * it, ties to the code with an even last bit; magnitudes beyond 448 (and infinities) saturate
+ * to +-448; the sign bit follows the quotient's sign; NaN stores 0x7F. Placement, skipped
+ * slots and preconditions are those of pkv_kv_cache_write.
+ */
+int pkv_kv_cache_write_fp8(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                           const int32_t* slot_mapping, int T, int num_kv_heads, int head_dim,
+                           int block_size, int num_blocks, int in_dtype, float k_scale,
+                           float v_scale, void* stream);
+
+/*
  * pkv_kv_cache_copy_blocks -- copy whole physical blocks between two pools (or inside one).
  * ["Serving Engines", How vLLM works: copy-on-write -- when one of several sequences sharing a
  *  block writes into it, only that block is copied and the block tables split there; swap
@@ -114,6 +139,7 @@ int pkv_kv_cache_write(const void* k_new, const void* v_new, void* k_pool, void*
  *
  *   src_k, src_v   source pools, layout above (read)
  *   dst_k, dst_v   destination pools, same layout and dtype (written); may equal the sources
+ *   dtype          PKV_F32, PKV_BF16 or PKV_FP8_E4M3 (only the element size matters)
  *   block_pairs    int32 [n_pairs][2]: (source block, destination block), device-accessible
  *   src_num_blocks, dst_num_blocks  pool sizes (for the caller's bookkeeping and validation)
  * For each pair every KV head's K tile and V tile of the destination block becomes a bit copy
@@ -178,7 +204,8 @@ int pkv_decode_partition_size(int partition_size, int num_seqs, int num_kv_heads
 /*
  * pkv_decode_workspace_size -- bytes of device workspace pkv_paged_attention_decode needs for
  * these sizes (0 when fixed partitions leave a single partition, so no partials are stored).
- * Library plumbing.
+ * With dtype PKV_FP8_E4M3 (partition_size ignored): what pkv_paged_attention_decode_fp8
+ * needs. Library plumbing.
  */
 size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                                  int max_context_len, int partition_size, int dtype);
@@ -229,6 +256,27 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_pool, con
                                float scale, int max_context_len, int partition_size,
                                void* workspace, size_t workspace_bytes, int dtype, int out_dtype,
                                void* stream);
+
+/*
+ * pkv_paged_attention_decode_fp8 -- pkv_paged_attention_decode over E4M3 pools.
+ * [VRAM black hole section 4: FP8 halves the bytes per cached element; Shootout 3.1 and 5.1 for
+ *  the attention itself, as above.]
+ * The pools hold E4M3 codes written by pkv_kv_cache_write_fp8 with the same k_scale and
+ * v_scale (finite, > 0); K's value is code value * k_scale, V's is code value * v_scale, and
+ * with those values the result is pkv_paged_attention_decode's. q is bf16; out_dtype PKV_BF16
+ * or PKV_F32. The context is always split the balanced way (2048 waves by default;
+ * PKV_DECODE_WAVES overrides it); workspace: pkv_decode_workspace_size(..., dtype =
+ * PKV_FP8_E4M3) bytes. Other arguments, preconditions and errors as for
+ * pkv_paged_attention_decode. Unwritten slots may hold any code, NaN included.
+ */
+int pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_pool,
+                                   const void* v_pool, const int32_t* block_table,
+                                   const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                   int num_kv_heads, int head_dim, int block_size,
+                                   int max_blocks_per_seq, int num_blocks, float scale,
+                                   float k_scale, float v_scale, int max_context_len,
+                                   void* workspace, size_t workspace_bytes, int out_dtype,
+                                   void* stream);
 
 /*
  * pkv_paged_attention_prefill_chunk -- a causal chunk of query tokens against the paged cache.

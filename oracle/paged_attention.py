@@ -30,10 +30,19 @@ Readings taken where the pages are silent (each is listed with its reason in DES
   * softmax is the textbook one: exp(a - max a) / sum exp(a - max a) (a stabilised but exact
     rewrite of exp(a) / sum exp(a)).
 
+  [VRAM black hole 4] the same zhichai.net topic, section 4 (the KV-cache memory formula:
+                      FP8 takes one byte per element), and [Serving Engines] "What they all
+                      agree on" (engines quantise the KV cache too). The pages fix no FP8
+                      detail beyond one byte per element; the readings taken are the OCP 8-bit
+                      floating point E4M3 ("fn") element format and one float32 scale per pool
+                      (stored code = value / scale).
+
 Array conventions (the same arrays the GPU receives):
   dtype "f32":  float32 arrays.
   dtype "bf16": uint16 arrays holding bf16 bit patterns (NumPy has no bf16 type). The oracle
                 decodes them exactly to float64 itself.
+  dtype "fp8":  uint8 arrays holding E4M3 codes (pools only; the value of a code is multiplied
+                by the pool's scale).
   k_pool [NB][Hkv][B][D]; v_pool [NB][Hkv][D][B]; q [S][Hq][D] (decode) or [Tq][Hq][D]
   (prefill); block_table int32 [S][MB]; context_lens int32 [S]; cu_q_lens int32 [S+1];
   slot_mapping int32 [T].
@@ -57,7 +66,49 @@ def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         assert a.dtype == np.uint16
         return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if dtype == "fp8":
+        return fp8_e4m3_value(a)
+    if dtype == "f64":
+        return np.asarray(a, dtype=np.float64)
     raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def fp8_e4m3_value(codes: np.ndarray) -> np.ndarray:
+    """float64 value of E4M3 codes (OCP 8-bit floating point, the "fn" variant): bit 7 the
+    sign, bits 6..3 a biased exponent e (bias 7), bits 2..0 a fraction f. e > 0: (1 + f/8) *
+    2^(e-7); e == 0: subnormal, f/8 * 2^-6. No infinities; e == 15 with f == 7 is NaN, so the
+    largest finite magnitude is 1.75 * 2^8 = 448."""
+    c = np.asarray(codes)
+    assert c.dtype == np.uint8
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = ((c >> 3) & 0xF).astype(np.int64)
+    f = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, f / 8.0 * 2.0 ** -6, (1.0 + f / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (f == 7), np.nan, mag)
+    return sign * mag
+
+
+FP8_E4M3_MAX = 448.0
+
+
+def fp8_e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """E4M3 code of each float32 x: the representable value nearest to x, ties to the code
+    with an even last bit (round to nearest even); magnitudes beyond 448 saturate to +-448
+    (the reading taken: the cache stays finite, as the format has no infinity). The sign
+    bit follows x's sign, so -0.0 and negatives that round to zero give 0x80. NaN gives 0x7F."""
+    x = np.asarray(x, dtype=np.float32)
+    finite = np.arange(127, dtype=np.uint8)           # non-negative finite codes, ascending
+    vals = fp8_e4m3_value(finite)
+    assert np.all(np.diff(vals) > 0)
+    a = np.abs(x.astype(np.float64)).reshape(-1)
+    hi = np.clip(np.searchsorted(vals, a), 1, 126)    # vals[hi-1] <= a <= vals[hi] in range
+    lo = hi - 1
+    dlo, dhi = a - vals[lo], vals[hi] - a
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    pick = np.where(a >= FP8_E4M3_MAX, 126, pick)
+    code = pick.astype(np.uint8) | np.where(np.signbit(x.reshape(-1)), 0x80, 0).astype(np.uint8)
+    code = np.where(np.isnan(x.reshape(-1)), np.uint8(0x7F), code)
+    return code.reshape(x.shape).astype(np.uint8)
 
 
 # ------------------------------------------------------------------------ kv cache write
@@ -107,6 +158,18 @@ def kv_cache_copy_blocks(src_k, src_v, dst_k, dst_v, pairs):
     return dst_k, dst_v
 
 
+def kv_cache_write_fp8(k_pool, v_pool, k_new, v_new, slot_mapping, block_size, in_dtype,
+                       k_scale, v_scale):
+    """kv_cache_write into E4M3 pools: each new element x (dtype in_dtype, exactly a float32)
+    is stored as the code of the float32 quotient x / scale (IEEE division rounded to float32,
+    then fp8_e4m3_encode), K with k_scale and V with v_scale. [VRAM black hole 4]: one byte per cached
+    element. The codes are then placed exactly as kv_cache_write places words."""
+    ks, vs = np.float32(k_scale), np.float32(v_scale)
+    kq = fp8_e4m3_encode(to_f64(k_new, in_dtype).astype(np.float32) / ks)
+    vq = fp8_e4m3_encode(to_f64(v_new, in_dtype).astype(np.float32) / vs)
+    return kv_cache_write(k_pool, v_pool, kq, vq, slot_mapping, block_size)
+
+
 # ----------------------------------------------------------------------------- gather
 
 def gather(k_pool, v_pool, bt_row, n, block_size, dtype):
@@ -141,8 +204,20 @@ def attend(qrow, k, v, scale):
     return (p @ v) / p.sum()
 
 
-def decode(q, k_pool, v_pool, block_table, context_lens, scale, dtype):
-    """paged_attention_decode: one query token per sequence; float64 [S][Hq][D]."""
+def gather_values(k_pool, v_pool, bt_row, n, block_size, kv_dtype, k_scale=1.0, v_scale=1.0):
+    """gather() for any pool type: the values of an E4M3 pool are its code values times the
+    pool's scale (K with k_scale, V with v_scale); other pools hold values as they are."""
+    k, v = gather(k_pool, v_pool, bt_row, n, block_size, kv_dtype)
+    if kv_dtype == "fp8":
+        return k * k_scale, v * v_scale
+    return k, v
+
+
+def decode(q, k_pool, v_pool, block_table, context_lens, scale, dtype, kv_dtype=None,
+           k_scale=1.0, v_scale=1.0):
+    """paged_attention_decode: one query token per sequence; float64 [S][Hq][D].
+    kv_dtype (default: dtype) may be "fp8": the pools hold E4M3 codes, K's and V's value are
+    code value * k_scale and * v_scale; q stays in dtype."""
     s_count, hq, d = q.shape
     hkv = k_pool.shape[1]
     b = k_pool.shape[2]
@@ -154,21 +229,24 @@ def decode(q, k_pool, v_pool, block_table, context_lens, scale, dtype):
         n = int(context_lens[s])
         if n == 0:
             continue  # reading: an empty context gives a zero row
-        k, v = gather(k_pool, v_pool, block_table[s], n, b, dtype)
+        k, v = gather_values(k_pool, v_pool, block_table[s], n, b, kv_dtype or dtype, k_scale,
+                             v_scale)
         for h in range(hq):
             g = h // group
             out[s, h] = attend(qf[s, h], k[g], v[g], scale)
     return out
 
 
-def decode_row(q, k_pool, v_pool, block_table, context_lens, scale, dtype, s, h):
+def decode_row(q, k_pool, v_pool, block_table, context_lens, scale, dtype, s, h,
+               kv_dtype=None, k_scale=1.0, v_scale=1.0):
     """One output row of decode (for sampled comparisons at full size)."""
     hq = q.shape[1]
     hkv, b = k_pool.shape[1], k_pool.shape[2]
     n = int(context_lens[s])
     if n == 0:
         return np.zeros(q.shape[2])
-    k, v = gather(k_pool, v_pool, block_table[s], n, b, dtype)
+    k, v = gather_values(k_pool, v_pool, block_table[s], n, b, kv_dtype or dtype, k_scale,
+                         v_scale)
     g = h // (hq // hkv)
     return attend(to_f64(q[s, h], dtype), k[g], v[g], scale)
 

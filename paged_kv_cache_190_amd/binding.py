@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(PKG, "lib", "libpkv.so")
 
 (PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP,
  PKV_ERR_OUT_OF_BLOCKS) = range(6)
-PKV_F32, PKV_BF16 = 0, 1
+PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 
 _lib = None
 
@@ -64,6 +64,12 @@ def lib() -> ctypes.CDLL:
     L.pkv_profile_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(ctypes.c_longlong)]
     L.pkv_profile_kernel_names.restype = ctypes.c_char_p
+    L.pkv_kv_cache_write_fp8.restype = i32
+    L.pkv_kv_cache_write_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
+                                         f32, vp]
+    L.pkv_paged_attention_decode_fp8.restype = i32
+    L.pkv_paged_attention_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                                 i32, i32, f32, f32, f32, i32, vp, sz, i32, vp]
     L.pkv_kv_cache_copy_blocks.restype = i32
     L.pkv_kv_cache_copy_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                            vp]
@@ -105,6 +111,16 @@ def _dtype_code(t) -> int:
     if t.dtype == torch.float32:
         return PKV_F32
     raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _is_fp8_pool(t) -> bool:
+    """E4M3 pools are uint8 tensors of codes (or torch.float8_e4m3fn views of them)."""
+    import torch
+    return t.dtype in (torch.uint8, torch.float8_e4m3fn)
+
+
+def _pool_code(t) -> int:
+    return PKV_FP8_E4M3 if _is_fp8_pool(t) else _dtype_code(t)
 
 
 def _dev(t, name: str):
@@ -184,6 +200,52 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_table, context_lens, sc
     return out
 
 
+def kv_cache_write_fp8(k_new, v_new, k_pool, v_pool, slot_mapping, k_scale, v_scale,
+                       stream=None) -> None:
+    """kv_cache_write into E4M3 pools (uint8 codes): each element x of k_new / v_new (bf16 or
+    fp32) is stored as the E4M3 code of x / k_scale or x / v_scale."""
+    T, hkv, d = k_new.shape
+    nb, hkv2, b, d2 = k_pool.shape
+    if (hkv, d) != (hkv2, d2) or v_pool.shape != (nb, hkv, d, b) or v_new.shape != k_new.shape:
+        raise ValueError("inconsistent shapes")
+    if not (_is_fp8_pool(k_pool) and _is_fp8_pool(v_pool)) or k_new.dtype != v_new.dtype:
+        raise TypeError("pools must be E4M3 (uint8); k_new and v_new must share a dtype")
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [T]")
+    _check(lib().pkv_kv_cache_write_fp8(_dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                                        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                                        _i32(slot_mapping, "slot_mapping"), T, hkv, d, b, nb,
+                                        _dtype_code(k_new), float(k_scale), float(v_scale),
+                                        _stream(stream)), "kv_cache_write_fp8")
+
+
+def paged_attention_decode_fp8(out, q, k_pool, v_pool, block_table, context_lens, scale, k_scale,
+                               v_scale, max_context_len=0, workspace=None, stream=None):
+    """paged_attention_decode over E4M3 pools (K value = code * k_scale, V value = code *
+    v_scale); q bf16; out bf16 or fp32. A workspace is allocated when needed and not given."""
+    import torch
+    S, hq, d = q.shape
+    nb, hkv, b, d2 = k_pool.shape
+    if d2 != d or v_pool.shape != (nb, hkv, d, b) or out.shape != q.shape:
+        raise ValueError("inconsistent shapes")
+    if not (_is_fp8_pool(k_pool) and _is_fp8_pool(v_pool)):
+        raise TypeError("pools must be E4M3 (uint8)")
+    if block_table.dim() != 2 or block_table.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_table must be [S][MB], context_lens [S]")
+    mb = block_table.shape[1]
+    ctx = max_context_len if max_context_len else mb * b
+    need = decode_workspace_size(S, hq, hkv, d, ctx, 0, PKV_FP8_E4M3)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().pkv_paged_attention_decode_fp8(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _i32(block_table, "block_table"), _i32(context_lens, "context_lens"), S, hq, hkv, d, b,
+        mb, nb, float(scale), float(k_scale), float(v_scale), int(max_context_len),
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+        _dtype_code(out), _stream(stream)), "paged_attention_decode_fp8")
+    return out
+
+
 def paged_attention_prefill_chunk(out, q, cu_q_lens, context_lens, k_pool, v_pool, block_table,
                                   scale, max_q_len=0, max_context_len=0, stream=None):
     """out [Tq][Hq][D]: causal attention of each sequence's chunk rows over its paged context
@@ -230,7 +292,7 @@ def kv_cache_copy_blocks(src_k, src_v, dst_k, dst_v, block_pairs, stream=None) -
     _check(lib().pkv_kv_cache_copy_blocks(
         _pool(src_k, "src_k"), _pool(src_v, "src_v"), _pool(dst_k, "dst_k"),
         _pool(dst_v, "dst_v"), _i32(block_pairs, "block_pairs") if n else None, n, hkv, d, b,
-        nbs, nbd, _dtype_code(src_k), _stream(stream)), "kv_cache_copy_blocks")
+        nbs, nbd, _pool_code(src_k), _stream(stream)), "kv_cache_copy_blocks")
 
 
 # ------------------------------------------------------------------------------ block manager

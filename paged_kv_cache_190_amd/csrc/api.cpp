@@ -40,7 +40,8 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 bool supported_dtype(int d) { return d == PKV_F32 || d == PKV_BF16; }
-int elem_bytes(int d) { return d == PKV_BF16 ? 2 : 4; }
+int elem_bytes(int d) { return d == PKV_FP8_E4M3 ? 1 : (d == PKV_BF16 ? 2 : 4); }
+bool valid_pool_scale(float s) { return std::isfinite(s) && s > 0.0f; }
 
 constexpr int kMaxGridYZ = 65535;
 
@@ -144,6 +145,8 @@ size_t fixed_workspace_bytes(int S, int Hq, int D, int NP) {
 // Balanced split (bf16 inputs, partition_size == 0).
 constexpr int kMinTilesPerWave = 8;     // 256 tokens
 constexpr int kDefaultDecodeWaves = 1024;
+// An E4M3 tile is half the bytes of a bf16 one; twice the waves keep as many bytes in flight.
+constexpr int kDefaultDecodeWavesFp8 = 2048;
 
 struct BalancedPlan {
   int waves;
@@ -151,23 +154,25 @@ struct BalancedPlan {
   size_t o_off, m_off, l_off, cnt_off, bytes;
 };
 
-int decode_waves_setting() {
+int decode_waves_setting(int default_waves) {
   const char* e = std::getenv("PKV_DECODE_WAVES");
   if (e) {
     const int v = std::atoi(e);
     if (v > 0) return v;
   }
-  return kDefaultDecodeWaves;
+  return default_waves;
 }
 
-BalancedPlan balanced_plan(int S, int Hq, int Hkv, int D, int max_ctx) {
+BalancedPlan balanced_plan(int S, int Hq, int Hkv, int D, int max_ctx,
+                           int default_waves = kDefaultDecodeWaves) {
   BalancedPlan pl{};
   const int G = Hq / Hkv;
   const long long segs = static_cast<long long>(Hkv) * ((G + 15) / 16);
   const long long seg_tiles = (std::max(max_ctx, 1) + 31) / 32;
   const long long t_upper = static_cast<long long>(S) * segs * seg_tiles;
   pl.waves = static_cast<int>(
-      std::max(1LL, std::min<long long>(decode_waves_setting(), t_upper / kMinTilesPerWave)));
+      std::max(1LL, std::min<long long>(decode_waves_setting(default_waves),
+                                        t_upper / kMinTilesPerWave)));
   pl.kmax = static_cast<int>((seg_tiles + kMinTilesPerWave - 1) / kMinTilesPerWave + 1);
   const size_t rows = static_cast<size_t>(S) * Hq * pl.kmax;
   auto align = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
@@ -233,6 +238,33 @@ int pkv_kv_cache_write(const void* k_new, const void* v_new, void* k_pool, void*
   return hip_status(pkv::launch_kv_write(a, static_cast<hipStream_t>(stream)), "kv_cache_write");
 }
 
+int pkv_kv_cache_write_fp8(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                           const int32_t* slot_mapping, int T, int num_kv_heads, int head_dim,
+                           int block_size, int num_blocks, int in_dtype, float k_scale,
+                           float v_scale, void* stream) {
+  if (T < 0) return fail(PKV_ERR_INVALID_ARG, "T = %d is negative", T);
+  if (T == 0) return PKV_OK;
+  if (!k_new || !v_new || !k_pool || !v_pool || !slot_mapping)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (num_kv_heads <= 0 || num_blocks <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_kv_heads and num_blocks must be positive");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", head_dim);
+  if (block_size != 16 && block_size != 32)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %d not in {16, 32}", block_size);
+  if (!supported_dtype(in_dtype))
+    return fail(PKV_ERR_UNSUPPORTED, "in_dtype %d not supported", in_dtype);
+  if (!valid_pool_scale(k_scale) || !valid_pool_scale(v_scale))
+    return fail(PKV_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
+  if (static_cast<long long>(num_blocks) * block_size > 0x7fffffffLL)
+    return fail(PKV_ERR_UNSUPPORTED, "pool of %d blocks exceeds int32 slot numbers", num_blocks);
+  pkv::KvWriteArgs a{k_new, v_new, k_pool, v_pool, slot_mapping, T, num_kv_heads, head_dim,
+                     block_size, num_blocks, elem_bytes(in_dtype)};
+  return hip_status(pkv::launch_kv_write_fp8(a, in_dtype == PKV_BF16, k_scale, v_scale,
+                                             static_cast<hipStream_t>(stream)),
+                    "kv_cache_write_fp8");
+}
+
 namespace {
 // A pool handed to the copy kernel may be device memory or pinned host memory; anything else
 // (pageable host memory, a stale pointer) would fault in the kernel, so it is refused here.
@@ -266,7 +298,8 @@ int pkv_kv_cache_copy_blocks(const void* src_k, const void* src_v, void* dst_k, 
     return fail(PKV_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", head_dim);
   if (block_size != 16 && block_size != 32)
     return fail(PKV_ERR_UNSUPPORTED, "block_size %d not in {16, 32}", block_size);
-  if (!supported_dtype(dtype)) return fail(PKV_ERR_UNSUPPORTED, "dtype %d not supported", dtype);
+  if (!supported_dtype(dtype) && dtype != PKV_FP8_E4M3)
+    return fail(PKV_ERR_UNSUPPORTED, "dtype %d not supported", dtype);
   if (n_pairs > kMaxGridYZ) return fail(PKV_ERR_UNSUPPORTED, "n_pairs %d too large", n_pairs);
   const void* ptrs[5] = {src_k, src_v, dst_k, dst_v, block_pairs};
   const char* names[5] = {"src_k", "src_v", "dst_k", "dst_v", "block_pairs"};
@@ -289,6 +322,9 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       num_q_heads % num_kv_heads != 0)
     return 0;
+  if (dtype == PKV_FP8_E4M3)
+    return balanced_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                         kDefaultDecodeWavesFp8).bytes;
   if (partition_size == 0 && dtype == PKV_BF16)
     return balanced_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len).bytes;
   const int p = resolve_partition(partition_size, num_seqs, num_kv_heads, max_context_len);
@@ -297,15 +333,38 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads
                                num_partitions(max_context_len, p));
 }
 
-int pkv_paged_attention_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
-                               const int32_t* block_table, const int32_t* context_lens,
-                               int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                               int block_size, int max_blocks_per_seq, int num_blocks,
-                               float scale, int max_context_len, int partition_size,
-                               void* workspace, size_t workspace_bytes, int dtype, int out_dtype,
-                               void* stream) {
-  if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs = %d is negative", num_seqs);
-  if (num_seqs == 0) return PKV_OK;
+}  // extern "C"
+
+namespace {
+
+// Balanced split set-up: the plan for a's sizes, and the partial buffers carved out of the
+// caller's workspace.
+int setup_balanced(pkv::DecodeArgs& a, void* workspace, size_t workspace_bytes,
+                   int default_waves) {
+  const BalancedPlan pl = balanced_plan(a.S, a.Hq, a.Hkv, a.D, a.max_ctx, default_waves);
+  if (!workspace || workspace_bytes < pl.bytes)
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.bytes,
+                workspace ? workspace_bytes : static_cast<size_t>(0));
+  char* base = static_cast<char*>(workspace);
+  a.balanced = 1;
+  a.waves = pl.waves;
+  a.min_tiles = kMinTilesPerWave;
+  a.KMAX = pl.kmax;
+  a.P = 32;
+  a.NP = 1;
+  a.part_o = reinterpret_cast<float*>(base + pl.o_off);
+  a.part_m = reinterpret_cast<float*>(base + pl.m_off);
+  a.part_l = reinterpret_cast<float*>(base + pl.l_off);
+  a.seg_count = reinterpret_cast<int32_t*>(base + pl.cnt_off);
+  return PKV_OK;
+}
+
+// Checks shared by both decode entry points; fills the size fields of a.
+int check_decode(pkv::DecodeArgs& a, void* out, const void* q, const void* k_pool,
+                 const void* v_pool, const int32_t* block_table, const int32_t* context_lens,
+                 int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                 int max_blocks_per_seq, int num_blocks, float scale, int max_context_len,
+                 int dtype, int out_dtype) {
   if (!out || !q || !k_pool || !v_pool || !block_table || !context_lens)
     return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
   int st = check_common(num_q_heads, num_kv_heads, head_dim, block_size, dtype, out_dtype);
@@ -319,12 +378,6 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_pool, con
     return fail(PKV_ERR_INVALID_ARG, "max_context_len %d outside [0, %lld]", max_context_len,
                 cap);
   if (num_seqs > kMaxGridYZ) return fail(PKV_ERR_UNSUPPORTED, "num_seqs %d too large", num_seqs);
-  const int max_ctx = max_context_len > 0 ? max_context_len : static_cast<int>(cap);
-  if (partition_size < 0 || partition_size % 16 != 0 || partition_size % block_size != 0)
-    return fail(PKV_ERR_INVALID_ARG,
-                "partition_size %d must be a non-negative multiple of 16 and of block_size",
-                partition_size);
-  pkv::DecodeArgs a{};
   a.out = out;
   a.q = q;
   a.k_pool = k_pool;
@@ -339,23 +392,66 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_pool, con
   a.MB = max_blocks_per_seq;
   a.NB = num_blocks;
   a.scale = scale;
-  a.max_ctx = max_ctx;
+  a.max_ctx = max_context_len > 0 ? max_context_len : static_cast<int>(cap);
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_pool,
+                                   const void* v_pool, const int32_t* block_table,
+                                   const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                   int num_kv_heads, int head_dim, int block_size,
+                                   int max_blocks_per_seq, int num_blocks, float scale,
+                                   float k_scale, float v_scale, int max_context_len,
+                                   void* workspace, size_t workspace_bytes, int out_dtype,
+                                   void* stream) {
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs = %d is negative", num_seqs);
+  if (num_seqs == 0) return PKV_OK;
+  pkv::DecodeArgs a{};
+  int st = check_decode(a, out, q, k_pool, v_pool, block_table, context_lens, num_seqs,
+                        num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                        num_blocks, scale, max_context_len, PKV_BF16, out_dtype);
+  if (st != PKV_OK) return st;
+  if (!valid_pool_scale(k_scale) || !valid_pool_scale(v_scale))
+    return fail(PKV_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
+  if (!std::isfinite(scale * k_scale))
+    return fail(PKV_ERR_INVALID_ARG, "scale * k_scale is not finite");
+  st = setup_balanced(a, workspace, workspace_bytes, kDefaultDecodeWavesFp8);
+  if (st != PKV_OK) return st;
+  a.fp8_kv = 1;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.bf16_in = 1;
+  a.bf16_out = out_dtype == PKV_BF16;
+  return hip_status(pkv::launch_decode(a, static_cast<hipStream_t>(stream)),
+                    "paged_attention_decode_fp8");
+}
+
+int pkv_paged_attention_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* block_table, const int32_t* context_lens,
+                               int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                               int block_size, int max_blocks_per_seq, int num_blocks,
+                               float scale, int max_context_len, int partition_size,
+                               void* workspace, size_t workspace_bytes, int dtype, int out_dtype,
+                               void* stream) {
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs = %d is negative", num_seqs);
+  if (num_seqs == 0) return PKV_OK;
+  pkv::DecodeArgs a{};
+  int st = check_decode(a, out, q, k_pool, v_pool, block_table, context_lens, num_seqs,
+                        num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                        num_blocks, scale, max_context_len, dtype, out_dtype);
+  if (st != PKV_OK) return st;
+  const int max_ctx = a.max_ctx;
+  if (partition_size < 0 || partition_size % 16 != 0 || partition_size % block_size != 0)
+    return fail(PKV_ERR_INVALID_ARG,
+                "partition_size %d must be a non-negative multiple of 16 and of block_size",
+                partition_size);
   if (partition_size == 0 && dtype == PKV_BF16) {
-    const BalancedPlan pl = balanced_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_ctx);
-    if (!workspace || workspace_bytes < pl.bytes)
-      return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.bytes,
-                  workspace ? workspace_bytes : static_cast<size_t>(0));
-    char* base = static_cast<char*>(workspace);
-    a.balanced = 1;
-    a.waves = pl.waves;
-    a.min_tiles = kMinTilesPerWave;
-    a.KMAX = pl.kmax;
-    a.P = 32;
-    a.NP = 1;
-    a.part_o = reinterpret_cast<float*>(base + pl.o_off);
-    a.part_m = reinterpret_cast<float*>(base + pl.m_off);
-    a.part_l = reinterpret_cast<float*>(base + pl.l_off);
-    a.seg_count = reinterpret_cast<int32_t*>(base + pl.cnt_off);
+    st = setup_balanced(a, workspace, workspace_bytes, kDefaultDecodeWaves);
+    if (st != PKV_OK) return st;
   } else {
     const int P = resolve_partition(partition_size, num_seqs, num_kv_heads, max_ctx);
     if (P % block_size != 0)

@@ -22,6 +22,14 @@
 // dropped; the kernel is bound by HBM reads of K and V, so the padded MFMA work is free.
 // K and V of the next tile are loaded while the current tile is computed (two register sets).
 //
+// E4M3 pools (same waves, same tiles): every E4M3 value is exactly a bf16 value, so each lane
+// widens the bytes it loaded with v_cvt_scalef32_pk_bf16_fp8 (scale 1) and feeds the same bf16
+// matrix products. A tile's K is 4 KB instead of 8, so the contraction slots are assigned
+// differently: lane group lg holds the D/4 consecutive dimensions lg*D/4 .. (lg+1)*D/4-1 of its
+// token row (one 16-byte load per 16 dimensions), and the query operand uses the same
+// assignment. The pool scales are folded in: k_scale into the score scale, v_scale into the
+// final normalisation.
+//
 // fp32 path (vector ALUs): one wave owns (sequence, query head, partition); lanes take one token
 // each for the scores, then one output dimension each for P.V.
 #include "common.hpp"
@@ -200,11 +208,180 @@ __device__ __forceinline__ void attend_tiles(WaveAttn<D>& st, const u32x4 (&qf)[
   }
 }
 
+// ----------------------------------------------------------------------------- E4M3 pools
+
+template <int D, int B>
+struct KvTile8 {
+  u32x4 k[2][D / 64];  // per half: the lane's D/4 bytes of one token row
+  u32x2 v[D / 16];     // per 16 dims: 8 tokens of one dimension row
+};
+
+// Q as the MFMA B operand for E4M3 K: contraction slot (kk, 8*lg + e) is dimension
+// lg*D/4 + 8*kk + e.
+template <int D>
+__device__ __forceinline__ void load_q_fp8(u32x4 (&qf)[D / 32], const uint16_t* qrow,
+                                           bool hvalid, int lg) {
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk)
+    qf[kk] = hvalid ? load16(qrow + (D / 4) * lg + 8 * kk) : u32x4{0u, 0u, 0u, 0u};
+}
+
+// Eight E4M3 codes (bytes 0..7 of w0, w1) as eight bf16 values, byte i -> element i. Exact.
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+  return r;
+}
+
+__device__ __forceinline__ u32x2 load8(const void* p) {
+  return *reinterpret_cast<const u32x2*>(p);
+}
+
+// attend_tiles for E4M3 pools: the same tiles, token-to-row assignment, softmax and pipeline;
+// only the loads (bytes) and the widening before each product differ.
+template <int D, int B>
+__device__ __forceinline__ void attend_tiles_fp8(WaveAttn<D>& st, const u32x4 (&qf)[D / 32],
+                                                 const uint8_t* __restrict__ kpool,
+                                                 const uint8_t* __restrict__ vpool,
+                                                 const int32_t* __restrict__ bt, int n, int g,
+                                                 int Hkv, int tok_begin, int tok_end,
+                                                 float scale_log2) {
+  constexpr int KK = D / 32;
+  constexpr int KL = D / 64;
+  constexpr int DT = D / 16;
+  constexpr int TILE = B * D;  // bytes of one (block, head) tile
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15;
+  const int lg = lane >> 4;
+  const int ntiles = (tok_end - tok_begin + 31) >> 5;
+  const int nblk = (n + B - 1) / B;
+
+  int koff[2];
+  int ksel = 0;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int tau = 8 * (r16 >> 2) + 4 * hf + (r16 & 3);
+    koff[hf] = (tau % B) * D + (D / 4) * lg;
+    ksel = tau / B;
+  }
+  const int vsel = (B == 16) ? (lg >> 1) : 0;
+  const int vtok = (B == 16) ? 8 * (lg & 1) : 8 * lg;
+  const int voff = r16 * B + vtok;
+  const int64_t head_off = static_cast<int64_t>(g) * TILE;
+  const int64_t blk_stride = static_cast<int64_t>(Hkv) * TILE;
+
+  int chunk_lb = 0;
+  int my_id = 0;
+  auto block_id = [&](int lb) -> int {
+    return __builtin_amdgcn_readlane(my_id, min(lb, nblk - 1) - chunk_lb);
+  };
+  auto load_tile = [&](KvTile8<D, B>& T, int t) {
+    const int lb0 = (tok_begin + 32 * t) / B;
+    const int id0 = block_id(lb0);
+    const int id1 = (B == 16) ? block_id(lb0 + 1) : id0;
+    const uint8_t* kb = kpool + (ksel ? id1 : id0) * blk_stride + head_off;
+    const uint8_t* vb = vpool + (vsel ? id1 : id0) * blk_stride + head_off;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int j = 0; j < KL; ++j) T.k[hf][j] = load16(kb + koff[hf] + 16 * j);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) T.v[dt] = load8(vb + voff + 16 * dt * B);
+  };
+
+  auto compute = [&](KvTile8<D, B>& T, int t) {
+    const int tok0 = tok_begin + 32 * t;
+    f32x4 sc[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      sc[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const u32x4 w = T.k[hf][kk >> 1];
+        const u32x4 a = (kk & 1) ? e4m3x8_to_bf16x8(w[2], w[3]) : e4m3x8_to_bf16x8(w[0], w[1]);
+        sc[hf] = mfma16x16x32(a, qf[kk], sc[hf]);
+      }
+    }
+    const int lim = tok_end - tok0;
+    float x[8];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tt = 8 * lg + 4 * hf + e;
+        x[4 * hf + e] = (tt < lim) ? sc[hf][e] * scale_log2 : -INFINITY;
+      }
+    float tmax = x[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
+    tmax = xor32_max(xor16_max(tmax));
+    const float mnew = fmaxf(st.m, tmax);
+    const float alpha = fast_exp2(st.m - mnew);
+    st.m = mnew;
+    float psum = 0.f;
+    u32x4 pb;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float p0 = fast_exp2(x[2 * w] - mnew);
+      const float p1 = fast_exp2(x[2 * w + 1] - mnew);
+      psum += p0 + p1;
+      pb[w] = pack_bf16x2(p0, p1);
+    }
+    st.l = st.l * alpha + psum;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) st.acc[dt] *= alpha;
+    u32x4 vv[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vv[dt] = e4m3x8_to_bf16x8(T.v[dt][0], T.v[dt][1]);
+    // Slots at or past n may hold any code, NaN included: clear those V values (0 * NaN).
+    const int vlim = n - tok0;
+    if (vlim < 32) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int t0 = 8 * lg + 2 * w;
+        const uint32_t keep =
+            (t0 < vlim ? 0x0000ffffu : 0u) | (t0 + 1 < vlim ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vv[dt][w] &= keep;
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) st.acc[dt] = mfma16x16x32(vv[dt], pb, st.acc[dt]);
+  };
+
+  constexpr int kChunkTiles = 64 * B / 32;
+  KvTile8<D, B> ta, tb;
+  for (int c0 = 0; c0 < ntiles; c0 += kChunkTiles) {
+    const int c1 = min(ntiles, c0 + kChunkTiles);
+    chunk_lb = (tok_begin + 32 * c0) / B;
+    my_id = bt[min(chunk_lb + lane, nblk - 1)];
+    load_tile(ta, c0);
+    int t = c0;
+    for (; t + 2 < c1; t += 2) {
+      load_tile(tb, t + 1);
+      compute(ta, t);
+      load_tile(ta, t + 2);
+      compute(tb, t + 1);
+    }
+    if (t + 1 < c1) {
+      load_tile(tb, t + 1);
+      compute(ta, t);
+      compute(tb, t + 1);
+    } else {
+      compute(ta, t);
+    }
+  }
+}
+
 // Final output of a wave whose state covers a head's whole context: out = acc / l.
+// out_scale multiplies the result (the V pool's scale for E4M3 pools, else 1).
 template <int D, typename OutT>
 __device__ __forceinline__ void write_final(OutT* __restrict__ o, const WaveAttn<D>& st,
-                                            float l_total, int lg) {
-  const float inv = 1.0f / l_total;
+                                            float l_total, int lg, float out_scale = 1.0f) {
+  const float inv = out_scale / l_total;
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
@@ -216,8 +393,9 @@ template <int D>
 __device__ __forceinline__ void write_partial(float* __restrict__ part_o,
                                               float* __restrict__ part_m,
                                               float* __restrict__ part_l, int64_t idx,
-                                              const WaveAttn<D>& st, float l_total, int lg) {
-  const float inv = 1.0f / l_total;
+                                              const WaveAttn<D>& st, float l_total, int lg,
+                                              float out_scale = 1.0f) {
+  const float inv = out_scale / l_total;
   if (lg == 0) {
     part_m[idx] = st.m;
     part_l[idx] = l_total;
@@ -298,14 +476,16 @@ __device__ __forceinline__ int wave_incl_scan_i(int v) {
 // (to within one), whatever the mix of context lengths. Wave 0 also records, per segment, how
 // many waves share it. W is lowered on the device so that each wave gets at least min_tiles
 // tiles, which bounds the partials per segment by ceil(ceil(max_ctx/32) / min_tiles) + 1 = KMAX.
-template <int D, int B, typename OutT>
+// KvT: uint16_t for bf16 pools, uint8_t for E4M3 pools (out_scale = the V scale).
+template <int D, int B, typename OutT, typename KvT>
 __global__ __launch_bounds__(64) void decode_balanced_kernel(
     OutT* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_m,
     float* __restrict__ part_l, int32_t* __restrict__ seg_count,
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kpool,
-    const uint16_t* __restrict__ vpool, const int32_t* __restrict__ block_table,
+    const uint16_t* __restrict__ q, const KvT* __restrict__ kpool,
+    const KvT* __restrict__ vpool, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ context_lens, int S, int Hq, int Hkv, int G, int HG, int MB,
-    int KMAX, int min_tiles, float scale_log2) {
+    int KMAX, int min_tiles, float scale_log2, float out_scale) {
+  constexpr bool kFp8 = sizeof(KvT) == 1;
   const int lane = threadIdx.x;
   const int lg = lane >> 4;
   const int w = blockIdx.x;
@@ -383,17 +563,25 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(
     const int h = g * G + (hvalid ? hl : 0);
     const int64_t row = static_cast<int64_t>(s) * Hq + h;
     u32x4 qf[D / 32];
-    load_q<D>(qf, q + row * D, hvalid, lg);
     WaveAttn<D> st;
     attn_init(st);
-    attend_tiles<D, B>(st, qf, kpool, vpool, block_table + static_cast<int64_t>(s) * MB, n, g,
-                       Hkv, 32 * t_begin, min(32 * t_end, n), scale_log2);
+    const int32_t* bt = block_table + static_cast<int64_t>(s) * MB;
+    if constexpr (kFp8) {
+      load_q_fp8<D>(qf, q + row * D, hvalid, lg);
+      attend_tiles_fp8<D, B>(st, qf, kpool, vpool, bt, n, g, Hkv, 32 * t_begin,
+                             min(32 * t_end, n), scale_log2);
+    } else {
+      load_q<D>(qf, q + row * D, hvalid, lg);
+      attend_tiles<D, B>(st, qf, kpool, vpool, bt, n, g, Hkv, 32 * t_begin, min(32 * t_end, n),
+                         scale_log2);
+    }
     const float l_total = xor32_sum(xor16_sum(st.l));
     const int64_t wf = wave_of(a);
+    const float osc = kFp8 ? out_scale : 1.0f;
     if (hvalid) {
-      if (wf == wave_of(a + ts - 1)) write_final<D>(out + row * D, st, l_total, lg);
+      if (wf == wave_of(a + ts - 1)) write_final<D>(out + row * D, st, l_total, lg, osc);
       else if (w - wf < KMAX)  // always true when context_lens respect max_context_len
-        write_partial<D>(part_o, part_m, part_l, row * KMAX + (w - wf), st, l_total, lg);
+        write_partial<D>(part_o, part_m, part_l, row * KMAX + (w - wf), st, l_total, lg, osc);
     }
     x = a + t_end;
     if (++j == segs) {  // next non-empty sequence
@@ -568,12 +756,20 @@ template <int D, int B, typename OutT>
 static void launch_bf16(const DecodeArgs& a, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   const int HG = (G + 15) / 16;
+  if (a.fp8_kv) {
+    (void)launch_kernel(K_DECODE_PARTITION, decode_balanced_kernel<D, B, OutT, uint8_t>,
+        dim3(a.waves), dim3(64), st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l,
+        a.seg_count, static_cast<const uint16_t*>(a.q), static_cast<const uint8_t*>(a.k_pool),
+        static_cast<const uint8_t*>(a.v_pool), a.block_table, a.context_lens, a.S, a.Hq, a.Hkv, G,
+        HG, a.MB, a.KMAX, a.min_tiles, a.scale * a.k_scale * kLog2e, a.v_scale);
+    return;
+  }
   if (a.balanced) {
-    (void)launch_kernel(K_DECODE_PARTITION, decode_balanced_kernel<D, B, OutT>, dim3(a.waves), dim3(64),
-        st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l, a.seg_count,
-        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
+    (void)launch_kernel(K_DECODE_PARTITION, decode_balanced_kernel<D, B, OutT, uint16_t>,
+        dim3(a.waves), dim3(64), st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l,
+        a.seg_count, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
         static_cast<const uint16_t*>(a.v_pool), a.block_table, a.context_lens, a.S, a.Hq, a.Hkv, G,
-        HG, a.MB, a.KMAX, a.min_tiles, a.scale * kLog2e);
+        HG, a.MB, a.KMAX, a.min_tiles, a.scale * kLog2e, 1.0f);
     return;
   }
   dim3 grid(a.Hkv * HG, a.S, a.NP);
@@ -602,7 +798,7 @@ static void launch_f32(const DecodeArgs& a, hipStream_t st) {
 
 template <int D, int B, typename OutT>
 static void dispatch_out_t(const DecodeArgs& a, hipStream_t st) {
-  if (a.bf16_in) {
+  if (a.bf16_in || a.fp8_kv) {
     launch_bf16<D, B, OutT>(a, st);
   } else {
     if (a.NP > 1) launch_f32<D, B, true, OutT>(a, st);

@@ -48,6 +48,9 @@ struct KvWriteArgs {
   int T, Hkv, D, B, NB, elem_bytes;
 };
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
+// E4M3 pools: inputs bf16 (in_bf16) or fp32, stored as the codes of x / scale.
+hipError_t launch_kv_write_fp8(const KvWriteArgs& a, int in_bf16, float k_scale, float v_scale,
+                               hipStream_t stream);
 
 struct CopyBlocksArgs {
   const void* src_k;
@@ -84,6 +87,10 @@ struct DecodeArgs {
   int32_t* seg_count;  // [S][Hkv][ceil(G/16)] (balanced)
   int bf16_in;
   int bf16_out;
+  // E4M3 pools (always balanced; q is bf16): K value = code * k_scale, V value = code * v_scale.
+  int fp8_kv;
+  float k_scale;
+  float v_scale;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

@@ -23,6 +23,12 @@ Allocation recipe (shared by every builder):
     including the slots the new tokens will be written to.
 Random draws, in order, from numpy.random.default_rng(seed): the lengths (by the config
 functions), the permutation, the K pool, the V pool, q, the new K rows, the new V rows.
+
+E4M3 pools (kv_dtype "fp8") hold codes drawn directly, field by field: a uniform sign bit, an
+exponent field uniform in 8..12 (2% of elements get exponent field 0: zeros and subnormals),
+a uniform 3-bit fraction; with the pool scale 1/16 the values lie within about +-0.06..3.75,
+the spread of N(0, 1) rows. Unused slots hold the NaN code 0x7F. q and the new rows are bf16
+N(0, 1) values; the new rows are quantised by the library's own write.
 """
 
 from __future__ import annotations
@@ -33,6 +39,8 @@ from dataclasses import dataclass, field
 import numpy as np
 
 BF16_NAN = np.uint16(0x7FC0)
+FP8_NAN = np.uint8(0x7F)
+FP8_POOL_SCALE = 1.0 / 16.0
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -77,6 +85,13 @@ class Workload:
     shared_blocks: int = 0
     name: str = ""
     meta: dict = field(default_factory=dict)
+    kv_dtype: str = ""             # pool element type when it differs from dtype ("fp8")
+    k_scale: float = 1.0           # E4M3 pools: value = code value * scale
+    v_scale: float = 1.0
+
+    @property
+    def pool_dtype(self) -> str:
+        return self.kv_dtype or self.dtype
 
     @property
     def max_context_len(self) -> int:
@@ -137,11 +152,25 @@ def _fill_pools(rng, bt, lens, new_from, hkv, d, b, nb, dtype):
             live[blk, : min(b, upto - j)] = True
     dead_k = ~live[:, None, :, None]
     dead_v = ~live[:, None, None, :]
+    if dtype == "fp8":
+        kc, vc = fp8_codes(rng, k.shape), fp8_codes(rng, v.shape)
+        np.copyto(kc, FP8_NAN, where=np.broadcast_to(dead_k, k.shape))
+        np.copyto(vc, FP8_NAN, where=np.broadcast_to(dead_v, v.shape))
+        return kc, vc
     np.copyto(k, np.float32(np.nan), where=np.broadcast_to(dead_k, k.shape))
     np.copyto(v, np.float32(np.nan), where=np.broadcast_to(dead_v, v.shape))
     if dtype == "bf16":
         return bf16_bits(k), bf16_bits(v)
     return k, v
+
+
+def fp8_codes(rng, shape) -> np.ndarray:
+    """Random E4M3 codes drawn field by field (see the module notes); never NaN."""
+    sign = rng.integers(0, 2, shape, dtype=np.uint8)
+    expo = rng.integers(8, 13, shape, dtype=np.uint8)
+    expo[rng.random(shape) < 0.02] = 0
+    frac = rng.integers(0, 8, shape, dtype=np.uint8)
+    return ((sign << 7) | (expo << 3) | frac).astype(np.uint8)
 
 
 def _values(rng, shape, dtype):
@@ -159,16 +188,18 @@ def _slots(bt, positions_per_seq, b):
 
 def build_decode(seed, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, lens,
                  dtype="bf16", prefix_tokens=0, num_blocks=None, max_blocks=None, name="",
-                 rng=None):
+                 rng=None, kv_dtype=""):
     """One decode step: sequence s has lens[s] tokens, the last of which is new (written by
-    kv_cache_write before attention). A zero length has no new token (slot -1)."""
+    kv_cache_write before attention). A zero length has no new token (slot -1).
+    kv_dtype "fp8": E4M3 pools with scale FP8_POOL_SCALE (q and new rows stay in dtype)."""
     rng = np.random.default_rng(seed) if rng is None else rng
     lens = np.asarray(lens, dtype=np.int32)
     assert len(lens) == num_seqs
+    assert kv_dtype in ("", "fp8") and (kv_dtype == "" or dtype == "bf16")
     bt, nb, mb, shared = _allocate(rng, lens, block_size, prefix_tokens, num_blocks, max_blocks)
     new_from = np.maximum(lens - 1, 0)
     k_pool, v_pool = _fill_pools(rng, bt, lens, new_from, num_kv_heads, head_dim, block_size,
-                                 nb, dtype)
+                                 nb, kv_dtype or dtype)
     q = _values(rng, (num_seqs, num_q_heads, head_dim), dtype)
     k_new = _values(rng, (num_seqs, num_kv_heads, head_dim), dtype)
     v_new = _values(rng, (num_seqs, num_kv_heads, head_dim), dtype)
@@ -177,9 +208,11 @@ def build_decode(seed, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size
         if n > 0:
             j = int(n) - 1
             slots[s] = int(bt[s, j // block_size]) * block_size + j % block_size
+    sc = FP8_POOL_SCALE if kv_dtype == "fp8" else 1.0
     return Workload("decode", dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                     nb, mb, 1.0 / math.sqrt(head_dim), q, k_pool, v_pool, k_new, v_new, slots,
-                    bt, lens, None, prefix_tokens, shared, name)
+                    bt, lens, None, prefix_tokens, shared, name, kv_dtype=kv_dtype, k_scale=sc,
+                    v_scale=sc)
 
 
 def build_prefill(seed, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, prior_lens,
@@ -219,9 +252,12 @@ CONFIG_NAMES = {
 }
 
 
-def make_config(k: int, seed: int | None = None) -> Workload:
-    """The five workloads, k = 1..5, seeded by default with seed = k."""
+def make_config(k: int, seed: int | None = None, kv_dtype: str = "") -> Workload:
+    """The five workloads, k = 1..5, seeded by default with seed = k. kv_dtype "fp8" gives the
+    decode workloads (2, 3, 4) with E4M3 pools and the same lengths and block tables."""
     seed = k if seed is None else seed
+    if kv_dtype:
+        assert k in (2, 3, 4), "E4M3 pools are built for the bf16 decode workloads"
     rng = np.random.default_rng(seed)
     if k == 1:
         return build_decode(seed, 4, 8, 8, 64, 16, [1, 17, 33, 100], "f32", num_blocks=64,
@@ -229,15 +265,15 @@ def make_config(k: int, seed: int | None = None) -> Workload:
     if k == 2:
         lens = rng.integers(512, 4097, 64)
         return build_decode(seed, 64, 32, 8, 128, 16, lens, "bf16", max_blocks=256, name="c2",
-                            rng=rng)
+                            rng=rng, kv_dtype=kv_dtype)
     if k == 3:
         lens = np.round(np.exp(rng.uniform(math.log(1024), math.log(32768), 32))).astype(int)
         return build_decode(seed, 32, 64, 8, 128, 32, lens, "bf16", max_blocks=1024,
-                            name="c3", rng=rng)
+                            name="c3", rng=rng, kv_dtype=kv_dtype)
     if k == 4:
         suffix = rng.integers(16, 513, 64)
         return build_decode(seed, 64, 32, 8, 128, 16, 2000 + suffix, "bf16", prefix_tokens=2000,
-                            max_blocks=157, name="c4", rng=rng)
+                            max_blocks=157, name="c4", rng=rng, kv_dtype=kv_dtype)
     if k == 5:
         prior = rng.integers(0, 8193, 8)
         return build_prefill(seed, 8, 32, 8, 128, 16, prior, [512] * 8, "bf16", max_blocks=544,

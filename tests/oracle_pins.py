@@ -10,7 +10,9 @@ raises AssertionError when the oracle disagrees with:
     heads),
   * a library routine: torch's CPU float64 scaled_dot_product_attention on the contiguous K/V
     the test scatters into the pool with its own index code,
-  * the flat-index formulas of the ABI header, for block copies between pools.
+  * the flat-index formulas of the ABI header, for block copies between pools,
+  * the OCP E4M3 format: fixed codes, and torch's own float8_e4m3fn conversions (an
+    independent implementation) for every code and for every midpoint between neighbours.
 test_oracle.py runs every pin on the real oracle; test_oracle_mutations.py plants mistakes in a
 copy of the oracle and checks that some pin fails for each.
 """
@@ -414,7 +416,94 @@ def pin_copy_blocks(orc):
     assert np.array_equal(bk, kp) and np.array_equal(bv, vp)
 
 
+def pin_fp8_format(orc):
+    """E4M3: fixed codes; every code's value equals torch's float8_e4m3fn decoding; encoding
+    agrees with torch's on every exact midpoint between neighbouring values (ties to even) and
+    on random values, wherever torch rounds (|x| < 464: beyond, torch gives NaN while the
+    reading taken here saturates to +-448); saturation, signed zero and NaN."""
+    import torch
+    fixed = {0x38: 1.0, 0x7E: 448.0, 0xFE: -448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9,
+             0x07: 7 * 2.0 ** -9, 0x3F: 1.875, 0x40: 2.0, 0x30: 0.5, 0xB8: -1.0, 0x00: 0.0}
+    for code, val in fixed.items():
+        assert orc.fp8_e4m3_value(np.asarray([code], np.uint8))[0] == val, hex(code)
+    assert math.copysign(1.0, orc.fp8_e4m3_value(np.asarray([0x80], np.uint8))[0]) == -1.0
+    assert np.isnan(orc.fp8_e4m3_value(np.asarray([0x7F, 0xFF], np.uint8))).all()
+    codes = np.arange(256, dtype=np.uint8)
+    ours = orc.fp8_e4m3_value(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    assert np.array_equal(ours[~np.isnan(ours)], ref[~np.isnan(ref)])
+    vals = ref[:127]
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    rng = np.random.default_rng(3)
+    rand = (rng.standard_normal(20000) * np.exp2(rng.integers(-14, 9, 20000))).astype(np.float32)
+    x = np.concatenate([vals.astype(np.float32), mids, rand, [450.0, 463.9]]).astype(np.float32)
+    x = np.concatenate([x, -x])
+    x = x[np.abs(x) < 464]
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(orc.fp8_e4m3_encode(x), want)
+    sat = orc.fp8_e4m3_encode(np.float32([464.0, 1e6, np.inf, -500.0, -np.inf]))
+    assert list(sat) == [0x7E, 0x7E, 0x7E, 0xFE, 0xFE]
+    assert list(orc.fp8_e4m3_encode(np.float32([-0.0, -1e-12, np.nan]))) == [0x80, 0x80, 0x7F]
+    # ties by hand: 1.0625 lies halfway between 1.0 (0x38) and 1.125 (0x39) -> the even 0x38;
+    # 1.1875 between 1.125 (0x39) and 1.25 (0x3A) -> 0x3A; 2^-10 between 0 and 2^-9 -> 0
+    assert list(orc.fp8_e4m3_encode(np.float32([1.0625, 1.1875, 2.0 ** -10]))) == [0x38, 0x3A, 0]
+
+
+def pin_fp8_write_and_decode(orc):
+    """The quantising write stores the code of the float32 quotient x / scale (torch computes
+    quotient and code here) at the header's flat indices; decode over E4M3 pools equals the
+    brute-force float32 decode of the same values (code value * scale, exact in float32 for a
+    power-of-two scale), and a non-power-of-two scale scales the scores (K) and the output (V)."""
+    import torch
+    rng = np.random.default_rng(17)
+    nb, hkv, b, d, T = 5, 2, 16, 8, 12
+    kn = wl.bf16_bits(rng.standard_normal((T, hkv, d)).astype(np.float32) * 3)
+    vn = wl.bf16_bits(rng.standard_normal((T, hkv, d)).astype(np.float32) * 3)
+    slots = rng.permutation(nb * b)[:T].astype(np.int32)
+    k0 = np.zeros((nb, hkv, b, d), np.uint8)
+    v0 = np.zeros((nb, hkv, d, b), np.uint8)
+    ks, vs = 0.37, 1.9
+    k2, v2 = orc.kv_cache_write_fp8(k0, v0, kn, vn, slots, b, "bf16", ks, vs)
+    kt = torch.from_numpy(orc.to_f64(kn, "bf16").astype(np.float32)) / torch.tensor(ks)
+    vt = torch.from_numpy(orc.to_f64(vn, "bf16").astype(np.float32)) / torch.tensor(vs)
+    kc = kt.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    vc = vt.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    for i, slot in enumerate(slots):
+        blk, off = divmod(int(slot), b)
+        for h in range(hkv):
+            for x in range(d):
+                assert k2.reshape(-1)[((blk * hkv + h) * b + off) * d + x] == kc[i, h, x]
+                assert v2.reshape(-1)[((blk * hkv + h) * d + x) * b + off] == vc[i, h, x]
+    # decode over fp8 pools: random codes (no NaN) and power-of-two scales
+    s_count, hq = 3, 4
+    kp = rng.integers(0, 256, (nb, hkv, b, d)).astype(np.uint8)
+    vp = rng.integers(0, 256, (nb, hkv, d, b)).astype(np.uint8)
+    kp[(kp & 0x7F) == 0x7F] = 0x3C
+    vp[(vp & 0x7F) == 0x7F] = 0x3C
+    kp = np.where((kp >> 3) & 0xF > 9, kp & 0xCF, kp).astype(np.uint8)  # keep scores moderate
+    bt = np.asarray([[3, 0], [1, 4], [2, 2]], np.int32)
+    lens = np.asarray([20, 5, 32], np.int32)
+    q = wl.bf16_bits(rng.standard_normal((s_count, hq, d)).astype(np.float32))
+    scale = 1 / math.sqrt(d)
+    got = orc.decode(q, kp, vp, bt, lens, scale, "bf16", kv_dtype="fp8", k_scale=0.25,
+                     v_scale=2.0)
+    kf = (torch.from_numpy(kp).view(torch.float8_e4m3fn).float() * 0.25).numpy()
+    vf = (torch.from_numpy(vp).view(torch.float8_e4m3fn).float() * 2.0).numpy()
+    qf = orc.to_f64(q, "bf16").astype(np.float32)
+    want = orc.brute_force_decode(qf, kf, vf, bt, lens, scale, "f32")
+    _assert_close(got, want, 1e-9, "fp8 decode vs brute force")
+    a = orc.decode(q, kp, vp, bt, lens, scale, "bf16", kv_dtype="fp8", k_scale=0.3, v_scale=0.7)
+    b2 = orc.decode(q, kp, vp, bt, lens, scale * 0.3, "bf16", kv_dtype="fp8", k_scale=1.0,
+                    v_scale=1.0)
+    _assert_close(a, 0.7 * b2, 1e-12, "k_scale scales the scores, v_scale the output")
+    row = orc.decode_row(q, kp, vp, bt, lens, scale, "bf16", 2, 3, kv_dtype="fp8",
+                         k_scale=0.3, v_scale=0.7)
+    assert np.array_equal(row, a[2, 3])
+
+
 PINS = [pin_figure_block_table, pin_bf16_decoding, pin_write_roundtrip, pin_decode_brute_force,
         pin_prefill_brute_force, pin_single_token, pin_zero_length, pin_closed_forms,
         pin_block_permutation, pin_shared_equals_duplicated, pin_gqa_equals_repeated_mha,
-        pin_decode_sdpa, pin_prefill_sdpa, pin_row_helpers, pin_copy_blocks]
+        pin_decode_sdpa, pin_prefill_sdpa, pin_row_helpers, pin_copy_blocks, pin_fp8_format,
+        pin_fp8_write_and_decode]

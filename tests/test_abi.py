@@ -108,6 +108,51 @@ def test_copy_blocks_validation():
     assert bd.lib().pkv_last_error()
 
 
+def test_fp8_write_validation():
+    w = bd.lib().pkv_kv_cache_write_fp8
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, 3, 8, 128, 16, 10, bd.PKV_BF16, 0.5, 2.0, None]
+
+    def call(i, x):
+        a = list(ok)
+        a[i] = x
+        return w(*a)
+
+    assert call(5, 0) == bd.PKV_OK
+    assert call(5, -2) == bd.PKV_ERR_INVALID_ARG
+    assert call(1, None) == bd.PKV_ERR_INVALID_ARG
+    assert call(10, bd.PKV_FP8_E4M3) == bd.PKV_ERR_UNSUPPORTED   # inputs are bf16 or fp32
+    assert call(7, 80) == bd.PKV_ERR_UNSUPPORTED
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert call(11, bad) == bd.PKV_ERR_INVALID_ARG
+        assert call(12, bad) == bd.PKV_ERR_INVALID_ARG
+
+
+def test_fp8_decode_validation():
+    L = bd.lib()
+
+    def call(**kw):
+        a = dict(S=4, Hq=32, Hkv=8, D=128, B=16, MB=8, NB=64, scale=0.088, ks=0.0625, vs=0.0625,
+                 mc=0, ws=None, wsb=0, odt=bd.PKV_BF16, q=FAKE)
+        a.update(kw)
+        return L.pkv_paged_attention_decode_fp8(
+            FAKE, a["q"], FAKE, FAKE, FAKE, FAKE, a["S"], a["Hq"], a["Hkv"], a["D"], a["B"],
+            a["MB"], a["NB"], a["scale"], a["ks"], a["vs"], a["mc"], a["ws"], a["wsb"], a["odt"],
+            None)
+
+    assert call(S=0, q=None) == bd.PKV_OK
+    assert call(q=None) == bd.PKV_ERR_INVALID_ARG
+    assert call(ks=0.0) == bd.PKV_ERR_INVALID_ARG
+    assert call(vs=float("nan")) == bd.PKV_ERR_INVALID_ARG
+    assert call(ks=1e38, scale=1e3) == bd.PKV_ERR_INVALID_ARG      # scale * k_scale overflows
+    assert call(D=96) == bd.PKV_ERR_UNSUPPORTED
+    assert call(odt=bd.PKV_FP8_E4M3) == bd.PKV_ERR_UNSUPPORTED
+    assert call(mc=8 * 16 + 1) == bd.PKV_ERR_INVALID_ARG
+    assert call() == bd.PKV_ERR_WORKSPACE
+    need = L.pkv_decode_workspace_size(4, 32, 8, 128, 128, 0, bd.PKV_FP8_E4M3)
+    assert need > 0
+    assert call(ws=FAKE, wsb=need - 1) == bd.PKV_ERR_WORKSPACE
+
+
 def test_prefill_validation():
     L = bd.lib()
     f = L.pkv_paged_attention_prefill_chunk

@@ -38,6 +38,15 @@ MUTANTS = [
     ("copy_v_from_k", "dst_v[d_blk] = src_v[s_blk]", "dst_v[d_blk] = src_k[s_blk].reshape(dst_v[d_blk].shape)"),
     ("copy_direction", "dst_k[d_blk] = src_k[s_blk]", "dst_k[s_blk % dst_k.shape[0]] = src_k[d_blk % src_k.shape[0]]"),
     ("copy_k_skipped", "        dst_k[d_blk] = src_k[s_blk]\n", "        pass\n"),
+    ("fp8_bias", "np.exp2(e - 7.0)", "np.exp2(e - 8.0)"),
+    ("fp8_subnormal_scale", "f / 8.0 * 2.0 ** -6", "f / 8.0 * 2.0 ** -7"),
+    ("fp8_ties_up", "np.where(lo % 2 == 0, lo, hi)", "hi"),
+    ("fp8_nan_code", "(e == 15) & (f == 7)", "(e == 15) & (f == 6)"),
+    ("fp8_negative_zero", "np.where(np.signbit(x.reshape(-1)), 0x80, 0)",
+     "np.where(x.reshape(-1) < 0, 0x80, 0)"),
+    ("fp8_write_multiplies", "to_f64(k_new, in_dtype).astype(np.float32) / ks",
+     "to_f64(k_new, in_dtype).astype(np.float32) * ks"),
+    ("fp8_v_scale_from_k", "return k * k_scale, v * v_scale", "return k * k_scale, v * k_scale"),
     ("prefill_rows_selection", "if wanted is not None and (lo + i, h) not in wanted:",
      "if wanted is not None and (i, h) not in wanted:"),
 ]
