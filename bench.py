@@ -44,6 +44,9 @@ WORKLOADS = {
     # the same decode batches with E4M3 (one byte per element) pools, per-pool scale 1/16
     "decode-8b-fp8": 2,
     "decode-70b-fp8": 3,
+    # the shared-prefix batch through the prefix-aware decode (prefix read once per KV head)
+    "shared-prefix-grouped": 4,
+    "shared-prefix-grouped-fp8": 4,
 }
 # Block-copy workloads, all on the decode-8b pool: copy-on-write of one block per sequence (a
 # fork of every sequence), a device-to-device migration of the blocks of half the sequences,
@@ -258,6 +261,7 @@ def run(args):
 
     cfg = WORKLOADS[args.workload]
     fp8 = args.workload.endswith("-fp8")
+    grouped = args.workload.startswith("shared-prefix-grouped")
     w = wl.make_config(cfg, kv_dtype="fp8" if fp8 else "")
     log(f"workload {args.workload} ({wl.CONFIG_NAMES[cfg]}): S={w.num_seqs} "
         f"sum(n)={int(w.context_lens.sum())} NB={w.num_blocks}")
@@ -279,12 +283,29 @@ def run(args):
             code = bd.PKV_FP8_E4M3
         need = bd.decode_workspace_size(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
                                         w.max_context_len, P, code)
+        if grouped:
+            need = bd.decode_shared_prefix_workspace_size(
+                w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.max_context_len,
+                w.prefix_tokens, code)
+            gstart = to_dev(np.asarray([0, w.num_seqs], np.int32))
+            gpre = to_dev(np.asarray([w.prefix_tokens], np.int32))
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-        P_eff = 0 if fp8 else bd.decode_partition_size(P, w.num_seqs, w.num_kv_heads,
-                                                        w.max_context_len, code)
+        P_eff = 0 if (fp8 or grouped) else bd.decode_partition_size(
+            P, w.num_seqs, w.num_kv_heads, w.max_context_len, code)
 
     def step(i):
         r = reps[i % replicas]
+        if grouped:
+            if fp8:
+                bd.kv_cache_write_fp8(k_new, v_new, r.k_pool, r.v_pool, slots, w.k_scale,
+                                      w.v_scale)
+            else:
+                bd.kv_cache_write(k_new, v_new, r.k_pool, r.v_pool, slots)
+            bd.paged_attention_decode_shared_prefix(
+                out, q, r.k_pool, r.v_pool, bt, ctx, gstart, gpre, w.scale, w.num_seqs,
+                w.prefix_tokens, k_scale=w.k_scale, v_scale=w.v_scale,
+                max_context_len=w.max_context_len, workspace=ws)
+            return
         if fp8:
             bd.kv_cache_write_fp8(k_new, v_new, r.k_pool, r.v_pool, slots, w.k_scale, w.v_scale)
             bd.paged_attention_decode_fp8(out, q, r.k_pool, r.v_pool, bt, ctx, w.scale,
@@ -350,6 +371,8 @@ def run(args):
         dom = "decode_partition"
         dom_bytes = b["kv"] + b["q"] + b["ids"] + b["ctx"] + (0 if "decode_reduce" in kern
                                                               else b["out"])
+        if grouped:  # the prefix-aware method needs each shared prefix block once
+            dom_bytes += unique_decode_kv_bytes(w) - b["kv"]
         dom_us = kern[dom]["avg_us"]
         achieved = dom_bytes / (dom_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -359,7 +382,10 @@ def run(args):
                 "algorithmic_bytes_per_launch": dom_bytes}
         shape = {"decode-8b": "8B-shaped", "decode-70b": "70B-shaped",
                  "shared-prefix": "shared-prefix, 8B-shaped", "decode-8b-fp8": "8B-shaped, fp8 KV",
-                 "decode-70b-fp8": "70B-shaped, fp8 KV"}[args.workload]
+                 "decode-70b-fp8": "70B-shaped, fp8 KV",
+                 "shared-prefix-grouped": "shared-prefix, prefix-aware, 8B-shaped",
+                 "shared-prefix-grouped-fp8": "shared-prefix, prefix-aware, 8B-shaped, fp8 KV",
+                 }[args.workload]
         result.update(
             metric=f"paged decode KV HBM GB/s (% of peak) and decode tokens/sec/GPU, {shape}",
             value=round(value, 1), unit="GB/s", higher_is_better=True,

@@ -279,6 +279,44 @@ int pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_pool,
                                    void* stream);
 
 /*
+ * pkv_paged_attention_decode_shared_prefix -- decode for batches whose sequences share
+ * prompt prefixes, reading each shared prefix once per group instead of once per sequence.
+ * [Inference Engines "Prefix caching" and Serving Engines "How vLLM works": sequences with a
+ *  common prompt prefix point their block tables at the same physical blocks; Shootout 3.2:
+ *  shared blocks are copy-on-write.] The result is pkv_paged_attention_decode's (bf16 pools) or
+ * pkv_paged_attention_decode_fp8's (E4M3 pools); only the order of the arithmetic differs.
+ *
+ *   group_start       int32 [num_groups+1], device: group i is sequences group_start[i] ..
+ *                     group_start[i+1]-1 (groups are consecutive runs covering the batch:
+ *                     group_start[0] = 0, non-decreasing, group_start[num_groups] = num_seqs)
+ *   group_prefix_len  int32 [num_groups], device: tokens every member of group i shares, a
+ *                     multiple of block_size; the first group_prefix_len[i] / block_size
+ *                     entries of the members' block tables are the same physical blocks (the
+ *                     kernel reads them from the first member's table); <= each member's
+ *                     context_len; 0 = no sharing
+ *   max_group_size, max_prefix_len  host bounds on group sizes and group_prefix_len
+ *                     (max_prefix_len a multiple of block_size)
+ *   kv_dtype          PKV_BF16 or PKV_FP8_E4M3 (then k_scale, v_scale as for the fp8 decode;
+ *                     ignored for bf16); q is bf16; out_dtype PKV_BF16 or PKV_F32
+ *   workspace         pkv_decode_shared_prefix_workspace_size(...) bytes
+ * Other arguments as for pkv_paged_attention_decode. Each shared prefix is split into chunks
+ * of 256 tokens; a chunk is attended for 16 (member, query head) rows at a time, and the
+ * private rest of every context goes through the balanced split; a reduce kernel merges the
+ * pieces by log-sum-exp.
+ */
+size_t pkv_decode_shared_prefix_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
+                                               int head_dim, int max_context_len,
+                                               int max_prefix_len, int kv_dtype);
+int pkv_paged_attention_decode_shared_prefix(
+    void* out, const void* q, const void* k_pool, const void* v_pool,
+    const int32_t* block_table, const int32_t* context_lens, const int32_t* group_start,
+    const int32_t* group_prefix_len, int num_groups, int max_group_size, int max_prefix_len,
+    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+    int max_blocks_per_seq, int num_blocks, float scale, int max_context_len, int kv_dtype,
+    float k_scale, float v_scale, void* workspace, size_t workspace_bytes, int out_dtype,
+    void* stream);
+
+/*
  * pkv_paged_attention_prefill_chunk -- a causal chunk of query tokens against the paged cache.
  * [Serving Engines, "How vLLM works": chunked prefill slices a long prompt into pieces that run
  *  interleaved with other sequences' decode steps.] [Shootout 3.1 equation, as for decode.]

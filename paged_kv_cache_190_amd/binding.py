@@ -70,6 +70,12 @@ def lib() -> ctypes.CDLL:
     L.pkv_paged_attention_decode_fp8.restype = i32
     L.pkv_paged_attention_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                                  i32, i32, f32, f32, f32, i32, vp, sz, i32, vp]
+    L.pkv_decode_shared_prefix_workspace_size.restype = sz
+    L.pkv_decode_shared_prefix_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    L.pkv_paged_attention_decode_shared_prefix.restype = i32
+    L.pkv_paged_attention_decode_shared_prefix.argtypes = [
+        vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, f32,
+        i32, i32, f32, f32, vp, sz, i32, vp]
     L.pkv_kv_cache_copy_blocks.restype = i32
     L.pkv_kv_cache_copy_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                            vp]
@@ -243,6 +249,48 @@ def paged_attention_decode_fp8(out, q, k_pool, v_pool, block_table, context_lens
         mb, nb, float(scale), float(k_scale), float(v_scale), int(max_context_len),
         ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
         _dtype_code(out), _stream(stream)), "paged_attention_decode_fp8")
+    return out
+
+
+def decode_shared_prefix_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                        max_context_len, max_prefix_len, kv_dtype=PKV_BF16):
+    return lib().pkv_decode_shared_prefix_workspace_size(num_seqs, num_q_heads, num_kv_heads,
+                                                         head_dim, max_context_len,
+                                                         max_prefix_len, kv_dtype)
+
+
+def paged_attention_decode_shared_prefix(out, q, k_pool, v_pool, block_table, context_lens,
+                                         group_start, group_prefix_len, scale, max_group_size,
+                                         max_prefix_len, k_scale=1.0, v_scale=1.0,
+                                         max_context_len=0, workspace=None, stream=None):
+    """paged_attention_decode (bf16 pools) or paged_attention_decode_fp8 (uint8 E4M3 pools) for
+    a batch in groups of consecutive sequences sharing prefixes: group i is sequences
+    group_start[i] .. group_start[i+1]-1, sharing their first group_prefix_len[i] tokens (the
+    same physical blocks). group_start / group_prefix_len are int32 device tensors."""
+    import torch
+    S, hq, d = q.shape
+    nb, hkv, b, d2 = k_pool.shape
+    if d2 != d or v_pool.shape != (nb, hkv, d, b) or out.shape != q.shape:
+        raise ValueError("inconsistent shapes")
+    if block_table.dim() != 2 or block_table.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_table must be [S][MB], context_lens [S]")
+    ng = group_prefix_len.shape[0]
+    if group_start.shape != (ng + 1,):
+        raise ValueError("group_start must be [num_groups + 1]")
+    kvd = PKV_FP8_E4M3 if _is_fp8_pool(k_pool) else _dtype_code(k_pool)
+    mb = block_table.shape[1]
+    ctx = max_context_len if max_context_len else mb * b
+    need = decode_shared_prefix_workspace_size(S, hq, hkv, d, ctx, max_prefix_len, kvd)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().pkv_paged_attention_decode_shared_prefix(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _i32(block_table, "block_table"), _i32(context_lens, "context_lens"),
+        _i32(group_start, "group_start"), _i32(group_prefix_len, "group_prefix_len"), ng,
+        int(max_group_size), int(max_prefix_len), S, hq, hkv, d, b, mb, nb, float(scale),
+        int(max_context_len), kvd, float(k_scale), float(v_scale),
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+        _dtype_code(out), _stream(stream)), "paged_attention_decode_shared_prefix")
     return out
 
 

@@ -163,8 +163,9 @@ int decode_waves_setting(int default_waves) {
   return default_waves;
 }
 
+// extra_slots: partial slots per row ahead of the balanced split's (the prefix chunks).
 BalancedPlan balanced_plan(int S, int Hq, int Hkv, int D, int max_ctx,
-                           int default_waves = kDefaultDecodeWaves) {
+                           int default_waves = kDefaultDecodeWaves, int extra_slots = 0) {
   BalancedPlan pl{};
   const int G = Hq / Hkv;
   const long long segs = static_cast<long long>(Hkv) * ((G + 15) / 16);
@@ -173,7 +174,8 @@ BalancedPlan balanced_plan(int S, int Hq, int Hkv, int D, int max_ctx,
   pl.waves = static_cast<int>(
       std::max(1LL, std::min<long long>(decode_waves_setting(default_waves),
                                         t_upper / kMinTilesPerWave)));
-  pl.kmax = static_cast<int>((seg_tiles + kMinTilesPerWave - 1) / kMinTilesPerWave + 1);
+  pl.kmax = static_cast<int>((seg_tiles + kMinTilesPerWave - 1) / kMinTilesPerWave + 1) +
+            extra_slots;
   const size_t rows = static_cast<size_t>(S) * Hq * pl.kmax;
   auto align = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   pl.o_off = 0;
@@ -340,8 +342,9 @@ namespace {
 // Balanced split set-up: the plan for a's sizes, and the partial buffers carved out of the
 // caller's workspace.
 int setup_balanced(pkv::DecodeArgs& a, void* workspace, size_t workspace_bytes,
-                   int default_waves) {
-  const BalancedPlan pl = balanced_plan(a.S, a.Hq, a.Hkv, a.D, a.max_ctx, default_waves);
+                   int default_waves, int extra_slots = 0) {
+  const BalancedPlan pl =
+      balanced_plan(a.S, a.Hq, a.Hkv, a.D, a.max_ctx, default_waves, extra_slots);
   if (!workspace || workspace_bytes < pl.bytes)
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.bytes,
                 workspace ? workspace_bytes : static_cast<size_t>(0));
@@ -359,7 +362,12 @@ int setup_balanced(pkv::DecodeArgs& a, void* workspace, size_t workspace_bytes,
   return PKV_OK;
 }
 
-// Checks shared by both decode entry points; fills the size fields of a.
+// Partial slots per row taken by the prefix chunks.
+int prefix_chunks(int max_prefix_len) {
+  return (max_prefix_len + pkv::kPrefixChunkTokens - 1) / pkv::kPrefixChunkTokens;
+}
+
+// Checks shared by the decode entry points; fills the size fields of a.
 int check_decode(pkv::DecodeArgs& a, void* out, const void* q, const void* k_pool,
                  const void* v_pool, const int32_t* block_table, const int32_t* context_lens,
                  int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
@@ -399,6 +407,77 @@ int check_decode(pkv::DecodeArgs& a, void* out, const void* q, const void* k_poo
 }  // namespace
 
 extern "C" {
+
+size_t pkv_decode_shared_prefix_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
+                                               int head_dim, int max_context_len,
+                                               int max_prefix_len, int kv_dtype) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || max_prefix_len < 0)
+    return 0;
+  return balanced_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                       kv_dtype == PKV_FP8_E4M3 ? kDefaultDecodeWavesFp8 : kDefaultDecodeWaves,
+                       prefix_chunks(max_prefix_len))
+      .bytes;
+}
+
+int pkv_paged_attention_decode_shared_prefix(
+    void* out, const void* q, const void* k_pool, const void* v_pool,
+    const int32_t* block_table, const int32_t* context_lens, const int32_t* group_start,
+    const int32_t* group_prefix_len, int num_groups, int max_group_size, int max_prefix_len,
+    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+    int max_blocks_per_seq, int num_blocks, float scale, int max_context_len, int kv_dtype,
+    float k_scale, float v_scale, void* workspace, size_t workspace_bytes, int out_dtype,
+    void* stream) {
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs = %d is negative", num_seqs);
+  if (num_seqs == 0) return PKV_OK;
+  pkv::DecodeArgs a{};
+  int st = check_decode(a, out, q, k_pool, v_pool, block_table, context_lens, num_seqs,
+                        num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                        num_blocks, scale, max_context_len, PKV_BF16, out_dtype);
+  if (st != PKV_OK) return st;
+  if (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3)
+    return fail(PKV_ERR_UNSUPPORTED, "kv_dtype %d: bf16 or E4M3 pools", kv_dtype);
+  if (kv_dtype == PKV_FP8_E4M3) {
+    if (!valid_pool_scale(k_scale) || !valid_pool_scale(v_scale))
+      return fail(PKV_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
+    if (!std::isfinite(scale * k_scale))
+      return fail(PKV_ERR_INVALID_ARG, "scale * k_scale is not finite");
+  }
+  if (!group_start || !group_prefix_len)
+    return fail(PKV_ERR_INVALID_ARG, "null group array");
+  if (num_groups <= 0 || num_groups > num_seqs)
+    return fail(PKV_ERR_INVALID_ARG, "num_groups %d outside [1, num_seqs]", num_groups);
+  if (max_group_size <= 0 || max_group_size > num_seqs)
+    return fail(PKV_ERR_INVALID_ARG, "max_group_size %d outside [1, num_seqs]", max_group_size);
+  if (max_prefix_len < 0 || max_prefix_len % block_size != 0 || max_prefix_len > a.max_ctx)
+    return fail(PKV_ERR_INVALID_ARG,
+                "max_prefix_len %d must be a multiple of block_size within the context bound",
+                max_prefix_len);
+  const int G = num_q_heads / num_kv_heads;
+  const int nch = prefix_chunks(max_prefix_len);
+  const long long col_tiles = (static_cast<long long>(max_group_size) * G + 15) / 16;
+  const long long units = static_cast<long long>(num_groups) * num_kv_heads * nch * col_tiles;
+  const long long waves_p = (units + 7) / 8 * 8;
+  const int default_waves =
+      kv_dtype == PKV_FP8_E4M3 ? kDefaultDecodeWavesFp8 : kDefaultDecodeWaves;
+  st = setup_balanced(a, workspace, workspace_bytes, default_waves, nch);
+  if (st != PKV_OK) return st;
+  if (waves_p + a.waves > 0x7fffffffLL)
+    return fail(PKV_ERR_UNSUPPORTED, "too many prefix units (%lld)", units);
+  a.num_groups = num_groups;
+  a.group_start = group_start;
+  a.group_prefix_len = group_prefix_len;
+  a.prefix_waves = static_cast<int>(waves_p);
+  a.prefix_col_tiles = static_cast<int>(col_tiles);
+  a.prefix_chunks = nch;
+  a.fp8_kv = kv_dtype == PKV_FP8_E4M3;
+  a.k_scale = a.fp8_kv ? k_scale : 1.0f;
+  a.v_scale = a.fp8_kv ? v_scale : 1.0f;
+  a.bf16_in = 1;
+  a.bf16_out = out_dtype == PKV_BF16;
+  return hip_status(pkv::launch_decode(a, static_cast<hipStream_t>(stream)),
+                    "paged_attention_decode_shared_prefix");
+}
 
 int pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_pool,
                                    const void* v_pool, const int32_t* block_table,

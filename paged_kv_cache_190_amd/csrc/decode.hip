@@ -469,47 +469,74 @@ __device__ __forceinline__ int wave_incl_scan_i(int v) {
   return v;
 }
 
+// Shared prefixes (the prefix-aware decode): sequences come in groups of consecutive ones,
+// group i being sequences group_start[i] .. group_start[i+1]-1, whose first group_prefix_len[i]
+// tokens (a multiple of B) are the same physical blocks. Such a prefix is attended once per
+// group: a prefix unit is one wave for (group, KV head, 16 query columns, one chunk of kPrefixChunk
+// prefix tokens), the 16 columns being (member sequence, query head) pairs -- the K/V tile is
+// then shared by 16 useful query rows instead of one sequence's G heads. The private rest of each
+// context goes through the balanced split as usual. A row's partials: the prefix chunks at slots
+// 0 .. pc-1 (pc = ceil(prefix / kPrefixChunk)), then its suffix pieces.
+constexpr int kPrefixChunk = kPrefixChunkTokens;
+
+struct PrefixInfo {
+  const int32_t* group_start;       // [NG+1]
+  const int32_t* group_prefix_len;  // [NG]
+  int NG;
+};
+
+// Prefix length of sequence s (binary search over the group starts).
+__device__ __forceinline__ int seq_prefix_len(const PrefixInfo& pf, int s) {
+  int lo = 0, hi = pf.NG;  // group_start[lo] <= s < group_start[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pf.group_start[mid] <= s) lo = mid; else hi = mid;
+  }
+  return pf.group_prefix_len[lo];
+}
+
 // Balanced split: the batch is a list of 32-token tiles ordered by (sequence, KV head x head
 // group, tile); wave w of W takes tiles [w*T/W, (w+1)*T/W). A (sequence, KV head) segment that
 // one wave covers whole is written as output directly; a segment shared by several waves gets
 // one partial per wave, merged by the reduce kernel. Every wave does the same number of tiles
 // (to within one), whatever the mix of context lengths. Wave 0 also records, per segment, how
-// many waves share it. W is lowered on the device so that each wave gets at least min_tiles
-// tiles, which bounds the partials per segment by ceil(ceil(max_ctx/32) / min_tiles) + 1 = KMAX.
-// KvT: uint16_t for bf16 pools, uint8_t for E4M3 pools (out_scale = the V scale).
-template <int D, int B, typename OutT, typename KvT>
-__global__ __launch_bounds__(64) void decode_balanced_kernel(
-    OutT* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_m,
-    float* __restrict__ part_l, int32_t* __restrict__ seg_count,
-    const uint16_t* __restrict__ q, const KvT* __restrict__ kpool,
-    const KvT* __restrict__ vpool, const int32_t* __restrict__ block_table,
-    const int32_t* __restrict__ context_lens, int S, int Hq, int Hkv, int G, int HG, int MB,
-    int KMAX, int min_tiles, float scale_log2, float out_scale) {
+// many partials its rows have. W is lowered on the device so that each wave gets at least
+// min_tiles tiles, which bounds the partials per segment by ceil(ceil(max_ctx/32) / min_tiles) + 1.
+// With PREFIX, a sequence's tiles start after its group's prefix, partial slots after the prefix
+// chunks' (KSTRIDE slots per row in all), and a segment with prefix chunks is never final.
+template <int D, int B, typename OutT, typename KvT, bool PREFIX>
+__device__ __forceinline__ void balanced_body(
+    int w, int W, OutT* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_m,
+    float* __restrict__ part_l, int32_t* __restrict__ seg_count, const uint16_t* __restrict__ q,
+    const KvT* __restrict__ kpool, const KvT* __restrict__ vpool,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ context_lens, int S,
+    int Hq, int Hkv, int G, int HG, int MB, int KSTRIDE, int min_tiles, float scale_log2,
+    float out_scale, PrefixInfo pf) {
   constexpr bool kFp8 = sizeof(KvT) == 1;
   const int lane = threadIdx.x;
   const int lg = lane >> 4;
-  const int w = blockIdx.x;
   const int segs = Hkv * HG;
+  // tiles of one segment of sequence s, and where they start
+  auto prefix_of = [&](int s) -> int { return PREFIX ? seq_prefix_len(pf, s) : 0; };
+  auto seq_tiles = [&](int s) -> int {
+    return (s < S) ? (context_lens[s] - prefix_of(s) + 31) >> 5 : 0;
+  };
 
   int64_t T = 0;  // tiles of the whole batch
-  for (int base = 0; base < S; base += 64) {
-    const int s = base + lane;
-    const int ts = (s < S) ? (context_lens[s] + 31) >> 5 : 0;
-    T += wave_sum_i(ts);
-  }
+  for (int base = 0; base < S; base += 64) T += wave_sum_i(seq_tiles(base + lane));
   T *= segs;
-  const int64_t Weff =
-      max<int64_t>(1, min<int64_t>(gridDim.x, T / max(1, min_tiles)));
+  const int64_t Weff = max<int64_t>(1, min<int64_t>(W, T / max(1, min_tiles)));
   // wave that owns tile x: the largest w with floor(w*T/Weff) <= x
   auto wave_of = [&](int64_t x) -> int64_t { return (x * Weff + Weff - 1) / T; };
 
-  if (w == 0) {  // segment sharing counts, for the reduce
+  if (w == 0) {  // partial counts per segment, for the reduce
     int64_t cum = 0;
     for (int base = 0; base < S; base += 64) {
       const int s = base + lane;
-      const int ts = (s < S) ? (context_lens[s] + 31) >> 5 : 0;
+      const int ts = seq_tiles(s);
       const int incl = wave_incl_scan_i(ts);
       if (s < S) {
+        const int pc = PREFIX ? (prefix_of(s) + kPrefixChunk - 1) / kPrefixChunk : 0;
         const int64_t seq0 = (cum + incl - ts) * segs;
         for (int j = 0; j < segs; ++j) {
           int cnt = 0;
@@ -517,13 +544,13 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(
             const int64_t a = seq0 + static_cast<int64_t>(j) * ts;
             cnt = static_cast<int>(wave_of(a + ts - 1) - wave_of(a) + 1);
           }
-          seg_count[static_cast<int64_t>(s) * segs + j] = cnt;
+          seg_count[static_cast<int64_t>(s) * segs + j] = cnt + pc;
         }
       }
       cum += __shfl(incl, 63);
     }
   }
-  if (w >= Weff) return;
+  if (w >= Weff || T == 0) return;
   const int64_t x0 = (static_cast<int64_t>(w) * T) / Weff;
   const int64_t x1 = (static_cast<int64_t>(w + 1) * T) / Weff;
   if (x0 >= x1) return;
@@ -535,7 +562,7 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(
     int64_t cum = 0;
     for (int base = 0; base < S && s < 0; base += 64) {
       const int sl = base + lane;
-      const int ts = (sl < S) ? (context_lens[sl] + 31) >> 5 : 0;
+      const int ts = seq_tiles(sl);
       const int incl = wave_incl_scan_i(ts);
       const int64_t end_l = (cum + incl) * segs;
       const uint64_t hit = __ballot(sl < S && end_l > x0);
@@ -549,7 +576,8 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(
   }
   if (s < 0) return;
   int n = context_lens[s];
-  int ts = (n + 31) >> 5;
+  int pre = prefix_of(s);
+  int ts = (n - pre + 31) >> 5;
   int j = static_cast<int>((x0 - sstart) / ts);
   int64_t x = x0;
   while (x < x1) {
@@ -566,22 +594,24 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(
     WaveAttn<D> st;
     attn_init(st);
     const int32_t* bt = block_table + static_cast<int64_t>(s) * MB;
+    const int tb = pre + 32 * t_begin;
+    const int te = min(pre + 32 * t_end, n);
     if constexpr (kFp8) {
       load_q_fp8<D>(qf, q + row * D, hvalid, lg);
-      attend_tiles_fp8<D, B>(st, qf, kpool, vpool, bt, n, g, Hkv, 32 * t_begin,
-                             min(32 * t_end, n), scale_log2);
+      attend_tiles_fp8<D, B>(st, qf, kpool, vpool, bt, n, g, Hkv, tb, te, scale_log2);
     } else {
       load_q<D>(qf, q + row * D, hvalid, lg);
-      attend_tiles<D, B>(st, qf, kpool, vpool, bt, n, g, Hkv, 32 * t_begin, min(32 * t_end, n),
-                         scale_log2);
+      attend_tiles<D, B>(st, qf, kpool, vpool, bt, n, g, Hkv, tb, te, scale_log2);
     }
     const float l_total = xor32_sum(xor16_sum(st.l));
     const int64_t wf = wave_of(a);
+    const int pc = PREFIX ? (pre + kPrefixChunk - 1) / kPrefixChunk : 0;
     const float osc = kFp8 ? out_scale : 1.0f;
     if (hvalid) {
-      if (wf == wave_of(a + ts - 1)) write_final<D>(out + row * D, st, l_total, lg, osc);
-      else if (w - wf < KMAX)  // always true when context_lens respect max_context_len
-        write_partial<D>(part_o, part_m, part_l, row * KMAX + (w - wf), st, l_total, lg, osc);
+      if (pc == 0 && wf == wave_of(a + ts - 1)) write_final<D>(out + row * D, st, l_total, lg, osc);
+      else if (pc + (w - wf) < KSTRIDE)  // always true when context_lens respect max_context_len
+        write_partial<D>(part_o, part_m, part_l, row * KSTRIDE + pc + (w - wf), st, l_total, lg,
+                         osc);
     }
     x = a + t_end;
     if (++j == segs) {  // next non-empty sequence
@@ -590,11 +620,108 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(
         sstart += static_cast<int64_t>(segs) * ts;
         if (++s >= S) break;
         n = context_lens[s];
-        ts = (n + 31) >> 5;
+        pre = prefix_of(s);
+        ts = (n - pre + 31) >> 5;
       } while (ts == 0);
       if (s >= S) break;
     }
   }
+}
+
+// KvT: uint16_t for bf16 pools, uint8_t for E4M3 pools (out_scale = the V scale).
+template <int D, int B, typename OutT, typename KvT>
+__global__ __launch_bounds__(64) void decode_balanced_kernel(
+    OutT* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_m,
+    float* __restrict__ part_l, int32_t* __restrict__ seg_count,
+    const uint16_t* __restrict__ q, const KvT* __restrict__ kpool,
+    const KvT* __restrict__ vpool, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ context_lens, int S, int Hq, int Hkv, int G, int HG, int MB,
+    int KMAX, int min_tiles, float scale_log2, float out_scale) {
+  balanced_body<D, B, OutT, KvT, false>(blockIdx.x, gridDim.x, out, part_o, part_m, part_l,
+                                        seg_count, q, kpool, vpool, block_table, context_lens, S,
+                                        Hq, Hkv, G, HG, MB, KMAX, min_tiles, scale_log2,
+                                        out_scale, PrefixInfo{nullptr, nullptr, 0});
+}
+
+// One prefix unit (see PrefixInfo). Units are numbered (group, KV head, chunk, column tile),
+// column tile fastest; `unit` is that number.
+template <int D, int B, typename OutT, typename KvT>
+__device__ __forceinline__ void prefix_unit(
+    int64_t unit, OutT* __restrict__ out, float* __restrict__ part_o,
+    float* __restrict__ part_m, float* __restrict__ part_l, const uint16_t* __restrict__ q,
+    const KvT* __restrict__ kpool, const KvT* __restrict__ vpool,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ context_lens, int Hq,
+    int Hkv, int G, int MB, int KSTRIDE, int CT, int NCH, float scale_log2, float out_scale,
+    PrefixInfo pf) {
+  constexpr bool kFp8 = sizeof(KvT) == 1;
+  const int lane = threadIdx.x;
+  const int lg = lane >> 4;
+  const int ct = static_cast<int>(unit % CT);
+  int64_t r = unit / CT;
+  const int ch = static_cast<int>(r % NCH);
+  r /= NCH;
+  const int g = static_cast<int>(r % Hkv);
+  const int gi = static_cast<int>(r / Hkv);
+  if (gi >= pf.NG) return;
+  const int s0 = pf.group_start[gi];
+  const int members = pf.group_start[gi + 1] - s0;
+  const int pre = pf.group_prefix_len[gi];
+  const int tok0 = ch * kPrefixChunk;
+  if (tok0 >= pre || ct * 16 >= members * G) return;
+  const int c = ct * 16 + (lane & 15);
+  const bool valid = c < members * G;
+  const int m = valid ? c / G : 0;
+  const int s = s0 + m;
+  const int h = g * G + (valid ? c - m * G : 0);
+  const int64_t row = static_cast<int64_t>(s) * Hq + h;
+  u32x4 qf[D / 32];
+  WaveAttn<D> st;
+  attn_init(st);
+  const int32_t* bt = block_table + static_cast<int64_t>(s0) * MB;  // the shared blocks
+  const int te = min(pre, tok0 + kPrefixChunk);
+  if constexpr (kFp8) {
+    load_q_fp8<D>(qf, q + row * D, valid, lg);
+    attend_tiles_fp8<D, B>(st, qf, kpool, vpool, bt, pre, g, Hkv, tok0, te, scale_log2);
+  } else {
+    load_q<D>(qf, q + row * D, valid, lg);
+    attend_tiles<D, B>(st, qf, kpool, vpool, bt, pre, g, Hkv, tok0, te, scale_log2);
+  }
+  // Each lane's column is its own row: reduce l over the 4 row groups only (lanes l ^ 16, ^ 32).
+  const float l_total = xor32_sum(xor16_sum(st.l));
+  if (!valid) return;
+  const float osc = kFp8 ? out_scale : 1.0f;
+  const int pc = (pre + kPrefixChunk - 1) / kPrefixChunk;
+  if (pc == 1 && context_lens[s] == pre) write_final<D>(out + row * D, st, l_total, lg, osc);
+  else write_partial<D>(part_o, part_m, part_l, row * KSTRIDE + ch, st, l_total, lg, osc);
+}
+
+// Prefix-aware decode: waves [0, Wp) are prefix units, waves [Wp, Wp + Ws) the balanced split
+// of the suffixes. Units are laid out so that the column tiles of one (group, KV head, chunk),
+// which read the same K/V, run on the same XCD (workgroups go to the 8 XCDs round-robin).
+template <int D, int B, typename OutT, typename KvT>
+__global__ __launch_bounds__(64) void decode_prefix_kernel(
+    OutT* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_m,
+    float* __restrict__ part_l, int32_t* __restrict__ seg_count,
+    const uint16_t* __restrict__ q, const KvT* __restrict__ kpool,
+    const KvT* __restrict__ vpool, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ group_start,
+    const int32_t* __restrict__ group_prefix_len, int NG, int S, int Hq, int Hkv, int G, int HG,
+    int MB, int KSTRIDE, int min_tiles, int Wp, int CT, int NCH, float scale_log2,
+    float out_scale) {
+  const PrefixInfo pf{group_start, group_prefix_len, NG};
+  const int b = blockIdx.x;
+  if (b < Wp) {  // Wp is a multiple of 8
+    const int per_xcd = Wp >> 3;
+    const int64_t unit = static_cast<int64_t>(b & 7) * per_xcd + (b >> 3);
+    prefix_unit<D, B, OutT, KvT>(unit, out, part_o, part_m, part_l, q, kpool, vpool,
+                                 block_table, context_lens, Hq, Hkv, G, MB, KSTRIDE, CT, NCH,
+                                 scale_log2, out_scale, pf);
+    return;
+  }
+  balanced_body<D, B, OutT, KvT, true>(b - Wp, gridDim.x - Wp, out, part_o, part_m, part_l,
+                                       seg_count, q, kpool, vpool, block_table, context_lens, S,
+                                       Hq, Hkv, G, HG, MB, KSTRIDE, min_tiles, scale_log2,
+                                       out_scale, pf);
 }
 
 // fp32 path. `rows` are decode sequences (PREFILL = false) or prefill query tokens.
@@ -787,6 +914,20 @@ static void launch_bf16(const DecodeArgs& a, hipStream_t st) {
         a.MB, a.P, a.NP, a.scale * kLog2e);
 }
 
+template <int D, int B, typename OutT, typename KvT>
+static void launch_prefix_t(const DecodeArgs& a, hipStream_t st) {
+  const int G = a.Hq / a.Hkv;
+  const int HG = (G + 15) / 16;
+  const float sl = a.scale * (a.fp8_kv ? a.k_scale : 1.0f) * kLog2e;
+  (void)launch_kernel(K_DECODE_PARTITION, decode_prefix_kernel<D, B, OutT, KvT>,
+      dim3(a.prefix_waves + a.waves), dim3(64), st, static_cast<OutT*>(a.out), a.part_o,
+      a.part_m, a.part_l, a.seg_count, static_cast<const uint16_t*>(a.q),
+      static_cast<const KvT*>(a.k_pool), static_cast<const KvT*>(a.v_pool), a.block_table,
+      a.context_lens, a.group_start, a.group_prefix_len, a.num_groups, a.S, a.Hq, a.Hkv, G, HG,
+      a.MB, a.KMAX, a.min_tiles, a.prefix_waves, a.prefix_col_tiles, a.prefix_chunks, sl,
+      a.fp8_kv ? a.v_scale : 1.0f);
+}
+
 template <int D, int B, bool SPLIT, typename OutT>
 static void launch_f32(const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.S, a.Hq, a.NP);
@@ -798,7 +939,10 @@ static void launch_f32(const DecodeArgs& a, hipStream_t st) {
 
 template <int D, int B, typename OutT>
 static void dispatch_out_t(const DecodeArgs& a, hipStream_t st) {
-  if (a.bf16_in || a.fp8_kv) {
+  if (a.num_groups > 0) {
+    if (a.fp8_kv) launch_prefix_t<D, B, OutT, uint8_t>(a, st);
+    else launch_prefix_t<D, B, OutT, uint16_t>(a, st);
+  } else if (a.bf16_in || a.fp8_kv) {
     launch_bf16<D, B, OutT>(a, st);
   } else {
     if (a.NP > 1) launch_f32<D, B, true, OutT>(a, st);

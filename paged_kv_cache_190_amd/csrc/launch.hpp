@@ -91,7 +91,18 @@ struct DecodeArgs {
   int fp8_kv;
   float k_scale;
   float v_scale;
+  // Shared prefixes (num_groups > 0; balanced): group i is sequences group_start[i] ..
+  // group_start[i+1]-1 sharing their first group_prefix_len[i] tokens. prefix_waves units of
+  // (group, KV head, chunk, 16-column tile) run before the `waves` suffix waves; KMAX is then
+  // the row stride of the partials (prefix chunks first).
+  int num_groups;
+  const int32_t* group_start;
+  const int32_t* group_prefix_len;
+  int prefix_waves;
+  int prefix_col_tiles;
+  int prefix_chunks;
 };
+constexpr int kPrefixChunkTokens = 256;  // tokens of the shared prefix per prefix unit
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 struct PrefillArgs {

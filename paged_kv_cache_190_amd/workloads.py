@@ -215,6 +215,62 @@ def build_decode(seed, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size
                     v_scale=sc)
 
 
+def build_grouped_decode(seed, groups, num_q_heads, num_kv_heads, head_dim, block_size,
+                         dtype="bf16", kv_dtype="", name="", rng=None):
+    """One decode step over groups of consecutive sequences that share prompt prefixes.
+    `groups` is a list of (prefix_tokens, [context lengths of the members]); prefix_tokens is a
+    multiple of B and at most each member's length. Each group's prefix blocks are allocated
+    once and named by every member's table; the rest of each context has private blocks. A
+    member whose context is exactly the prefix has no new token (its last token sits in a shared
+    block). meta holds group_start [G+1] and group_prefix_len [G] (int32)."""
+    rng = np.random.default_rng(seed) if rng is None else rng
+    b = block_size
+    lens, prefix_of, starts, plens = [], [], [0], []
+    for pre, members in groups:
+        assert pre % b == 0 and all(n >= pre for n in members)
+        lens += [int(n) for n in members]
+        prefix_of += [pre] * len(members)
+        starts.append(starts[-1] + len(members))
+        plens.append(pre)
+    lens = np.asarray(lens, dtype=np.int32)
+    S = len(lens)
+    per_seq = [-(-int(n) // b) for n in lens]
+    distinct = sum(pre // b for pre, _ in groups) + sum(
+        nb - p // b for nb, p in zip(per_seq, prefix_of))
+    num_blocks = max(1, math.ceil(1.1 * distinct))
+    mb = max(max(per_seq), 1)
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    bt = np.full((S, mb), -1, dtype=np.int32)
+    nxt = 0
+    for gi, (pre, members) in enumerate(groups):
+        shared = perm[nxt: nxt + pre // b]
+        nxt += pre // b
+        for s in range(starts[gi], starts[gi + 1]):
+            bt[s, : pre // b] = shared
+            own = per_seq[s] - pre // b
+            bt[s, pre // b: per_seq[s]] = perm[nxt: nxt + own]
+            nxt += own
+    new = np.asarray([n > p for n, p in zip(lens, prefix_of)])
+    new_from = np.where(new, lens - 1, lens)
+    k_pool, v_pool = _fill_pools(rng, bt, lens, new_from, num_kv_heads, head_dim, b, num_blocks,
+                                 kv_dtype or dtype)
+    q = _values(rng, (S, num_q_heads, head_dim), dtype)
+    k_new = _values(rng, (S, num_kv_heads, head_dim), dtype)
+    v_new = _values(rng, (S, num_kv_heads, head_dim), dtype)
+    slots = np.full(S, -1, dtype=np.int32)
+    for s in range(S):
+        if new[s]:
+            j = int(lens[s]) - 1
+            slots[s] = int(bt[s, j // b]) * b + j % b
+    sc = FP8_POOL_SCALE if kv_dtype == "fp8" else 1.0
+    meta = {"group_start": np.asarray(starts, np.int32),
+            "group_prefix_len": np.asarray(plens, np.int32)}
+    return Workload("decode", dtype, S, num_q_heads, num_kv_heads, head_dim, b, num_blocks, mb,
+                    1.0 / math.sqrt(head_dim), q, k_pool, v_pool, k_new, v_new, slots, bt, lens,
+                    None, max(plens) if plens else 0, 0, name, meta, kv_dtype=kv_dtype,
+                    k_scale=sc, v_scale=sc)
+
+
 def build_prefill(seed, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, prior_lens,
                   chunk_lens, dtype="bf16", prefix_tokens=0, num_blocks=None, max_blocks=None,
                   name="", rng=None):

@@ -153,6 +153,34 @@ def test_fp8_decode_validation():
     assert call(ws=FAKE, wsb=need - 1) == bd.PKV_ERR_WORKSPACE
 
 
+def test_shared_prefix_validation():
+    L = bd.lib()
+
+    def call(**kw):
+        a = dict(S=4, Hq=32, Hkv=8, D=128, B=16, MB=8, NB=64, ng=2, mgs=2, mpl=32, mc=0,
+                 kvd=bd.PKV_BF16, ks=1.0, vs=1.0, ws=None, wsb=0, gs=FAKE, odt=bd.PKV_BF16)
+        a.update(kw)
+        return L.pkv_paged_attention_decode_shared_prefix(
+            FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["gs"], FAKE, a["ng"], a["mgs"], a["mpl"], a["S"],
+            a["Hq"], a["Hkv"], a["D"], a["B"], a["MB"], a["NB"], 0.088, a["mc"], a["kvd"],
+            a["ks"], a["vs"], a["ws"], a["wsb"], a["odt"], None)
+
+    assert call(S=0) == bd.PKV_OK
+    assert call(gs=None) == bd.PKV_ERR_INVALID_ARG
+    assert call(ng=0) == bd.PKV_ERR_INVALID_ARG
+    assert call(ng=5) == bd.PKV_ERR_INVALID_ARG          # more groups than sequences
+    assert call(mgs=0) == bd.PKV_ERR_INVALID_ARG
+    assert call(mpl=24) == bd.PKV_ERR_INVALID_ARG        # not a multiple of block_size
+    assert call(mpl=8 * 16 + 16) == bd.PKV_ERR_INVALID_ARG
+    assert call(kvd=bd.PKV_F32) == bd.PKV_ERR_UNSUPPORTED
+    assert call(kvd=bd.PKV_FP8_E4M3, ks=0.0) == bd.PKV_ERR_INVALID_ARG
+    assert call() == bd.PKV_ERR_WORKSPACE
+    plain = L.pkv_decode_workspace_size(4, 32, 8, 128, 128, 0, bd.PKV_BF16)
+    pre = L.pkv_decode_shared_prefix_workspace_size(4, 32, 8, 128, 128, 32, bd.PKV_BF16)
+    assert pre > plain                                    # one more partial slot per row
+    assert call(ws=FAKE, wsb=pre - 1) == bd.PKV_ERR_WORKSPACE
+
+
 def test_prefill_validation():
     L = bd.lib()
     f = L.pkv_paged_attention_prefill_chunk
