@@ -695,11 +695,15 @@ __device__ __forceinline__ void prefix_unit(
   else write_partial<D>(part_o, part_m, part_l, row * KSTRIDE + ch, st, l_total, lg, osc);
 }
 
-// Prefix-aware decode: waves [0, Wp) are prefix units, waves [Wp, Wp + Ws) the balanced split
-// of the suffixes. Units are laid out so that the column tiles of one (group, KV head, chunk),
-// which read the same K/V, run on the same XCD (workgroups go to the 8 XCDs round-robin).
+// Prefix-aware decode: Wp prefix-unit waves and Ws = gridDim.x - Wp waves of the balanced split
+// of the suffixes. The two kinds alternate in runs of 8 workgroups (while both last), so that
+// prefix work, which mostly hits in L2, runs beside suffix work, which streams from HBM.
+// Workgroups go to the 8 XCDs round-robin; prefix units are numbered so that the column tiles of
+// one (group, KV head, chunk), which read the same K/V, land on the same XCD. At most 256
+// VGPRs, so that two waves share each SIMD (both kinds of work run side by side).
 template <int D, int B, typename OutT, typename KvT>
-__global__ __launch_bounds__(64) void decode_prefix_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void
+decode_prefix_kernel(
     OutT* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_m,
     float* __restrict__ part_l, int32_t* __restrict__ seg_count,
     const uint16_t* __restrict__ q, const KvT* __restrict__ kpool,
@@ -710,18 +714,31 @@ __global__ __launch_bounds__(64) void decode_prefix_kernel(
     float out_scale) {
   const PrefixInfo pf{group_start, group_prefix_len, NG};
   const int b = blockIdx.x;
-  if (b < Wp) {  // Wp is a multiple of 8
+  const int Ws = gridDim.x - Wp;
+  const int m = min(Wp, Ws & ~7);  // Wp is a multiple of 8
+  bool is_prefix;
+  int idx;
+  if (b < 2 * m) {  // alternating runs of 8; idx keeps b's XCD (idx % 8 == b % 8)
+    is_prefix = ((b >> 3) & 1) == 0;
+    idx = 8 * (b >> 4) + (b & 7);
+  } else if (b < m + Wp) {
+    is_prefix = true;
+    idx = b - m;
+  } else {
+    is_prefix = false;
+    idx = b - Wp;
+  }
+  if (is_prefix) {
     const int per_xcd = Wp >> 3;
-    const int64_t unit = static_cast<int64_t>(b & 7) * per_xcd + (b >> 3);
+    const int64_t unit = static_cast<int64_t>(idx & 7) * per_xcd + (idx >> 3);
     prefix_unit<D, B, OutT, KvT>(unit, out, part_o, part_m, part_l, q, kpool, vpool,
                                  block_table, context_lens, Hq, Hkv, G, MB, KSTRIDE, CT, NCH,
                                  scale_log2, out_scale, pf);
     return;
   }
-  balanced_body<D, B, OutT, KvT, true>(b - Wp, gridDim.x - Wp, out, part_o, part_m, part_l,
-                                       seg_count, q, kpool, vpool, block_table, context_lens, S,
-                                       Hq, Hkv, G, HG, MB, KSTRIDE, min_tiles, scale_log2,
-                                       out_scale, pf);
+  balanced_body<D, B, OutT, KvT, true>(idx, Ws, out, part_o, part_m, part_l, seg_count, q,
+                                       kpool, vpool, block_table, context_lens, S, Hq, Hkv, G,
+                                       HG, MB, KSTRIDE, min_tiles, scale_log2, out_scale, pf);
 }
 
 // fp32 path. `rows` are decode sequences (PREFILL = false) or prefill query tokens.
