@@ -650,7 +650,9 @@ def main():
         if args.summarize_trace:
             print(summarize_trace(args.summarize_trace, args.workload))
         if args.summarize_pmc:
-            dom = "prefill" if args.workload == "prefill-chunk" else "decode_balanced"
+            dom = ("prefill" if args.workload == "prefill-chunk" else
+                   "decode_prefix" if args.workload.startswith("shared-prefix-grouped") else
+                   "copy_blocks" if args.workload in BLOCK_WORKLOADS else "decode_balanced")
             print(summarize_pmc(*args.summarize_pmc, args.workload, dom))
     if args.summarize_trace or args.summarize_pmc or args.summarize_mfma:
         return
