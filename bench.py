@@ -435,11 +435,16 @@ def traffic_from_profile(workload, algorithmic):
 
 
 def kernel_sources_sha():
+    """SHA-256 of the device sources' code: comments dropped and whitespace collapsed, so that
+    editing a comment does not disown counters taken on the same code."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_190_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".hpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+            text = open(os.path.join(csrc, f)).read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
+            h.update(f.encode() + b"\0" + " ".join(text.split()).encode())
     return h.hexdigest()
 
 

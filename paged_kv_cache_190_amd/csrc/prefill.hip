@@ -14,9 +14,12 @@
 // Keys are assigned to the MFMA rows of the first product so that the lane half hb ends up
 // with keys 16*hb .. 16*hb+15, in order: then its P values are the B operand of the second
 // product as they stand, and its V^T operand is 16 contiguous bytes of the dim-major V tile.
-// K/V tiles are double-buffered in LDS: the next tile is read from HBM into registers while the
-// current one is multiplied, then written to the other buffer. Tiles wholly above a wave's
-// causal diagonal are skipped; only diagonal tiles apply the mask.
+// K/V tiles go from HBM straight into LDS (global_load_lds: each lane's 16 bytes land at its own
+// place in the wave's 1 KiB of LDS, no register round trip) through a ring of four stages, so
+// three tiles are in flight while one is multiplied. Waits count those DMAs only (explicit
+// s_waitcnt and a bare barrier per tile); LDS rows are XOR-swizzled instead of padded, so that
+// the 128-bit LDS reads are free of bank conflicts. Tiles wholly above a wave's causal diagonal
+// are skipped; only diagonal tiles apply the mask.
 // Workgroups are numbered so that the XCDs (the GPU deals consecutive workgroups round-robin to
 // its eight XCDs, each with its own L2) get equal shares of the work, with the row tiles of one
 // (sequence, KV head) on the same XCD and the tiles with the most keys first.
