@@ -47,6 +47,9 @@ WORKLOADS = {
     # the shared-prefix batch through the prefix-aware decode (prefix read once per KV head)
     "shared-prefix-grouped": 4,
     "shared-prefix-grouped-fp8": 4,
+    # the decode batches through the fused write-and-decode call (one launch per step)
+    "decode-8b-fused": 2,
+    "decode-70b-fused": 3,
 }
 # Block-copy workloads, all on the decode-8b pool: copy-on-write of one block per sequence (a
 # fork of every sequence), a device-to-device migration of the blocks of half the sequences,
@@ -262,6 +265,7 @@ def run(args):
     cfg = WORKLOADS[args.workload]
     fp8 = args.workload.endswith("-fp8")
     grouped = args.workload.startswith("shared-prefix-grouped")
+    fused = args.workload.endswith("-fused")
     w = wl.make_config(cfg, kv_dtype="fp8" if fp8 else "")
     log(f"workload {args.workload} ({wl.CONFIG_NAMES[cfg]}): S={w.num_seqs} "
         f"sum(n)={int(w.context_lens.sum())} NB={w.num_blocks}")
@@ -290,11 +294,16 @@ def run(args):
             gstart = to_dev(np.asarray([0, w.num_seqs], np.int32))
             gpre = to_dev(np.asarray([w.prefix_tokens], np.int32))
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-        P_eff = 0 if (fp8 or grouped) else bd.decode_partition_size(
+        P_eff = 0 if (fp8 or grouped or fused) else bd.decode_partition_size(
             P, w.num_seqs, w.num_kv_heads, w.max_context_len, code)
 
     def step(i):
         r = reps[i % replicas]
+        if fused:
+            bd.kv_cache_write_and_decode(out, q, k_new, v_new, slots, r.k_pool, r.v_pool, bt, ctx,
+                                         w.scale, max_context_len=w.max_context_len,
+                                         workspace=ws)
+            return
         if grouped:
             if fp8:
                 bd.kv_cache_write_fp8(k_new, v_new, r.k_pool, r.v_pool, slots, w.k_scale,
@@ -371,6 +380,8 @@ def run(args):
         dom = "decode_partition"
         dom_bytes = b["kv"] + b["q"] + b["ids"] + b["ctx"] + (0 if "decode_reduce" in kern
                                                               else b["out"])
+        if fused:  # the one kernel also stores the new tokens
+            dom_bytes += write_bytes(w)
         if w.prefix_tokens:
             # HBM has to deliver each shared prefix block once; the plain decode reads it once
             # per sequence, mostly from cache, the prefix-aware one once per KV head
@@ -388,6 +399,8 @@ def run(args):
                  "decode-70b-fp8": "70B-shaped, fp8 KV",
                  "shared-prefix-grouped": "shared-prefix, prefix-aware, 8B-shaped",
                  "shared-prefix-grouped-fp8": "shared-prefix, prefix-aware, 8B-shaped, fp8 KV",
+                 "decode-8b-fused": "8B-shaped, fused write+decode",
+                 "decode-70b-fused": "70B-shaped, fused write+decode",
                  }[args.workload]
         result.update(
             metric=f"paged decode KV HBM GB/s (% of peak) and decode tokens/sec/GPU, {shape}",

@@ -258,6 +258,32 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_pool, con
                                void* stream);
 
 /*
+ * pkv_kv_cache_write_and_decode -- pkv_kv_cache_write of each sequence's new token followed by
+ * pkv_paged_attention_decode, with the same results, the write folded into the attention
+ * kernel (bf16 pools). [Serving Engines "How vLLM works": each decode step writes the new
+ * token's K/V through the slot mapping and attends over the whole context; Shootout 3.1 and 5.1
+ * for the attention.]
+ *
+ *   k_new, v_new  [num_seqs][num_kv_heads][head_dim] bf16: sequence s's newest token, at
+ *                 position context_lens[s] - 1
+ *   slot_mapping  int32 [num_seqs]: that token's slot (the block table's slot for position
+ *                 n - 1), or negative when the pool already holds every token of s
+ *   k_pool, v_pool  read, and written at the new tokens' slots
+ *   workspace     pkv_decode_workspace_size(..., partition_size = 0, PKV_BF16) bytes
+ * Other arguments, preconditions and errors as for pkv_paged_attention_decode (balanced split;
+ * PKV_DECODE_WAVES applies). The attention takes the newest token's K/V from k_new / v_new, and
+ * the wave that does so also stores them into the pool, so no kernel has to wait for the write.
+ */
+int pkv_kv_cache_write_and_decode(void* out, const void* q, const void* k_new,
+                                  const void* v_new, const int32_t* slot_mapping, void* k_pool,
+                                  void* v_pool, const int32_t* block_table,
+                                  const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                  int num_kv_heads, int head_dim, int block_size,
+                                  int max_blocks_per_seq, int num_blocks, float scale,
+                                  int max_context_len, void* workspace, size_t workspace_bytes,
+                                  int out_dtype, void* stream);
+
+/*
  * pkv_paged_attention_decode_fp8 -- pkv_paged_attention_decode over E4M3 pools.
  * [VRAM black hole section 4: FP8 halves the bytes per cached element; Shootout 3.1 and 5.1 for
  *  the attention itself, as above.]

@@ -76,6 +76,9 @@ def lib() -> ctypes.CDLL:
     L.pkv_paged_attention_decode_shared_prefix.argtypes = [
         vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, f32,
         i32, i32, f32, f32, vp, sz, i32, vp]
+    L.pkv_kv_cache_write_and_decode.restype = i32
+    L.pkv_kv_cache_write_and_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                                i32, i32, i32, i32, f32, i32, vp, sz, i32, vp]
     L.pkv_kv_cache_copy_blocks.restype = i32
     L.pkv_kv_cache_copy_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                            vp]
@@ -203,6 +206,40 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_table, context_lens, sc
         _i32(block_table, "block_table"), _i32(context_lens, "context_lens"), S, hq, hkv, d, b,
         mb, nb, float(scale), int(max_context_len), int(partition_size), ws_ptr, ws_bytes,
         _dtype_code(q), _dtype_code(out), _stream(stream)), "paged_attention_decode")
+    return out
+
+
+def kv_cache_write_and_decode(out, q, k_new, v_new, slot_mapping, k_pool, v_pool, block_table,
+                              context_lens, scale, max_context_len=0, workspace=None,
+                              stream=None):
+    """kv_cache_write of each sequence's newest token (k_new / v_new [S][Hkv][D], slot_mapping
+    [S], negative = none) and paged_attention_decode over the contexts including it, the write
+    folded into the attention kernel (bf16). A workspace is allocated when needed and not
+    given."""
+    import torch
+    S, hq, d = q.shape
+    nb, hkv, b, d2 = k_pool.shape
+    if d2 != d or v_pool.shape != (nb, hkv, d, b) or out.shape != q.shape:
+        raise ValueError("inconsistent shapes")
+    if k_new.shape != (S, hkv, d) or v_new.shape != k_new.shape or slot_mapping.shape != (S,):
+        raise ValueError("k_new / v_new must be [S][Hkv][D], slot_mapping [S]")
+    if block_table.dim() != 2 or block_table.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_table must be [S][MB], context_lens [S]")
+    for t in (q, k_new, v_new, k_pool, v_pool):
+        if t.dtype != torch.bfloat16:
+            raise TypeError("q, k_new, v_new and the pools must be bfloat16")
+    mb = block_table.shape[1]
+    ctx = max_context_len if max_context_len else mb * b
+    if workspace is None:
+        need = decode_workspace_size(S, hq, hkv, d, ctx, 0, PKV_BF16)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().pkv_kv_cache_write_and_decode(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+        _i32(slot_mapping, "slot_mapping"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _i32(block_table, "block_table"), _i32(context_lens, "context_lens"), S, hq, hkv, d, b,
+        mb, nb, float(scale), int(max_context_len), ctypes.c_void_p(workspace.data_ptr()),
+        workspace.numel() * workspace.element_size(), _dtype_code(out), _stream(stream)),
+        "kv_cache_write_and_decode")
     return out
 
 

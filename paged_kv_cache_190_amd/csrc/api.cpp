@@ -479,6 +479,37 @@ int pkv_paged_attention_decode_shared_prefix(
                     "paged_attention_decode_shared_prefix");
 }
 
+int pkv_kv_cache_write_and_decode(void* out, const void* q, const void* k_new,
+                                  const void* v_new, const int32_t* slot_mapping, void* k_pool,
+                                  void* v_pool, const int32_t* block_table,
+                                  const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                  int num_kv_heads, int head_dim, int block_size,
+                                  int max_blocks_per_seq, int num_blocks, float scale,
+                                  int max_context_len, void* workspace, size_t workspace_bytes,
+                                  int out_dtype, void* stream) {
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs = %d is negative", num_seqs);
+  if (num_seqs == 0) return PKV_OK;
+  if (!k_new || !v_new || !slot_mapping)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  pkv::DecodeArgs a{};
+  int st = check_decode(a, out, q, k_pool, v_pool, block_table, context_lens, num_seqs,
+                        num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                        num_blocks, scale, max_context_len, PKV_BF16, out_dtype);
+  if (st != PKV_OK) return st;
+  if (static_cast<long long>(num_blocks) * block_size > 0x7fffffffLL)
+    return fail(PKV_ERR_UNSUPPORTED, "pool of %d blocks exceeds int32 slot numbers", num_blocks);
+  st = setup_balanced(a, workspace, workspace_bytes, kDefaultDecodeWaves);
+  if (st != PKV_OK) return st;
+  a.step = 1;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.slot_mapping = slot_mapping;
+  a.bf16_in = 1;
+  a.bf16_out = out_dtype == PKV_BF16;
+  return hip_status(pkv::launch_decode(a, static_cast<hipStream_t>(stream)),
+                    "kv_cache_write_and_decode");
+}
+
 int pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_pool,
                                    const void* v_pool, const int32_t* block_table,
                                    const int32_t* context_lens, int num_seqs, int num_q_heads,

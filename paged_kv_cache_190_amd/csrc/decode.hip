@@ -70,6 +70,88 @@ __device__ __forceinline__ void load_q(u32x4 (&qf)[D / 32], const uint16_t* qrow
     qf[kk] = hvalid ? load16(qrow + 32 * kk + 8 * lg) : u32x4{0u, 0u, 0u, 0u};
 }
 
+// One 32-token tile's step of the online softmax, bf16 operands already in registers: scores
+// by MFMA, running max / sum / rescale, then P.V by MFMA. Tile tokens at or past lim get no
+// weight; V words of tokens at or past vlim are cleared first (stale slots may hold NaN, and
+// 0 * NaN is NaN).
+template <int D>
+__device__ __forceinline__ void tile_update(WaveAttn<D>& st, const u32x4 (&k)[2][D / 32],
+                                            u32x4 (&v)[D / 16], const u32x4 (&qf)[D / 32],
+                                            int lim, int vlim, float scale_log2, int lg) {
+  constexpr int KK = D / 32;
+  constexpr int DT = D / 16;
+  f32x4 sc[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    sc[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) sc[hf] = mfma16x16x32(k[hf][kk], qf[kk], sc[hf]);
+  }
+  // lane: head column r16, tile tokens 8*lg + 4*hf + e
+  float x[8];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int tt = 8 * lg + 4 * hf + e;
+      x[4 * hf + e] = (tt < lim) ? sc[hf][e] * scale_log2 : -INFINITY;
+    }
+  float tmax = x[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
+  tmax = xor32_max(xor16_max(tmax));
+  const float mnew = fmaxf(st.m, tmax);
+  const float alpha = fast_exp2(st.m - mnew);
+  st.m = mnew;
+  float psum = 0.f;
+  u32x4 pb;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float p0 = fast_exp2(x[2 * w] - mnew);
+    const float p1 = fast_exp2(x[2 * w + 1] - mnew);
+    psum += p0 + p1;
+    pb[w] = pack_bf16x2(p0, p1);
+  }
+  st.l = st.l * alpha + psum;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) st.acc[dt] *= alpha;
+  if (vlim < 32) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int t0 = 8 * lg + 2 * w;
+      const uint32_t keep = (t0 < vlim ? 0x0000ffffu : 0u) | (t0 + 1 < vlim ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) v[dt][w] &= keep;
+    }
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) st.acc[dt] = mfma16x16x32(v[dt], pb, st.acc[dt]);
+}
+
+// A one-token tile from rows outside the pool (the token being added this step): the token
+// takes tile row 0, i.e. K row 0 (held by the lanes of column 0) and V token 0 (element 0 of
+// the lanes of row group 0); everything else is zero and masked.
+template <int D>
+__device__ __forceinline__ void attend_one_token(WaveAttn<D>& st, const u32x4 (&qf)[D / 32],
+                                                 const uint16_t* __restrict__ krow,
+                                                 const uint16_t* __restrict__ vrow,
+                                                 float scale_log2) {
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15;
+  const int lg = lane >> 4;
+  u32x4 k[2][D / 32];
+  u32x4 v[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    k[0][kk] = (r16 == 0) ? load16(krow + 32 * kk + 8 * lg) : u32x4{0u, 0u, 0u, 0u};
+    k[1][kk] = u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt)
+    v[dt] = u32x4{(lg == 0) ? static_cast<uint32_t>(vrow[16 * dt + r16]) : 0u, 0u, 0u, 0u};
+  tile_update<D>(st, k, v, qf, 1, 1, scale_log2, lg);
+}
+
 // Attend the wave's 16 head columns (KV head g) to tokens [tok_begin, tok_end) of one
 // sequence with n tokens, walking 32-token tiles from tok_begin (a multiple of B).
 template <int D, int B>
@@ -128,57 +210,7 @@ __device__ __forceinline__ void attend_tiles(WaveAttn<D>& st, const u32x4 (&qf)[
 
   auto compute = [&](KvTile<D, B>& T, int t) {
     const int tok0 = tok_begin + 32 * t;
-    f32x4 sc[2];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      sc[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) sc[hf] = mfma16x16x32(T.k[hf][kk], qf[kk], sc[hf]);
-    }
-    // lane: head column r16, tile tokens 8*lg + 4*hf + e
-    const int lim = tok_end - tok0;
-    float x[8];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int tt = 8 * lg + 4 * hf + e;
-        x[4 * hf + e] = (tt < lim) ? sc[hf][e] * scale_log2 : -INFINITY;
-      }
-    float tmax = x[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
-    tmax = xor32_max(xor16_max(tmax));
-    const float mnew = fmaxf(st.m, tmax);
-    const float alpha = fast_exp2(st.m - mnew);
-    st.m = mnew;
-    float psum = 0.f;
-    u32x4 pb;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float p0 = fast_exp2(x[2 * w] - mnew);
-      const float p1 = fast_exp2(x[2 * w + 1] - mnew);
-      psum += p0 + p1;
-      pb[w] = pack_bf16x2(p0, p1);
-    }
-    st.l = st.l * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) st.acc[dt] *= alpha;
-    // Token slots at or past n may hold stale words (NaN) or come from a borrowed block:
-    // their P is 0, but 0 * NaN is NaN, so clear the V words themselves.
-    const int vlim = n - tok0;
-    if (vlim < 32) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int t0 = 8 * lg + 2 * w;
-        const uint32_t keep =
-            (t0 < vlim ? 0x0000ffffu : 0u) | (t0 + 1 < vlim ? 0xffff0000u : 0u);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) T.v[dt][w] &= keep;
-      }
-    }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) st.acc[dt] = mfma16x16x32(T.v[dt], pb, st.acc[dt]);
+    tile_update<D>(st, T.k, T.v, qf, tok_end - tok0, n - tok0, scale_log2, lg);
   };
 
   // Software pipeline: every compute of tile t runs while the loads of tile t+1 are in
@@ -495,6 +527,20 @@ __device__ __forceinline__ int seq_prefix_len(const PrefixInfo& pf, int s) {
   return pf.group_prefix_len[lo];
 }
 
+// Fused decode step (kv_cache_write_and_decode): sequence s's newest token, at position n-1,
+// comes from k_new / v_new (slot_mapping[s] >= 0) instead of the pool; the wave whose piece ends
+// at n attends to it as a one-token tile and stores it into the pool slot. Nothing reads that
+// slot in the same launch, so the store needs no ordering. (Merging the split rows inside this
+// kernel as well, by the last wave to finish each row, was measured slower: publishing a
+// partial across XCDs needs a device-scope release, which writes back the XCD's whole L2.)
+struct StepInfo {
+  const uint16_t* k_new;   // [S][Hkv][D]
+  const uint16_t* v_new;
+  const int32_t* slots;    // [S]
+  uint16_t* kpool;         // the pools, written at the new tokens' slots
+  uint16_t* vpool;
+};
+
 // Balanced split: the batch is a list of 32-token tiles ordered by (sequence, KV head x head
 // group, tile); wave w of W takes tiles [w*T/W, (w+1)*T/W). A (sequence, KV head) segment that
 // one wave covers whole is written as output directly; a segment shared by several waves gets
@@ -504,15 +550,17 @@ __device__ __forceinline__ int seq_prefix_len(const PrefixInfo& pf, int s) {
 // min_tiles tiles, which bounds the partials per segment by ceil(ceil(max_ctx/32) / min_tiles) + 1.
 // With PREFIX, a sequence's tiles start after its group's prefix, partial slots after the prefix
 // chunks' (KSTRIDE slots per row in all), and a segment with prefix chunks is never final.
-template <int D, int B, typename OutT, typename KvT, bool PREFIX>
+// With STEP (bf16 only), the new tokens are handled as described at StepInfo.
+template <int D, int B, typename OutT, typename KvT, bool PREFIX, bool STEP = false>
 __device__ __forceinline__ void balanced_body(
     int w, int W, OutT* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_m,
     float* __restrict__ part_l, int32_t* __restrict__ seg_count, const uint16_t* __restrict__ q,
     const KvT* __restrict__ kpool, const KvT* __restrict__ vpool,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ context_lens, int S,
     int Hq, int Hkv, int G, int HG, int MB, int KSTRIDE, int min_tiles, float scale_log2,
-    float out_scale, PrefixInfo pf) {
+    float out_scale, PrefixInfo pf, StepInfo sp = StepInfo{}) {
   constexpr bool kFp8 = sizeof(KvT) == 1;
+  static_assert(!STEP || (!PREFIX && !kFp8), "the fused step is built for plain bf16 decode");
   const int lane = threadIdx.x;
   const int lg = lane >> 4;
   const int segs = Hkv * HG;
@@ -599,16 +647,35 @@ __device__ __forceinline__ void balanced_body(
     if constexpr (kFp8) {
       load_q_fp8<D>(qf, q + row * D, hvalid, lg);
       attend_tiles_fp8<D, B>(st, qf, kpool, vpool, bt, n, g, Hkv, tb, te, scale_log2);
+    } else if constexpr (STEP) {
+      load_q<D>(qf, q + row * D, hvalid, lg);
+      const int slot = sp.slots[s];
+      const int np = slot >= 0 ? n - 1 : n;  // tokens read from the pool
+      attend_tiles<D, B>(st, qf, kpool, vpool, bt, np, g, Hkv, tb, min(te, np), scale_log2);
+      if (slot >= 0 && te == n) {
+        const int64_t src = (static_cast<int64_t>(s) * Hkv + g) * D;
+        attend_one_token<D>(st, qf, sp.k_new + src, sp.v_new + src, scale_log2);
+        if (hgrp == 0) {  // store the token: K row (16-byte pieces), V column (stride B)
+          const int64_t blk = slot / B;
+          const int off = slot - static_cast<int>(blk) * B;
+          const int64_t tile = blk * Hkv + g;
+          if (lane < D / 8)
+            *reinterpret_cast<u32x4*>(sp.kpool + (tile * B + off) * D + 8 * lane) =
+                load16(sp.k_new + src + 8 * lane);
+          for (int d = lane; d < D; d += 64) sp.vpool[(tile * D + d) * B + off] = sp.v_new[src + d];
+        }
+      }
     } else {
       load_q<D>(qf, q + row * D, hvalid, lg);
       attend_tiles<D, B>(st, qf, kpool, vpool, bt, n, g, Hkv, tb, te, scale_log2);
     }
     const float l_total = xor32_sum(xor16_sum(st.l));
     const int64_t wf = wave_of(a);
+    const int64_t wl = wave_of(a + ts - 1);
     const int pc = PREFIX ? (pre + kPrefixChunk - 1) / kPrefixChunk : 0;
     const float osc = kFp8 ? out_scale : 1.0f;
     if (hvalid) {
-      if (pc == 0 && wf == wave_of(a + ts - 1)) write_final<D>(out + row * D, st, l_total, lg, osc);
+      if (pc == 0 && wf == wl) write_final<D>(out + row * D, st, l_total, lg, osc);
       else if (pc + (w - wf) < KSTRIDE)  // always true when context_lens respect max_context_len
         write_partial<D>(part_o, part_m, part_l, row * KSTRIDE + pc + (w - wf), st, l_total, lg,
                          osc);
@@ -641,6 +708,22 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(
                                         seg_count, q, kpool, vpool, block_table, context_lens, S,
                                         Hq, Hkv, G, HG, MB, KMAX, min_tiles, scale_log2,
                                         out_scale, PrefixInfo{nullptr, nullptr, 0});
+}
+
+// kv_cache_write_and_decode for bf16 pools (see StepInfo).
+template <int D, int B, typename OutT>
+__global__ __launch_bounds__(64) void decode_step_kernel(
+    OutT* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_m,
+    float* __restrict__ part_l, int32_t* __restrict__ seg_count, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const int32_t* __restrict__ slots, uint16_t* __restrict__ kpool,
+    uint16_t* __restrict__ vpool, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ context_lens, int S, int Hq, int Hkv, int G, int HG, int MB,
+    int KMAX, int min_tiles, float scale_log2) {
+  balanced_body<D, B, OutT, uint16_t, false, true>(
+      blockIdx.x, gridDim.x, out, part_o, part_m, part_l, seg_count, q, kpool, vpool,
+      block_table, context_lens, S, Hq, Hkv, G, HG, MB, KMAX, min_tiles, scale_log2, 1.0f,
+      PrefixInfo{nullptr, nullptr, 0}, StepInfo{k_new, v_new, slots, kpool, vpool});
 }
 
 // One prefix unit (see PrefixInfo). Units are numbered (group, KV head, chunk, column tile),
@@ -945,6 +1028,19 @@ static void launch_prefix_t(const DecodeArgs& a, hipStream_t st) {
       a.fp8_kv ? a.v_scale : 1.0f);
 }
 
+template <int D, int B, typename OutT>
+static void launch_step_t(const DecodeArgs& a, hipStream_t st) {
+  const int G = a.Hq / a.Hkv;
+  const int HG = (G + 15) / 16;
+  (void)launch_kernel(K_DECODE_PARTITION, decode_step_kernel<D, B, OutT>, dim3(a.waves),
+      dim3(64), st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l, a.seg_count,
+      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_new),
+      static_cast<const uint16_t*>(a.v_new), a.slot_mapping,
+      static_cast<uint16_t*>(const_cast<void*>(a.k_pool)),
+      static_cast<uint16_t*>(const_cast<void*>(a.v_pool)), a.block_table, a.context_lens, a.S,
+      a.Hq, a.Hkv, G, HG, a.MB, a.KMAX, a.min_tiles, a.scale * kLog2e);
+}
+
 template <int D, int B, bool SPLIT, typename OutT>
 static void launch_f32(const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.S, a.Hq, a.NP);
@@ -956,7 +1052,9 @@ static void launch_f32(const DecodeArgs& a, hipStream_t st) {
 
 template <int D, int B, typename OutT>
 static void dispatch_out_t(const DecodeArgs& a, hipStream_t st) {
-  if (a.num_groups > 0) {
+  if (a.step) {
+    launch_step_t<D, B, OutT>(a, st);
+  } else if (a.num_groups > 0) {
     if (a.fp8_kv) launch_prefix_t<D, B, OutT, uint8_t>(a, st);
     else launch_prefix_t<D, B, OutT, uint16_t>(a, st);
   } else if (a.bf16_in || a.fp8_kv) {

@@ -101,6 +101,12 @@ struct DecodeArgs {
   int prefix_waves;
   int prefix_col_tiles;
   int prefix_chunks;
+  // Fused write + decode (bf16, balanced): token s's newest K/V come from k_new / v_new when
+  // slot_mapping[s] >= 0, and the same launch stores them into the pool.
+  int step;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* slot_mapping;
 };
 constexpr int kPrefixChunkTokens = 256;  // tokens of the shared prefix per prefix unit
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
