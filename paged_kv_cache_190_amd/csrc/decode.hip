@@ -924,17 +924,24 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
 // One workgroup per (sequence, query head). Fixed partitions (seg_count == nullptr): the row has
 // ceil(n / P) partials. Balanced split: seg_count gives the number of waves that shared the
 // row's segment; 1 means the output was written already, 0 an empty context.
+// Latency: the row's count and the (m, l) of its first 64 slots are loaded together (slots past
+// the count hold stale values and are ignored), then all partial outputs with their loads in
+// flight together: two dependent round trips to memory.
 template <typename OutT>
 __global__ __launch_bounds__(64) void decode_reduce_kernel(
     OutT* __restrict__ out, const float* __restrict__ part_o, const float* __restrict__ part_m,
     const float* __restrict__ part_l, const int32_t* __restrict__ context_lens,
     const int32_t* __restrict__ seg_count, int Hq, int G, int HG, int D, int P, int KMAX) {
-  __shared__ float wts[64];
   const int h = blockIdx.x;
   const int s = blockIdx.y;
   const int tid = threadIdx.x;
   const int64_t row = static_cast<int64_t>(s) * Hq + h;
   OutT* o = out + row * D;
+  const float* pm = part_m + row * KMAX;
+  const float* pl = part_l + row * KMAX;
+  const float* po = part_o + row * KMAX * D;
+  const float m0 = (tid < KMAX) ? pm[tid] : -INFINITY;
+  const float l0 = (tid < KMAX) ? pl[tid] : 0.f;
   int cnt;
   if (seg_count) {
     const int g = h / G;
@@ -949,32 +956,44 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(
     for (int d = tid; d < D; d += 64) store_out(o + d, 0.0f);
     return;
   }
-  const float* pm = part_m + row * KMAX;
-  const float* pl = part_l + row * KMAX;
-  const float* po = part_o + row * KMAX * D;
-  float M = -INFINITY;
-  for (int k = tid; k < cnt; k += 64) M = fmaxf(M, pm[k]);
+  float M = (tid < cnt) ? m0 : -INFINITY;
+  for (int k = tid + 64; k < cnt; k += 64) M = fmaxf(M, pm[k]);
 #pragma unroll
   for (int mk = 32; mk >= 1; mk >>= 1) M = fmaxf(M, __shfl_xor(M, mk));
+  const bool two = tid + 64 < D;
   float acc0 = 0.f, acc1 = 0.f, wsum = 0.f;
   for (int k0 = 0; k0 < cnt; k0 += 64) {
     const int k = k0 + tid;
-    const float wk = (k < cnt) ? pl[k] * fast_exp2(pm[k] - M) : 0.f;
-    wts[tid] = wk;
-    __syncthreads();
+    float wk = 0.f;
+    if (k < cnt) wk = (k0 == 0) ? l0 * fast_exp2(m0 - M) : pl[k] * fast_exp2(pm[k] - M);
     const int kn = min(64, cnt - k0);
-    for (int i = 0; i < kn; ++i) {
-      const float wi = wts[i];
-      wsum += wi;
-      const float* pi = po + static_cast<int64_t>(k0 + i) * D;
-      acc0 += wi * pi[tid];
-      if (tid + 64 < D) acc1 += wi * pi[tid + 64];
+    const float* pk = po + static_cast<int64_t>(k0) * D;
+    int i = 0;
+    for (; i + 4 <= kn; i += 4) {  // four partials' loads in flight together
+      float a[4], b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a[u] = pk[static_cast<int64_t>(i + u) * D + tid];
+        b[u] = two ? pk[static_cast<int64_t>(i + u) * D + tid + 64] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), i + u));
+        wsum += wi;
+        acc0 += wi * a[u];
+        acc1 += wi * b[u];
+      }
     }
-    __syncthreads();
+    for (; i < kn; ++i) {
+      const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), i));
+      wsum += wi;
+      acc0 += wi * pk[static_cast<int64_t>(i) * D + tid];
+      if (two) acc1 += wi * pk[static_cast<int64_t>(i) * D + tid + 64];
+    }
   }
   const float inv = 1.0f / wsum;
   store_out(o + tid, acc0 * inv);
-  if (tid + 64 < D) store_out(o + tid + 64, acc1 * inv);
+  if (two) store_out(o + tid + 64, acc1 * inv);
 }
 
 // ------------------------------------------------------------------------------ launchers
