@@ -5,9 +5,10 @@
 // Sequence s holds n tokens, the last c of which are this chunk (its K/V already written);
 // chunk row i sits at position r + i, r = n - c, and attends to keys 0 .. r + i.
 //
-// bf16 path (matrix cores). A workgroup of four waves owns (sequence, group of query heads
+// bf16 path (matrix cores). A workgroup of eight waves owns (sequence, group of query heads
 // sharing one KV head, tile of chunk rows). Each wave owns 32 query rows of one head, so the
-// heads of a KV group share every K/V tile the workgroup stages into LDS. Per 32-key tile:
+// heads of a KV group, and two to eight row tiles, share every K/V tile the workgroup stages
+// into LDS. Per 32-key tile:
 //   S^T[32 keys][32 rows] = K_tile . Q^T      one 32x32x16 MFMA per 16 dims
 //   online softmax per row (a lane owns a query row; the two lane halves hold 16 keys each)
 //   O^T[D][32 rows]      += V_tile^T . P^T    two 32x32x16 MFMAs per 32 dims
@@ -15,8 +16,9 @@
 // with keys 16*hb .. 16*hb+15, in order: then its P values are the B operand of the second
 // product as they stand, and its V^T operand is 16 contiguous bytes of the dim-major V tile.
 // K/V tiles go from HBM straight into LDS (global_load_lds: each lane's 16 bytes land at its own
-// place in the wave's 1 KiB of LDS, no register round trip) through a ring of four stages, so
-// three tiles are in flight while one is multiplied. Waits count those DMAs only (explicit
+// place in the wave's 1 KiB of LDS, no register round trip) through a ring of six stages, so
+// five tiles are in flight while one is multiplied (104 KB of LDS: one workgroup per CU, two
+// waves per SIMD). Waits count those DMAs only (explicit
 // s_waitcnt and a bare barrier per tile); LDS rows are XOR-swizzled instead of padded, so that
 // the 128-bit LDS reads are free of bank conflicts. Tiles wholly above a wave's causal diagonal
 // are skipped; only diagonal tiles apply the mask.
@@ -55,23 +57,27 @@ __device__ __forceinline__ int kswz(int row) {
 }
 __device__ __forceinline__ int vswz(int d) { return (d >> 2) & 3; }  // 4 chunks, 4 rows per line
 
+constexpr int kPrefillWaves = 8;  // waves per workgroup
+
 template <int D, int B, typename OutT>
-__global__ __launch_bounds__(256) void prefill_bf16_kernel(
+__global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
     OutT* __restrict__ out, const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q_lens,
     const int32_t* __restrict__ context_lens, const uint16_t* __restrict__ kpool,
     const uint16_t* __restrict__ vpool, const int32_t* __restrict__ block_table, int Hq, int Hkv,
     int G, int HW, int MB, int n_tiles, int n_groups, float scale_log2, int neg_scale) {
   constexpr int KK = D / 16;             // QK MFMA steps
   constexpr int DT = D / 32;             // PV output tiles
-  constexpr int NS = 4;                  // pipeline stages (prefetch distance NS - 1)
+  constexpr int NW = kPrefillWaves;
+  constexpr int NT = 64 * NW;            // threads
+  constexpr int NS = 6;                  // pipeline stages (prefetch distance NS - 1)
   constexpr int KROW = 2 * D;            // bytes of one K row in LDS
   constexpr int CPR = D / 8;             // 16-byte chunks per K row
   constexpr int K_BYTES = 32 * KROW;     // K tile [32 keys][D]
   constexpr int V_BYTES = D * 64;        // V tile [D][32 keys]
   constexpr int STAGE = K_BYTES + V_BYTES;
-  constexpr int KI = K_BYTES / 4096;     // DMA instructions per thread for K (4 waves x 1 KiB)
-  constexpr int VI = V_BYTES / 4096;
-  constexpr int LPT = KI + VI;           // vector-memory operations per thread per tile
+  constexpr int KC = K_BYTES / 1024;     // 1 KiB DMA instructions for K (V follows at KC)
+  constexpr int LPT = STAGE / 1024 / NW; // DMA instructions per wave (and per thread) per tile
+  static_assert(LPT >= 1 && (STAGE / 1024) % NW == 0, "DMA work must split evenly over waves");
   constexpr int kIdCap = 2048;           // block ids staged in LDS at a time
   // One LDS object holds the stages and, after them, the block-id window.
   __shared__ __attribute__((aligned(16))) unsigned char smem[NS * STAGE + 4 * kIdCap];
@@ -105,7 +111,7 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
   const int col = lane & 31;
   const int hb = lane >> 5;
   const int head = g * G + grp * HW + (wave % HW);
-  const int WGT = 32 * (4 / HW);
+  const int WGT = 32 * (NW / HW);
 
   const int q0 = cu_q_lens[s];
   const int c = cu_q_lens[s + 1] - q0;
@@ -145,13 +151,13 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
   int win = 0;
   auto load_window = [&](int first) {
     const int cnt = min(kIdCap, nblk - first);
-    int v[kIdCap / 256];
+    int v[kIdCap / NT];
 #pragma unroll
-    for (int j = 0; j < kIdCap / 256; ++j)  // all loads in flight before any store
-      v[j] = (tid + 256 * j < cnt) ? bt[first + tid + 256 * j] : 0;
+    for (int j = 0; j < kIdCap / NT; ++j)  // all loads in flight before any store
+      v[j] = (tid + NT * j < cnt) ? bt[first + tid + NT * j] : 0;
 #pragma unroll
-    for (int j = 0; j < kIdCap / 256; ++j)
-      if (tid + 256 * j < cnt) ids[tid + 256 * j] = v[j];
+    for (int j = 0; j < kIdCap / NT; ++j)
+      if (tid + NT * j < cnt) ids[tid + NT * j] = v[j];
   };
   load_window(0);
   // q and the first ids must have arrived before the tile DMAs start counting in the same
@@ -160,26 +166,30 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
   __syncthreads();
   auto block_id = [&](int lb) -> int64_t { return ids[min(lb, nblk - 1) - win]; };
 
-  // DMA of key tile t into stage t % NS. K: wave instruction j covers physical rows
-  // 4*(KI*wave + j) .. (D = 128); V: 16 dims x 32 keys per instruction. Block ids are
+  // DMA of key tile t into stage t % NS: STAGE / 1 KiB instructions, LPT per wave; instruction
+  // c (= LPT * wave + j) fills bytes c KiB .. of the stage. K instructions (c < KC) cover
+  // 64 / CPR physical key rows each, V instructions 16 dims x 32 keys. Block ids are
   // wave-uniform per tile (two candidates when B = 16); a lane's offset inside the block tile
   // does not change from tile to tile (tiles start at multiples of 32, which B divides or
-  // equals), so it is computed once.
-  int koff[KI], voff[VI];
-  bool ksel[KI], vsel[VI];
+  // equals), so it is computed once. Each wave's instructions are all K or all V.
+  int soff[LPT];
+  bool ssel[LPT];
+  bool sk[LPT];
 #pragma unroll
-  for (int j = 0; j < KI; ++j) {
-    const int prow = (KI * wave + j) * (64 / CPR) + lane / CPR;
-    const int chunk = (lane % CPR) ^ kswz<D>(prow);
-    koff[j] = (prow % B) * D + 8 * chunk;
-    ksel[j] = B == 16 && prow >= 16;
-  }
-#pragma unroll
-  for (int j = 0; j < VI; ++j) {
-    const int d = (VI * wave + j) * 16 + lane / 4;
-    const int chunk = (lane & 3) ^ vswz(d);  // keys 8*chunk .. 8*chunk+7
-    voff[j] = d * B + (8 * chunk) % B;
-    vsel[j] = B == 16 && chunk >= 2;
+  for (int j = 0; j < LPT; ++j) {
+    const int c = LPT * wave + j;
+    sk[j] = c < KC;
+    if (c < KC) {
+      const int prow = c * (64 / CPR) + lane / CPR;
+      const int chunk = (lane % CPR) ^ kswz<D>(prow);
+      soff[j] = (prow % B) * D + 8 * chunk;
+      ssel[j] = B == 16 && prow >= 16;
+    } else {
+      const int d = (c - KC) * 16 + lane / 4;
+      const int chunk = (lane & 3) ^ vswz(d);  // keys 8*chunk .. 8*chunk+7
+      soff[j] = d * B + (8 * chunk) % B;
+      ssel[j] = B == 16 && chunk >= 2;
+    }
   }
   auto issue = [&](int t) {
     unsigned char* st = smem + (t % NS) * STAGE;
@@ -191,21 +201,14 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
       load_window(win);
       __syncthreads();
     }
-    const uint16_t* kb0 = kg + block_id(lb0) * blk_stride;
-    const uint16_t* vb0 = vg + block_id(lb0) * blk_stride;
-    const uint16_t* kb1 = (B == 16) ? kg + block_id(lb0 + 1) * blk_stride : kb0;
-    const uint16_t* vb1 = (B == 16) ? vg + block_id(lb0 + 1) * blk_stride : vb0;
+    const int64_t id0 = block_id(lb0);
+    const int64_t id1 = (B == 16) ? block_id(lb0 + 1) : id0;
     // (The source pointer is a named variable: given a conditional expression directly, the
     // builtin makes clang drop this kernel's host-side launch stub without a diagnostic.)
 #pragma unroll
-    for (int j = 0; j < KI; ++j) {
-      const uint16_t* src = (ksel[j] ? kb1 : kb0) + koff[j];
-      __builtin_amdgcn_global_load_lds(src, st + (KI * wave + j) * 1024, 16, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < VI; ++j) {
-      const uint16_t* src = (vsel[j] ? vb1 : vb0) + voff[j];
-      __builtin_amdgcn_global_load_lds(src, st + K_BYTES + (VI * wave + j) * 1024, 16, 0, 0);
+    for (int j = 0; j < LPT; ++j) {
+      const uint16_t* src = (sk[j] ? kg : vg) + (ssel[j] ? id1 : id0) * blk_stride + soff[j];
+      __builtin_amdgcn_global_load_lds(src, st + (LPT * wave + j) * 1024, 16, 0, 0);
     }
   };
 
@@ -306,8 +309,12 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
   for (int t = 0; t < NS - 1; ++t)
     if (t < ntiles) issue(t);
   for (int t = 0; t < ntiles; ++t) {
+    // wait for tile t, leaving the `ahead` tiles issued after it in flight
     const int ahead = min(NS - 2, ntiles - 1 - t);
-    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPT));
+    static_assert(NS - 2 <= 4, "one wait per possible depth below");
+    if (ahead >= 4) __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * LPT));
+    else if (ahead == 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * LPT));
+    else if (ahead == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPT));
     else if (ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPT));
     else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_barrier();
@@ -333,11 +340,12 @@ template <int D, int B, typename OutT>
 static void launch_t(const PrefillArgs& a, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   const int HW = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
-  const int WGT = 32 * (4 / HW);
+  const int WGT = 32 * (kPrefillWaves / HW);
   const int n_tiles = (a.max_q_len + WGT - 1) / WGT;
   const int n_groups = G / HW;
   dim3 grid(n_tiles, a.Hkv * n_groups, a.S);
-  (void)launch_kernel(K_PREFILL, prefill_bf16_kernel<D, B, OutT>, dim3(grid), dim3(256), st,
+  (void)launch_kernel(K_PREFILL, prefill_bf16_kernel<D, B, OutT>, dim3(grid),
+      dim3(64 * kPrefillWaves), st,
       static_cast<OutT*>(a.out), static_cast<const uint16_t*>(a.q), a.cu_q_lens, a.context_lens,
       static_cast<const uint16_t*>(a.k_pool), static_cast<const uint16_t*>(a.v_pool), a.block_table,
       a.Hq, a.Hkv, G, HW, a.MB, n_tiles, n_groups, fmaxf(fabsf(a.scale) * kLog2eP, 1e-30f),

@@ -250,6 +250,7 @@ PREFILL_CASES = [
     ("empty_chunk", 205, 3, 8, 2, 128, 16, [5, 7, 0], [0, 9, 1], "bf16"),
     ("f32", 206, 2, 4, 2, 64, 16, [20, 0], [5, 17], "f32"),
     ("f32_d128_b32", 207, 2, 8, 2, 128, 32, [40, 3], [9, 33], "f32"),
+    ("g3_long_chunks", 208, 2, 6, 2, 128, 16, [100, 0], [300, 257], "bf16"),
 ]
 
 
