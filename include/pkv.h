@@ -290,7 +290,7 @@ int pkv_kv_cache_write_and_decode(void* out, const void* q, const void* k_new,
  * The pools hold E4M3 codes written by pkv_kv_cache_write_fp8 with the same k_scale and
  * v_scale (finite, > 0); K's value is code value * k_scale, V's is code value * v_scale, and
  * with those values the result is pkv_paged_attention_decode's. q is bf16; out_dtype PKV_BF16
- * or PKV_F32. The context is always split the balanced way (2048 waves by default;
+ * or PKV_F32. The context is always split the balanced way (1024 waves by default;
  * PKV_DECODE_WAVES overrides it); workspace: pkv_decode_workspace_size(..., dtype =
  * PKV_FP8_E4M3) bytes. Other arguments, preconditions and errors as for
  * pkv_paged_attention_decode. Unwritten slots may hold any code, NaN included.

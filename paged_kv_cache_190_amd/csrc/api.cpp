@@ -145,8 +145,9 @@ size_t fixed_workspace_bytes(int S, int Hq, int D, int NP) {
 // Balanced split (bf16 inputs, partition_size == 0).
 constexpr int kMinTilesPerWave = 8;     // 256 tokens
 constexpr int kDefaultDecodeWaves = 1024;
-// An E4M3 tile is half the bytes of a bf16 one; twice the waves keep as many bytes in flight.
-constexpr int kDefaultDecodeWavesFp8 = 2048;
+// E4M3 pools: the same count measured best (768 - 2048 tried; their tile loop keeps three
+// tiles in flight instead).
+constexpr int kDefaultDecodeWavesFp8 = 1024;
 
 struct BalancedPlan {
   int waves;

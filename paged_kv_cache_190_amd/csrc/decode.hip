@@ -274,7 +274,8 @@ __device__ __forceinline__ u32x2 load8(const void* p) {
 
 // attend_tiles for E4M3 pools: the same tiles, token-to-row assignment, softmax and pipeline;
 // only the loads (bytes) and the widening before each product differ.
-template <int D, int B>
+// DEPTH: register sets in the tile pipeline (3, or 2 where registers are tighter).
+template <int D, int B, int DEPTH = 3>
 __device__ __forceinline__ void attend_tiles_fp8(WaveAttn<D>& st, const u32x4 (&qf)[D / 32],
                                                  const uint8_t* __restrict__ kpool,
                                                  const uint8_t* __restrict__ vpool,
@@ -384,27 +385,57 @@ __device__ __forceinline__ void attend_tiles_fp8(WaveAttn<D>& st, const u32x4 (&
     for (int dt = 0; dt < DT; ++dt) st.acc[dt] = mfma16x16x32(vv[dt], pb, st.acc[dt]);
   };
 
+  // Three register sets: two tiles' loads stay in flight during each compute (an E4M3 tile is
+  // half the bytes of a bf16 one, so the bf16 loop's two-deep pipeline would keep half the
+  // bytes in flight).
   constexpr int kChunkTiles = 64 * B / 32;
-  KvTile8<D, B> ta, tb;
+  if constexpr (DEPTH == 2) {
+    KvTile8<D, B> ta, tb;
+    for (int c0 = 0; c0 < ntiles; c0 += kChunkTiles) {
+      const int c1 = min(ntiles, c0 + kChunkTiles);
+      chunk_lb = (tok_begin + 32 * c0) / B;
+      my_id = bt[min(chunk_lb + lane, nblk - 1)];
+      load_tile(ta, c0);
+      int t = c0;
+      for (; t + 2 < c1; t += 2) {
+        load_tile(tb, t + 1);
+        compute(ta, t);
+        load_tile(ta, t + 2);
+        compute(tb, t + 1);
+      }
+      if (t + 1 < c1) {
+        load_tile(tb, t + 1);
+        compute(ta, t);
+        compute(tb, t + 1);
+      } else {
+        compute(ta, t);
+      }
+    }
+    return;
+  }
+  KvTile8<D, B> t0, t1, t2;
   for (int c0 = 0; c0 < ntiles; c0 += kChunkTiles) {
     const int c1 = min(ntiles, c0 + kChunkTiles);
     chunk_lb = (tok_begin + 32 * c0) / B;
     my_id = bt[min(chunk_lb + lane, nblk - 1)];
-    load_tile(ta, c0);
+    load_tile(t0, c0);
+    if (c0 + 1 < c1) load_tile(t1, c0 + 1);
     int t = c0;
-    for (; t + 2 < c1; t += 2) {
-      load_tile(tb, t + 1);
-      compute(ta, t);
-      load_tile(ta, t + 2);
-      compute(tb, t + 1);
+    for (; t + 4 < c1; t += 3) {  // on entry t0 and t1 hold tiles t and t+1
+      load_tile(t2, t + 2);
+      compute(t0, t);
+      load_tile(t0, t + 3);
+      compute(t1, t + 1);
+      load_tile(t1, t + 4);
+      compute(t2, t + 2);
     }
-    if (t + 1 < c1) {
-      load_tile(tb, t + 1);
-      compute(ta, t);
-      compute(tb, t + 1);
-    } else {
-      compute(ta, t);
-    }
+    const int rem = c1 - t;  // 1 .. 4 tiles left
+    if (rem >= 3) load_tile(t2, t + 2);
+    compute(t0, t);
+    if (rem == 4) load_tile(t0, t + 3);
+    if (rem >= 2) compute(t1, t + 1);
+    if (rem >= 3) compute(t2, t + 2);
+    if (rem == 4) compute(t0, t + 3);
   }
 }
 
@@ -646,7 +677,9 @@ __device__ __forceinline__ void balanced_body(
     const int te = min(pre + 32 * t_end, n);
     if constexpr (kFp8) {
       load_q_fp8<D>(qf, q + row * D, hvalid, lg);
-      attend_tiles_fp8<D, B>(st, qf, kpool, vpool, bt, n, g, Hkv, tb, te, scale_log2);
+      // the prefix kernel is held to 256 VGPRs: two register sets there
+      attend_tiles_fp8<D, B, PREFIX ? 2 : 3>(st, qf, kpool, vpool, bt, n, g, Hkv, tb, te,
+                                            scale_log2);
     } else if constexpr (STEP) {
       load_q<D>(qf, q + row * D, hvalid, lg);
       const int slot = sp.slots[s];
@@ -764,7 +797,7 @@ __device__ __forceinline__ void prefix_unit(
   const int te = min(pre, tok0 + kPrefixChunk);
   if constexpr (kFp8) {
     load_q_fp8<D>(qf, q + row * D, valid, lg);
-    attend_tiles_fp8<D, B>(st, qf, kpool, vpool, bt, pre, g, Hkv, tok0, te, scale_log2);
+    attend_tiles_fp8<D, B, 2>(st, qf, kpool, vpool, bt, pre, g, Hkv, tok0, te, scale_log2);
   } else {
     load_q<D>(qf, q + row * D, valid, lg);
     attend_tiles<D, B>(st, qf, kpool, vpool, bt, pre, g, Hkv, tok0, te, scale_log2);
