@@ -234,6 +234,8 @@ int pkv_kv_cache_write(const void* k_new, const void* v_new, void* k_pool, void*
   if (block_size != 16 && block_size != 32)
     return fail(PKV_ERR_UNSUPPORTED, "block_size %d not in {16, 32}", block_size);
   if (!supported_dtype(dtype)) return fail(PKV_ERR_UNSUPPORTED, "dtype %d not supported", dtype);
+  if (num_kv_heads > kMaxGridYZ)
+    return fail(PKV_ERR_UNSUPPORTED, "num_kv_heads %d too large", num_kv_heads);
   if (static_cast<long long>(num_blocks) * block_size > 0x7fffffffLL)
     return fail(PKV_ERR_UNSUPPORTED, "pool of %d blocks exceeds int32 slot numbers", num_blocks);
   pkv::KvWriteArgs a{k_new, v_new, k_pool, v_pool, slot_mapping, T, num_kv_heads, head_dim,
@@ -259,6 +261,8 @@ int pkv_kv_cache_write_fp8(const void* k_new, const void* v_new, void* k_pool, v
     return fail(PKV_ERR_UNSUPPORTED, "in_dtype %d not supported", in_dtype);
   if (!valid_pool_scale(k_scale) || !valid_pool_scale(v_scale))
     return fail(PKV_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
+  if (num_kv_heads > kMaxGridYZ)
+    return fail(PKV_ERR_UNSUPPORTED, "num_kv_heads %d too large", num_kv_heads);
   if (static_cast<long long>(num_blocks) * block_size > 0x7fffffffLL)
     return fail(PKV_ERR_UNSUPPORTED, "pool of %d blocks exceeds int32 slot numbers", num_blocks);
   pkv::KvWriteArgs a{k_new, v_new, k_pool, v_pool, slot_mapping, T, num_kv_heads, head_dim,

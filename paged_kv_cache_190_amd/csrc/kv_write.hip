@@ -10,40 +10,43 @@
 //
 // Layout: k_pool [NB][Hkv][B][D] (a token's row is D contiguous elements),
 //         v_pool [NB][Hkv][D][B] (a token's values are B elements apart).
-// One workgroup per token; a thread copies 16 contiguous bytes of one head's row.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace pkv {
 
+// Work split (both kernels): a workgroup takes 16 consecutive tokens of one KV head; thread
+// (token tt = tid % 16, chunk c = tid / 16) moves one 16-byte piece of the token's row. The token
+// is the fastest lane index, so when consecutive tokens go to consecutive slots of a block (a
+// prefill chunk) each V dimension's values of the 16 tokens form one contiguous run in the
+// dim-major V tile, and the stores of a wave coalesce. Any slot mapping is still handled.
+constexpr int kWriteGroup = 16;
+
 template <typename T>
-__global__ __launch_bounds__(256) void kv_write_kernel(const T* __restrict__ k_new,
+__global__ __launch_bounds__(512) void kv_write_kernel(const T* __restrict__ k_new,
                                                        const T* __restrict__ v_new,
                                                        T* __restrict__ k_pool,
                                                        T* __restrict__ v_pool,
                                                        const int32_t* __restrict__ slot_mapping,
-                                                       int Hkv, int D, int B) {
+                                                       int T_tokens, int Hkv, int D, int B) {
   constexpr int VEC = 16 / sizeof(T);
-  const int i = blockIdx.x;
+  const int i = blockIdx.x * kWriteGroup + (threadIdx.x % kWriteGroup);
+  const int d0 = (threadIdx.x / kWriteGroup) * VEC;
+  const int h = blockIdx.y;
+  if (i >= T_tokens || d0 >= D) return;
   const int slot = slot_mapping[i];
   if (slot < 0) return;
   const int64_t blk = slot / B;
   const int off = slot - static_cast<int>(blk) * B;
-  const int chunks = Hkv * (D / VEC);
-  for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
-    const int h = c / (D / VEC);
-    const int d0 = (c - h * (D / VEC)) * VEC;
-    const int64_t src = (static_cast<int64_t>(i) * Hkv + h) * D + d0;
-    const u32x4 kv = load16(k_new + src);
-    const u32x4 vv = load16(v_new + src);
-    const int64_t tile = blk * Hkv + h;
-    *reinterpret_cast<u32x4*>(k_pool + (tile * B + off) * D + d0) = kv;
-    T vals[VEC];
-    __builtin_memcpy(vals, &vv, 16);
-    T* vdst = v_pool + (tile * D + d0) * B + off;
+  const int64_t src = (static_cast<int64_t>(i) * Hkv + h) * D + d0;
+  const int64_t tile = blk * Hkv + h;
+  *reinterpret_cast<u32x4*>(k_pool + (tile * B + off) * D + d0) = load16(k_new + src);
+  const u32x4 vv = load16(v_new + src);
+  T vals[VEC];
+  __builtin_memcpy(vals, &vv, 16);
+  T* vdst = v_pool + (tile * D + d0) * B + off;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) vdst[static_cast<int64_t>(e) * B] = vals[e];
-  }
+  for (int e = 0; e < VEC; ++e) vdst[static_cast<int64_t>(e) * B] = vals[e];
 }
 
 // E4M3 code of a float32: the nearest representable value, ties to the even code; magnitudes
@@ -88,56 +91,51 @@ __device__ __forceinline__ void load_row16(const In* p, float (&x)[16]) {
   }
 }
 
-// One workgroup per token; a thread quantises 16 consecutive elements of one head's row: K
-// leaves as one 16-byte store, V as 16 single bytes B apart.
+// Same work split as kv_write_kernel; a thread quantises 16 consecutive elements of one head's
+// row: K leaves as one 16-byte store, V as 16 single bytes, one per dimension.
 template <typename In>
-__global__ __launch_bounds__(256) void kv_write_fp8_kernel(const In* __restrict__ k_new,
-                                                           const In* __restrict__ v_new,
-                                                           uint8_t* __restrict__ k_pool,
-                                                           uint8_t* __restrict__ v_pool,
-                                                           const int32_t* __restrict__ slot_mapping,
-                                                           int Hkv, int D, int B, float k_scale,
-                                                           float v_scale) {
-  const int i = blockIdx.x;
+__global__ __launch_bounds__(512) void kv_write_fp8_kernel(
+    const In* __restrict__ k_new, const In* __restrict__ v_new, uint8_t* __restrict__ k_pool,
+    uint8_t* __restrict__ v_pool, const int32_t* __restrict__ slot_mapping, int T_tokens, int Hkv,
+    int D, int B, float k_scale, float v_scale) {
+  const int i = blockIdx.x * kWriteGroup + (threadIdx.x % kWriteGroup);
+  const int d0 = (threadIdx.x / kWriteGroup) * 16;
+  const int h = blockIdx.y;
+  if (i >= T_tokens || d0 >= D) return;
   const int slot = slot_mapping[i];
   if (slot < 0) return;
   const int64_t blk = slot / B;
   const int off = slot - static_cast<int>(blk) * B;
-  const int chunks = Hkv * (D / 16);
-  for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
-    const int h = c / (D / 16);
-    const int d0 = (c - h * (D / 16)) * 16;
-    const int64_t src = (static_cast<int64_t>(i) * Hkv + h) * D + d0;
-    const int64_t tile = blk * Hkv + h;
-    float x[16];
-    load_row16(k_new + src, x);
-    u32x4 kw = {0u, 0u, 0u, 0u};
+  const int64_t src = (static_cast<int64_t>(i) * Hkv + h) * D + d0;
+  const int64_t tile = blk * Hkv + h;
+  float x[16];
+  load_row16(k_new + src, x);
+  u32x4 kw = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int e = 0; e < 16; ++e) kw[e / 4] |= e4m3_code(x[e] / k_scale) << (8 * (e % 4));
-    *reinterpret_cast<u32x4*>(k_pool + (tile * B + off) * D + d0) = kw;
-    load_row16(v_new + src, x);
-    uint8_t* vdst = v_pool + (tile * D + d0) * B + off;
+  for (int e = 0; e < 16; ++e) kw[e / 4] |= e4m3_code(x[e] / k_scale) << (8 * (e % 4));
+  *reinterpret_cast<u32x4*>(k_pool + (tile * B + off) * D + d0) = kw;
+  load_row16(v_new + src, x);
+  uint8_t* vdst = v_pool + (tile * D + d0) * B + off;
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-      vdst[static_cast<int64_t>(e) * B] = static_cast<uint8_t>(e4m3_code(x[e] / v_scale));
-  }
+  for (int e = 0; e < 16; ++e)
+    vdst[static_cast<int64_t>(e) * B] = static_cast<uint8_t>(e4m3_code(x[e] / v_scale));
 }
 
 hipError_t launch_kv_write_fp8(const KvWriteArgs& a, int in_bf16, float k_scale, float v_scale,
                                hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
-  const int chunks = a.Hkv * (a.D / 16);
-  const int threads = chunks >= 256 ? 256 : ((chunks + 63) / 64) * 64;
+  const dim3 grid((a.T + kWriteGroup - 1) / kWriteGroup, a.Hkv);
+  const dim3 block(kWriteGroup * (a.D / 16));
   if (in_bf16) {
-    (void)launch_kernel(K_KV_WRITE, kv_write_fp8_kernel<uint16_t>, dim3(a.T), dim3(threads),
-        stream, static_cast<const uint16_t*>(a.k_new), static_cast<const uint16_t*>(a.v_new),
-        static_cast<uint8_t*>(a.k_pool), static_cast<uint8_t*>(a.v_pool), a.slot_mapping, a.Hkv,
-        a.D, a.B, k_scale, v_scale);
+    (void)launch_kernel(K_KV_WRITE, kv_write_fp8_kernel<uint16_t>, grid, block, stream,
+        static_cast<const uint16_t*>(a.k_new), static_cast<const uint16_t*>(a.v_new),
+        static_cast<uint8_t*>(a.k_pool), static_cast<uint8_t*>(a.v_pool), a.slot_mapping, a.T,
+        a.Hkv, a.D, a.B, k_scale, v_scale);
   } else {
-    (void)launch_kernel(K_KV_WRITE, kv_write_fp8_kernel<float>, dim3(a.T), dim3(threads),
-        stream, static_cast<const float*>(a.k_new), static_cast<const float*>(a.v_new),
-        static_cast<uint8_t*>(a.k_pool), static_cast<uint8_t*>(a.v_pool), a.slot_mapping, a.Hkv,
-        a.D, a.B, k_scale, v_scale);
+    (void)launch_kernel(K_KV_WRITE, kv_write_fp8_kernel<float>, grid, block, stream,
+        static_cast<const float*>(a.k_new), static_cast<const float*>(a.v_new),
+        static_cast<uint8_t*>(a.k_pool), static_cast<uint8_t*>(a.v_pool), a.slot_mapping, a.T,
+        a.Hkv, a.D, a.B, k_scale, v_scale);
   }
   return hipGetLastError();
 }
@@ -145,21 +143,20 @@ hipError_t launch_kv_write_fp8(const KvWriteArgs& a, int in_bf16, float k_scale,
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
   const int vec = 16 / a.elem_bytes;
-  const int chunks = a.Hkv * (a.D / vec);
-  const int threads = chunks >= 256 ? 256 : ((chunks + 63) / 64) * 64;
+  const dim3 grid((a.T + kWriteGroup - 1) / kWriteGroup, a.Hkv);
+  const dim3 block(kWriteGroup * (a.D / vec));
   if (a.elem_bytes == 2) {
-    (void)launch_kernel(K_KV_WRITE, kv_write_kernel<uint16_t>, dim3(a.T), dim3(threads), stream,
+    (void)launch_kernel(K_KV_WRITE, kv_write_kernel<uint16_t>, grid, block, stream,
         static_cast<const uint16_t*>(a.k_new), static_cast<const uint16_t*>(a.v_new),
-        static_cast<uint16_t*>(a.k_pool), static_cast<uint16_t*>(a.v_pool), a.slot_mapping, a.Hkv,
-        a.D, a.B);
+        static_cast<uint16_t*>(a.k_pool), static_cast<uint16_t*>(a.v_pool), a.slot_mapping, a.T,
+        a.Hkv, a.D, a.B);
   } else {
-    (void)launch_kernel(K_KV_WRITE, kv_write_kernel<float>, dim3(a.T), dim3(threads), stream,
+    (void)launch_kernel(K_KV_WRITE, kv_write_kernel<float>, grid, block, stream,
         static_cast<const float*>(a.k_new), static_cast<const float*>(a.v_new),
-        static_cast<float*>(a.k_pool), static_cast<float*>(a.v_pool), a.slot_mapping, a.Hkv, a.D,
-        a.B);
+        static_cast<float*>(a.k_pool), static_cast<float*>(a.v_pool), a.slot_mapping, a.T, a.Hkv,
+        a.D, a.B);
   }
-  hipError_t e = hipGetLastError();
-  return e;
+  return hipGetLastError();
 }
 
 }  // namespace pkv
