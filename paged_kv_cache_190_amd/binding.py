@@ -132,6 +132,19 @@ def _pool_code(t) -> int:
     return PKV_FP8_E4M3 if _is_fp8_pool(t) else _dtype_code(t)
 
 
+def _same_dtype(what: str, *ts) -> None:
+    """The kernels take element types from one argument; a tensor of another type would be
+    read with the wrong element size, so a mismatch is refused here."""
+    if any(t.dtype != ts[0].dtype for t in ts):
+        raise TypeError(f"{what} must share one dtype (got {[str(t.dtype) for t in ts]})")
+
+
+def _bf16(what: str, *ts) -> None:
+    import torch
+    if any(t.dtype != torch.bfloat16 for t in ts):
+        raise TypeError(f"{what} must be bfloat16")
+
+
 def _dev(t, name: str):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
@@ -194,6 +207,7 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_table, context_lens, sc
         raise ValueError("inconsistent shapes")
     if block_table.dim() != 2 or block_table.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("block_table must be [S][MB], context_lens [S]")
+    _same_dtype("q, k_pool and v_pool", q, k_pool, v_pool)
     mb = block_table.shape[1]
     ctx = max_context_len if max_context_len else mb * b
     need = decode_workspace_size(S, hq, hkv, d, ctx, partition_size, _dtype_code(q))
@@ -273,6 +287,7 @@ def paged_attention_decode_fp8(out, q, k_pool, v_pool, block_table, context_lens
         raise ValueError("inconsistent shapes")
     if not (_is_fp8_pool(k_pool) and _is_fp8_pool(v_pool)):
         raise TypeError("pools must be E4M3 (uint8)")
+    _bf16("q", q)
     if block_table.dim() != 2 or block_table.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("block_table must be [S][MB], context_lens [S]")
     mb = block_table.shape[1]
@@ -311,6 +326,10 @@ def paged_attention_decode_shared_prefix(out, q, k_pool, v_pool, block_table, co
         raise ValueError("inconsistent shapes")
     if block_table.dim() != 2 or block_table.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("block_table must be [S][MB], context_lens [S]")
+    _bf16("q", q)
+    _same_dtype("k_pool and v_pool", k_pool, v_pool)
+    if not (_is_fp8_pool(k_pool) or k_pool.dtype == torch.bfloat16):
+        raise TypeError("pools must be bfloat16 or E4M3 (uint8)")
     ng = group_prefix_len.shape[0]
     if group_start.shape != (ng + 1,):
         raise ValueError("group_start must be [num_groups + 1]")
@@ -342,6 +361,7 @@ def paged_attention_prefill_chunk(out, q, cu_q_lens, context_lens, k_pool, v_poo
         raise ValueError("inconsistent shapes")
     if cu_q_lens.shape != (S + 1,) or block_table.dim() != 2 or block_table.shape[0] != S:
         raise ValueError("cu_q_lens must be [S+1], block_table [S][MB]")
+    _same_dtype("q, k_pool and v_pool", q, k_pool, v_pool)
     _check(lib().pkv_paged_attention_prefill_chunk(
         _dev(out, "out"), _dev(q, "q"), _i32(cu_q_lens, "cu_q_lens"),
         _i32(context_lens, "context_lens"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),

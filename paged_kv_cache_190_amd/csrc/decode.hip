@@ -28,7 +28,10 @@
 // differently: lane group lg holds the D/4 consecutive dimensions lg*D/4 .. (lg+1)*D/4-1 of its
 // token row (one 16-byte load per 16 dimensions), and the query operand uses the same
 // assignment. The pool scales are folded in: k_scale into the score scale, v_scale into the
-// final normalisation.
+// final normalisation. The tile loop keeps three register sets (two tiles in flight).
+//
+// Also here: the prefix-aware decode for batches that share prompt prefixes (see PrefixInfo),
+// the write folded into the decode (see StepInfo), and the reduce kernel.
 //
 // fp32 path (vector ALUs): one wave owns (sequence, query head, partition); lanes take one token
 // each for the scores, then one output dimension each for P.V.

@@ -236,3 +236,36 @@ def test_profile_registry_host_side():
     with pytest.raises(bd.PkvError):
         bd.profile_read("no_such_kernel")
     assert L.pkv_profile_enable(0) == bd.PKV_OK
+
+
+def test_binding_refuses_mismatched_dtypes():
+    """Element types come from one argument; the binding refuses mixed types before any device
+    work (host tensors suffice to reach the check)."""
+    import torch
+    S, hq, hkv, d, b, nb = 2, 4, 2, 64, 16, 4
+    q = torch.zeros(S, hq, d, dtype=torch.bfloat16)
+    kb = torch.zeros(nb, hkv, b, d, dtype=torch.bfloat16)
+    vb = torch.zeros(nb, hkv, d, b, dtype=torch.bfloat16)
+    k8 = torch.zeros(nb, hkv, b, d, dtype=torch.uint8)
+    v8 = torch.zeros(nb, hkv, d, b, dtype=torch.uint8)
+    bt = torch.zeros(S, 2, dtype=torch.int32)
+    ctx = torch.zeros(S, dtype=torch.int32)
+    out = torch.zeros(S, hq, d, dtype=torch.float32)
+    with pytest.raises(TypeError):
+        bd.paged_attention_decode(out, q, k8, v8, bt, ctx, 0.1)
+    with pytest.raises(TypeError):
+        bd.paged_attention_decode(out, q.float(), kb, vb, bt, ctx, 0.1)
+    with pytest.raises(TypeError):
+        bd.paged_attention_decode_fp8(out, q.float(), k8, v8, bt, ctx, 0.1, 1.0, 1.0)
+    with pytest.raises(TypeError):
+        bd.paged_attention_decode_fp8(out, q, kb, vb, bt, ctx, 0.1, 1.0, 1.0)
+    gs = torch.tensor([0, S], dtype=torch.int32)
+    gp = torch.tensor([0], dtype=torch.int32)
+    with pytest.raises(TypeError):
+        bd.paged_attention_decode_shared_prefix(out, q, kb, v8, bt, ctx, gs, gp, 0.1, S, 0)
+    with pytest.raises(TypeError):
+        bd.paged_attention_decode_shared_prefix(out, q, kb.float(), vb.float(), bt, ctx, gs, gp,
+                                                0.1, S, 0)
+    cu = torch.tensor([0, 1, 2], dtype=torch.int32)
+    with pytest.raises(TypeError):
+        bd.paged_attention_prefill_chunk(out, q, cu, ctx, k8, v8, bt, 0.1)
