@@ -58,6 +58,35 @@ __device__ __forceinline__ int kswz(int row) {
 __device__ __forceinline__ int vswz(int d) { return (d >> 2) & 3; }  // 4 chunks, 4 rows per line
 
 constexpr int kPrefillWaves = 8;  // waves per workgroup
+constexpr int kRankMax = 64;       // largest batch whose sequences are ranked by work
+
+// The sequence of rank j when sequences are ordered by decreasing c * (2n - c) (chunk length c,
+// context length n), ties by index; j itself when the batch has more than RMAX sequences.
+// Block-wide (every thread calls it, two barriers); scratch: 8 * RMAX + 4 bytes of LDS.
+template <int NT, int RMAX>
+__device__ __forceinline__ int seq_by_rank(int j, int S, const int32_t* __restrict__ cu_q_lens,
+                                           const int32_t* __restrict__ context_lens,
+                                           unsigned char* lds, int tid) {
+  if (S > RMAX) return j;
+  int64_t* key = reinterpret_cast<int64_t*>(lds);
+  int* found = reinterpret_cast<int*>(lds + 8 * RMAX);
+  for (int i = tid; i < S; i += NT) {
+    const int64_t c = cu_q_lens[i + 1] - cu_q_lens[i];
+    key[i] = c * (2 * static_cast<int64_t>(context_lens[i]) - c);
+  }
+  __syncthreads();
+  for (int i = tid; i < S; i += NT) {
+    const int64_t ki = key[i];
+    int rank = 0;
+    for (int o = 0; o < S; ++o) {
+      const int64_t ko = key[o];
+      rank += (ko > ki || (ko == ki && o < i)) ? 1 : 0;
+    }
+    if (rank == j) *found = i;  // exactly one sequence has rank j
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(*found);
+}
 
 template <int D, int B, typename OutT>
 __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
@@ -78,6 +107,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
   constexpr int KC = K_BYTES / 1024;     // 1 KiB DMA instructions for K (V follows at KC)
   constexpr int LPT = STAGE / 1024 / NW; // DMA instructions per wave (and per thread) per tile
   static_assert(LPT >= 1 && (STAGE / 1024) % NW == 0, "DMA work must split evenly over waves");
+  static_assert(NS * STAGE >= 8 * kRankMax + 4, "the ranking scratch must fit the stages");
   constexpr int kIdCap = 2048;           // block ids staged in LDS at a time
   // One LDS object holds the stages and, after them, the block-id window.
   __shared__ __attribute__((aligned(16))) unsigned char smem[NS * STAGE + 4 * kIdCap];
@@ -101,11 +131,17 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
   }
   const int tile = n_tiles - 1 - tix;
   const int gy = pair % gridDim.y;
-  const int s = pair / gridDim.y;
+  const int tid = threadIdx.x;
+  // pair / gridDim.y is a rank: sequences are taken in order of decreasing work (estimated as
+  // c * (2n - c), which grows with the chunk's visible (row, key) pairs), so that the longest
+  // jobs start first and the short ones fill in behind them. Every workgroup ranks the batch
+  // itself, in the LDS that the tile stages use later (up to kRankMax sequences; past that,
+  // batch order).
+  const int s = seq_by_rank<NT, kRankMax>(pair / gridDim.y, gridDim.z, cu_q_lens, context_lens,
+                                          smem, tid);
 
   const int g = gy / n_groups;
   const int grp = gy - g * n_groups;
-  const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
   const int lane = tid & 63;
   const int col = lane & 31;
@@ -158,6 +194,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
 #pragma unroll
     for (int j = 0; j < kIdCap / NT; ++j)
       if (tid + NT * j < cnt) ids[tid + NT * j] = v[j];
+    // Every load above has landed on every path out of here; otherwise the compiler carries
+    // them as pending into the tile loop and drains all DMAs when it next reuses a register.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   };
   load_window(0);
   // q and the first ids must have arrived before the tile DMAs start counting in the same

@@ -251,6 +251,12 @@ PREFILL_CASES = [
     ("f32", 206, 2, 4, 2, 64, 16, [20, 0], [5, 17], "f32"),
     ("f32_d128_b32", 207, 2, 8, 2, 128, 32, [40, 3], [9, 33], "f32"),
     ("g3_long_chunks", 208, 2, 6, 2, 128, 16, [100, 0], [300, 257], "bf16"),
+    # workgroups take sequences in order of decreasing work: equal keys (ties) and an empty
+    # chunk among them
+    ("ranked_ties", 209, 5, 8, 2, 128, 16, [40, 40, 7, 40, 3], [20, 20, 60, 20, 0], "bf16"),
+    # more sequences than the kernel ranks (64): batch order
+    ("past_rank_limit", 210, 70, 4, 2, 64, 16, [(7 * i) % 50 for i in range(70)],
+     [1 + i % 5 for i in range(70)], "bf16"),
 ]
 
 
