@@ -74,6 +74,7 @@ __device__ __forceinline__ int seq_by_rank(int j, int S, const int32_t* __restri
     const int64_t c = cu_q_lens[i + 1] - cu_q_lens[i];
     key[i] = c * (2 * static_cast<int64_t>(context_lens[i]) - c);
   }
+  if (tid == 0) *found = j;  // overwritten below; keeps the result in range whatever happens
   __syncthreads();
   for (int i = tid; i < S; i += NT) {
     const int64_t ki = key[i];
