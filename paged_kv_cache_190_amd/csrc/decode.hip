@@ -18,8 +18,9 @@
 // rows) is also the B-operand layout the second product needs, so P never leaves registers. For
 // that to line up, the tile's tokens are assigned to MFMA rows so that the lane in row group lg
 // ends up holding tokens 8*lg .. 8*lg+7: then its V^T operand is 16 contiguous bytes of the
-// dim-major V tile. Heads beyond G in the 16-wide column are zero queries whose results are
-// dropped; the kernel is bound by HBM reads of K and V, so the padded MFMA work is free.
+// dim-major V tile. Heads beyond G in the 16-wide column are zero queries: their lanes skip the
+// softmax and feed P = 0, and their results are dropped; the kernel is bound by HBM reads of K
+// and V, so the padded MFMA work costs no time.
 // K and V of the next tile are loaded while the current tile is computed (two register sets).
 //
 // E4M3 pools (same waves, same tiles): every E4M3 value is exactly a bf16 value, so each lane
@@ -80,7 +81,8 @@ __device__ __forceinline__ void load_q(u32x4 (&qf)[D / 32], const uint16_t* qrow
 template <int D>
 __device__ __forceinline__ void tile_update(WaveAttn<D>& st, const u32x4 (&k)[2][D / 32],
                                             u32x4 (&v)[D / 16], const u32x4 (&qf)[D / 32],
-                                            int lim, int vlim, float scale_log2, int lg) {
+                                            int lim, int vlim, float scale_log2, int lg,
+                                            bool col_used = true) {
   constexpr int KK = D / 32;
   constexpr int DT = D / 16;
   f32x4 sc[2];
@@ -90,34 +92,37 @@ __device__ __forceinline__ void tile_update(WaveAttn<D>& st, const u32x4 (&k)[2]
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) sc[hf] = mfma16x16x32(k[hf][kk], qf[kk], sc[hf]);
   }
-  // lane: head column r16, tile tokens 8*lg + 4*hf + e
-  float x[8];
+  // lane: head column r16, tile tokens 8*lg + 4*hf + e. Padding columns (no query head) skip
+  // the softmax and give P = 0; all four lanes of a column agree on col_used.
+  u32x4 pb = {0u, 0u, 0u, 0u};
+  if (col_used) {
+    float x[8];
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf)
+    for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int tt = 8 * lg + 4 * hf + e;
-      x[4 * hf + e] = (tt < lim) ? sc[hf][e] * scale_log2 : -INFINITY;
+      for (int e = 0; e < 4; ++e) {
+        const int tt = 8 * lg + 4 * hf + e;
+        x[4 * hf + e] = (tt < lim) ? sc[hf][e] * scale_log2 : -INFINITY;
+      }
+    float tmax = x[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
+    tmax = xor32_max(xor16_max(tmax));
+    const float mnew = fmaxf(st.m, tmax);
+    const float alpha = fast_exp2(st.m - mnew);
+    st.m = mnew;
+    float psum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float p0 = fast_exp2(x[2 * w] - mnew);
+      const float p1 = fast_exp2(x[2 * w + 1] - mnew);
+      psum += p0 + p1;
+      pb[w] = pack_bf16x2(p0, p1);
     }
-  float tmax = x[0];
+    st.l = st.l * alpha + psum;
 #pragma unroll
-  for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
-  tmax = xor32_max(xor16_max(tmax));
-  const float mnew = fmaxf(st.m, tmax);
-  const float alpha = fast_exp2(st.m - mnew);
-  st.m = mnew;
-  float psum = 0.f;
-  u32x4 pb;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const float p0 = fast_exp2(x[2 * w] - mnew);
-    const float p1 = fast_exp2(x[2 * w + 1] - mnew);
-    psum += p0 + p1;
-    pb[w] = pack_bf16x2(p0, p1);
+    for (int dt = 0; dt < DT; ++dt) st.acc[dt] *= alpha;
   }
-  st.l = st.l * alpha + psum;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) st.acc[dt] *= alpha;
   if (vlim < 32) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -163,7 +168,7 @@ __device__ __forceinline__ void attend_tiles(WaveAttn<D>& st, const u32x4 (&qf)[
                                              const uint16_t* __restrict__ vpool,
                                              const int32_t* __restrict__ bt, int n, int g,
                                              int Hkv, int tok_begin, int tok_end,
-                                             float scale_log2) {
+                                             float scale_log2, bool col_used = true) {
   constexpr int KK = D / 32;
   constexpr int DT = D / 16;
   constexpr int TILE = B * D;  // elements of one (block, head) tile
@@ -213,7 +218,7 @@ __device__ __forceinline__ void attend_tiles(WaveAttn<D>& st, const u32x4 (&qf)[
 
   auto compute = [&](KvTile<D, B>& T, int t) {
     const int tok0 = tok_begin + 32 * t;
-    tile_update<D>(st, T.k, T.v, qf, tok_end - tok0, n - tok0, scale_log2, lg);
+    tile_update<D>(st, T.k, T.v, qf, tok_end - tok0, n - tok0, scale_log2, lg, col_used);
   };
 
   // Software pipeline: every compute of tile t runs while the loads of tile t+1 are in
@@ -595,7 +600,7 @@ __device__ __forceinline__ void balanced_body(
     float out_scale, PrefixInfo pf, StepInfo sp = StepInfo{}) {
   constexpr bool kFp8 = sizeof(KvT) == 1;
   static_assert(!STEP || (!PREFIX && !kFp8), "the fused step is built for plain bf16 decode");
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int lg = lane >> 4;
   const int segs = Hkv * HG;
   // tiles of one segment of sequence s, and where they start
@@ -703,7 +708,7 @@ __device__ __forceinline__ void balanced_body(
       }
     } else {
       load_q<D>(qf, q + row * D, hvalid, lg);
-      attend_tiles<D, B>(st, qf, kpool, vpool, bt, n, g, Hkv, tb, te, scale_log2);
+      attend_tiles<D, B>(st, qf, kpool, vpool, bt, n, g, Hkv, tb, te, scale_log2, hvalid);
     }
     const float l_total = xor32_sum(xor16_sum(st.l));
     const int64_t wf = wave_of(a);
@@ -732,15 +737,20 @@ __device__ __forceinline__ void balanced_body(
 }
 
 // KvT: uint16_t for bf16 pools, uint8_t for E4M3 pools (out_scale = the V scale).
+// Four waves per workgroup (one per SIMD of a compute unit): a quarter of the workgroup
+// dispatches of one wave per workgroup, so the grid is in place sooner.
+constexpr int kBalancedWavesPerGroup = 4;
 template <int D, int B, typename OutT, typename KvT>
-__global__ __launch_bounds__(64) void decode_balanced_kernel(
+__global__ __launch_bounds__(64 * kBalancedWavesPerGroup) void decode_balanced_kernel(
     OutT* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_m,
     float* __restrict__ part_l, int32_t* __restrict__ seg_count,
     const uint16_t* __restrict__ q, const KvT* __restrict__ kpool,
     const KvT* __restrict__ vpool, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ context_lens, int S, int Hq, int Hkv, int G, int HG, int MB,
     int KMAX, int min_tiles, float scale_log2, float out_scale) {
-  balanced_body<D, B, OutT, KvT, false>(blockIdx.x, gridDim.x, out, part_o, part_m, part_l,
+  balanced_body<D, B, OutT, KvT, false>(
+      blockIdx.x * kBalancedWavesPerGroup + (threadIdx.x >> 6),
+      gridDim.x * kBalancedWavesPerGroup, out, part_o, part_m, part_l,
                                         seg_count, q, kpool, vpool, block_table, context_lens, S,
                                         Hq, Hkv, G, HG, MB, KMAX, min_tiles, scale_log2,
                                         out_scale, PrefixInfo{nullptr, nullptr, 0});
@@ -1038,9 +1048,10 @@ template <int D, int B, typename OutT>
 static void launch_bf16(const DecodeArgs& a, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   const int HG = (G + 15) / 16;
+  const int groups = (a.waves + kBalancedWavesPerGroup - 1) / kBalancedWavesPerGroup;
   if (a.fp8_kv) {
     (void)launch_kernel(K_DECODE_PARTITION, decode_balanced_kernel<D, B, OutT, uint8_t>,
-        dim3(a.waves), dim3(64), st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l,
+        dim3(groups), dim3(64 * kBalancedWavesPerGroup), st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l,
         a.seg_count, static_cast<const uint16_t*>(a.q), static_cast<const uint8_t*>(a.k_pool),
         static_cast<const uint8_t*>(a.v_pool), a.block_table, a.context_lens, a.S, a.Hq, a.Hkv, G,
         HG, a.MB, a.KMAX, a.min_tiles, a.scale * a.k_scale * kLog2e, a.v_scale);
@@ -1048,7 +1059,7 @@ static void launch_bf16(const DecodeArgs& a, hipStream_t st) {
   }
   if (a.balanced) {
     (void)launch_kernel(K_DECODE_PARTITION, decode_balanced_kernel<D, B, OutT, uint16_t>,
-        dim3(a.waves), dim3(64), st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l,
+        dim3(groups), dim3(64 * kBalancedWavesPerGroup), st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l,
         a.seg_count, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
         static_cast<const uint16_t*>(a.v_pool), a.block_table, a.context_lens, a.S, a.Hq, a.Hkv, G,
         HG, a.MB, a.KMAX, a.min_tiles, a.scale * kLog2e, 1.0f);
