@@ -460,7 +460,10 @@ int pkv_paged_attention_decode_shared_prefix(
                 max_prefix_len);
   const int G = num_q_heads / num_kv_heads;
   const int nch = prefix_chunks(max_prefix_len);
-  const long long col_tiles = (static_cast<long long>(max_group_size) * G + 15) / 16;
+  // column units: 16 (sequence, query head) columns each over E4M3 pools, 32 over bf16 pools
+  const int cols_per_unit = kv_dtype == PKV_FP8_E4M3 ? 16 : 32;
+  const long long col_tiles =
+      (static_cast<long long>(max_group_size) * G + cols_per_unit - 1) / cols_per_unit;
   const long long units = static_cast<long long>(num_groups) * num_kv_heads * nch * col_tiles;
   const long long waves_p = (units + 7) / 8 * 8;
   const int default_waves =

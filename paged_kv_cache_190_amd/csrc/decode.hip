@@ -248,6 +248,76 @@ __device__ __forceinline__ void attend_tiles(WaveAttn<D>& st, const u32x4 (&qf)[
   }
 }
 
+// attend_tiles for two 16-column tiles at once (the prefix units): each K/V tile is loaded once
+// and feeds both column tiles' products. Both columns sets see the same tokens.
+template <int D, int B>
+__device__ __forceinline__ void attend_tiles2(WaveAttn<D> (&st)[2],
+                                              const u32x4 (&qf)[2][D / 32],
+                                              const uint16_t* __restrict__ kpool,
+                                              const uint16_t* __restrict__ vpool,
+                                              const int32_t* __restrict__ bt, int n, int g,
+                                              int Hkv, int tok_begin, int tok_end,
+                                              float scale_log2) {
+  constexpr int KK = D / 32;
+  constexpr int DT = D / 16;
+  constexpr int TILE = B * D;
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15;
+  const int lg = lane >> 4;
+  const int ntiles = (tok_end - tok_begin + 31) >> 5;
+  const int nblk = (n + B - 1) / B;
+  int koff[2];
+  int ksel = 0;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int tau = 8 * (r16 >> 2) + 4 * hf + (r16 & 3);
+    koff[hf] = (tau % B) * D + 8 * lg;
+    ksel = tau / B;
+  }
+  const int vsel = (B == 16) ? (lg >> 1) : 0;
+  const int vtok = (B == 16) ? 8 * (lg & 1) : 8 * lg;
+  const int voff = r16 * B + vtok;
+  const int64_t head_off = static_cast<int64_t>(g) * TILE;
+  const int64_t blk_stride = static_cast<int64_t>(Hkv) * TILE;
+  int chunk_lb = 0;
+  int my_id = 0;
+  auto block_id = [&](int lb) -> int {
+    return __builtin_amdgcn_readlane(my_id, min(lb, nblk - 1) - chunk_lb);
+  };
+  auto load_tile = [&](KvTile<D, B>& T, int t) {
+    const int lb0 = (tok_begin + 32 * t) / B;
+    const int id0 = block_id(lb0);
+    const int id1 = (B == 16) ? block_id(lb0 + 1) : id0;
+    const uint16_t* kb = kpool + (ksel ? id1 : id0) * blk_stride + head_off;
+    const uint16_t* vb = vpool + (vsel ? id1 : id0) * blk_stride + head_off;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) T.k[hf][kk] = load16(kb + koff[hf] + 32 * kk);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) T.v[dt] = load16(vb + voff + 16 * dt * B);
+  };
+  auto compute = [&](KvTile<D, B>& T, int t) {
+    const int tok0 = tok_begin + 32 * t;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      tile_update<D>(st[c], T.k, T.v, qf[c], tok_end - tok0, n - tok0, scale_log2, lg);
+  };
+  // One register set (the kernel is held to 256 VGPRs): a tile's loads, mostly L2 hits, are
+  // waited for at once; the suffix wave that shares the SIMD runs meanwhile.
+  constexpr int kChunkTiles = 64 * B / 32;
+  KvTile<D, B> ta;
+  for (int c0 = 0; c0 < ntiles; c0 += kChunkTiles) {
+    const int c1 = min(ntiles, c0 + kChunkTiles);
+    chunk_lb = (tok_begin + 32 * c0) / B;
+    my_id = bt[min(chunk_lb + lane, nblk - 1)];
+    for (int t = c0; t < c1; ++t) {
+      load_tile(ta, t);
+      compute(ta, t);
+    }
+  }
+}
+
 // ----------------------------------------------------------------------------- E4M3 pools
 
 template <int D, int B>
@@ -796,32 +866,43 @@ __device__ __forceinline__ void prefix_unit(
   const int members = pf.group_start[gi + 1] - s0;
   const int pre = pf.group_prefix_len[gi];
   const int tok0 = ch * kPrefixChunk;
-  if (tok0 >= pre || ct * 16 >= members * G) return;
-  const int c = ct * 16 + (lane & 15);
-  const bool valid = c < members * G;
-  const int m = valid ? c / G : 0;
-  const int s = s0 + m;
-  const int h = g * G + (valid ? c - m * G : 0);
-  const int64_t row = static_cast<int64_t>(s) * Hq + h;
-  u32x4 qf[D / 32];
-  WaveAttn<D> st;
-  attn_init(st);
+  constexpr int NCW = kFp8 ? 1 : 2;  // column tiles per unit
+  if (tok0 >= pre || ct * 16 * NCW >= members * G) return;
   const int32_t* bt = block_table + static_cast<int64_t>(s0) * MB;  // the shared blocks
   const int te = min(pre, tok0 + kPrefixChunk);
-  if constexpr (kFp8) {
-    load_q_fp8<D>(qf, q + row * D, valid, lg);
-    attend_tiles_fp8<D, B, 2>(st, qf, kpool, vpool, bt, pre, g, Hkv, tok0, te, scale_log2);
-  } else {
-    load_q<D>(qf, q + row * D, valid, lg);
-    attend_tiles<D, B>(st, qf, kpool, vpool, bt, pre, g, Hkv, tok0, te, scale_log2);
-  }
-  // Each lane's column is its own row: reduce l over the 4 row groups only (lanes l ^ 16, ^ 32).
-  const float l_total = xor32_sum(xor16_sum(st.l));
-  if (!valid) return;
-  const float osc = kFp8 ? out_scale : 1.0f;
   const int pc = (pre + kPrefixChunk - 1) / kPrefixChunk;
-  if (pc == 1 && context_lens[s] == pre) write_final<D>(out + row * D, st, l_total, lg, osc);
-  else write_partial<D>(part_o, part_m, part_l, row * KSTRIDE + ch, st, l_total, lg, osc);
+  const float osc = kFp8 ? out_scale : 1.0f;
+  bool valid[NCW];
+  int seq[NCW];
+  int64_t row[NCW];
+  u32x4 qf[NCW][D / 32];
+  WaveAttn<D> st[NCW];
+#pragma unroll
+  for (int k = 0; k < NCW; ++k) {
+    const int c = (ct * NCW + k) * 16 + (lane & 15);
+    valid[k] = c < members * G;
+    const int m = valid[k] ? c / G : 0;
+    seq[k] = s0 + m;
+    const int h = g * G + (valid[k] ? c - m * G : 0);
+    row[k] = static_cast<int64_t>(seq[k]) * Hq + h;
+    attn_init(st[k]);
+    if constexpr (kFp8) load_q_fp8<D>(qf[k], q + row[k] * D, valid[k], lg);
+    else load_q<D>(qf[k], q + row[k] * D, valid[k], lg);
+  }
+  if constexpr (kFp8)
+    attend_tiles_fp8<D, B, 2>(st[0], qf[0], kpool, vpool, bt, pre, g, Hkv, tok0, te, scale_log2);
+  else
+    attend_tiles2<D, B>(st, qf, kpool, vpool, bt, pre, g, Hkv, tok0, te, scale_log2);
+#pragma unroll
+  for (int k = 0; k < NCW; ++k) {
+    // Each lane's column is its own row: reduce l over the 4 row groups only (lanes ^16, ^32).
+    const float l_total = xor32_sum(xor16_sum(st[k].l));
+    if (!valid[k]) continue;
+    if (pc == 1 && context_lens[seq[k]] == pre)
+      write_final<D>(out + row[k] * D, st[k], l_total, lg, osc);
+    else
+      write_partial<D>(part_o, part_m, part_l, row[k] * KSTRIDE + ch, st[k], l_total, lg, osc);
+  }
 }
 
 // Prefix-aware decode: Wp prefix-unit waves and Ws = gridDim.x - Wp waves of the balanced split
