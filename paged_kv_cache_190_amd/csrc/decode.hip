@@ -762,7 +762,8 @@ __device__ __forceinline__ void balanced_body(
       load_q<D>(qf, q + row * D, hvalid, lg);
       const int slot = sp.slots[s];
       const int np = slot >= 0 ? n - 1 : n;  // tokens read from the pool
-      attend_tiles<D, B>(st, qf, kpool, vpool, bt, np, g, Hkv, tb, min(te, np), scale_log2);
+      attend_tiles<D, B>(st, qf, kpool, vpool, bt, np, g, Hkv, tb, min(te, np), scale_log2,
+                         hvalid);
       if (slot >= 0 && te == n) {
         const int64_t src = (static_cast<int64_t>(s) * Hkv + g) * D;
         attend_one_token<D>(st, qf, sp.k_new + src, sp.v_new + src, scale_log2);
@@ -828,7 +829,7 @@ __global__ __launch_bounds__(64 * kBalancedWavesPerGroup) void decode_balanced_k
 
 // kv_cache_write_and_decode for bf16 pools (see StepInfo).
 template <int D, int B, typename OutT>
-__global__ __launch_bounds__(64) void decode_step_kernel(
+__global__ __launch_bounds__(64 * kBalancedWavesPerGroup) void decode_step_kernel(
     OutT* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_m,
     float* __restrict__ part_l, int32_t* __restrict__ seg_count, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
@@ -837,7 +838,8 @@ __global__ __launch_bounds__(64) void decode_step_kernel(
     const int32_t* __restrict__ context_lens, int S, int Hq, int Hkv, int G, int HG, int MB,
     int KMAX, int min_tiles, float scale_log2) {
   balanced_body<D, B, OutT, uint16_t, false, true>(
-      blockIdx.x, gridDim.x, out, part_o, part_m, part_l, seg_count, q, kpool, vpool,
+      blockIdx.x * kBalancedWavesPerGroup + (threadIdx.x >> 6),
+      gridDim.x * kBalancedWavesPerGroup, out, part_o, part_m, part_l, seg_count, q, kpool, vpool,
       block_table, context_lens, S, Hq, Hkv, G, HG, MB, KMAX, min_tiles, scale_log2, 1.0f,
       PrefixInfo{nullptr, nullptr, 0}, StepInfo{k_new, v_new, slots, kpool, vpool});
 }
@@ -1179,8 +1181,9 @@ template <int D, int B, typename OutT>
 static void launch_step_t(const DecodeArgs& a, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   const int HG = (G + 15) / 16;
-  (void)launch_kernel(K_DECODE_PARTITION, decode_step_kernel<D, B, OutT>, dim3(a.waves),
-      dim3(64), st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l, a.seg_count,
+  (void)launch_kernel(K_DECODE_PARTITION, decode_step_kernel<D, B, OutT>,
+      dim3((a.waves + kBalancedWavesPerGroup - 1) / kBalancedWavesPerGroup),
+      dim3(64 * kBalancedWavesPerGroup), st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l, a.seg_count,
       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_new),
       static_cast<const uint16_t*>(a.v_new), a.slot_mapping,
       static_cast<uint16_t*>(const_cast<void*>(a.k_pool)),
