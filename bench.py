@@ -523,9 +523,9 @@ def cpu_baseline(w, budget_s):
 
 # ------------------------------------------------------------------- rocprofv3 summaries
 
-TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/trace_{w} -o run -- "
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d {d} -o run -- "
              "python3 bench.py --workload {w} --steps 20 --warmup 5 --no-cpu-baseline")
-PMC_CMD = ("rocprofv3 --pmc {c} -f csv -d gpurun_out/pmc_{c}_{w} -o run -- python3 bench.py "
+PMC_CMD = ("rocprofv3 --pmc {c} -f csv -d {d} -o run -- python3 bench.py "
            "--workload {w} --steps 10 --warmup 2 --no-cpu-baseline --calibrate-copy")
 
 
@@ -546,9 +546,16 @@ def _short(name):
     return name.split("(")[0].replace("void ", "").replace("pkv::", "")
 
 
+def _rel(d):
+    """The output directory as the recorded command names it (relative to the repository root
+    when it lies inside it)."""
+    a = os.path.abspath(d)
+    return os.path.relpath(a, ROOT) if a.startswith(ROOT + os.sep) else a
+
+
 def summarize_trace(d, workload):
     rows = _csv(_find(d, "kernel_stats.csv"))
-    cmd = TRACE_CMD.format(w=workload)
+    cmd = TRACE_CMD.format(w=workload, d=_rel(d))
     out = [f"# Kernel durations, workload {workload}", "",
            "rocprofv3 kernel trace of `bench.py` on one MI355X (gfx950).", "",
            f"Command (from the repository root): `{cmd}`", "",
@@ -589,8 +596,8 @@ def summarize_pmc(fetch_dir, write_dir, workload, dominant):
         per.setdefault(k, []).append((fv, wv))
     out = [f"# HBM traffic per dispatch, workload {workload}", "",
            "rocprofv3 counters on one MI355X (gfx950), one run per counter:", "",
-           f"- `{PMC_CMD.format(c='FETCH_SIZE', w=workload)}`",
-           f"- `{PMC_CMD.format(c='WRITE_SIZE', w=workload)}`", "",
+           f"- `{PMC_CMD.format(c='FETCH_SIZE', w=workload, d=_rel(fetch_dir))}`",
+           f"- `{PMC_CMD.format(c='WRITE_SIZE', w=workload, d=_rel(write_dir))}`", "",
            f"Scale: the {len(calib)} calibration copies of {COPY_BYTES >> 20} MiB (device to "
            f"device) read {copy_kib / f_scale:.0f} KiB and write {copy_kib / w_scale:.0f} KiB each "
            f"by these counters, so FETCH_SIZE is multiplied by {f_scale:.4f} and WRITE_SIZE by "
@@ -614,7 +621,7 @@ def summarize_pmc(fetch_dir, write_dir, workload, dominant):
 
 
 MFMA_CMD = ("rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES "
-            "GRBM_GUI_ACTIVE -f csv -d gpurun_out/pmc_mfma_{w} -o run -- python3 bench.py "
+            "GRBM_GUI_ACTIVE -f csv -d {d} -o run -- python3 bench.py "
             "--workload {w} --steps 10 --warmup 2 --no-cpu-baseline")
 
 
@@ -627,7 +634,7 @@ def summarize_mfma(d, workload):
         k = _short(r["Kernel_Name"])
         per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     out = [f"# MFMA utilisation, workload {workload}", "",
-           f"Command (from the repository root): `{MFMA_CMD.format(w=workload)}`", "",
+           f"Command (from the repository root): `{MFMA_CMD.format(w=workload, d=_rel(d))}`", "",
            "| kernel | dispatches | MFMA bf16 MOPs (x512 flops) | busy cycles | GUI active "
            "(sum of 8 XCDs) | MFMA busy % | bf16 flops per dispatch |",
            "|---|---|---|---|---|---|---|"]
