@@ -686,7 +686,7 @@ def main():
     if args.summarize_trace or args.summarize_pmc or args.summarize_mfma:
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
               "(the paged-attention kernels shard by sequence or KV head without any exchange; "
               "multi-GPU runs are out of scope here)", file=sys.stderr)
         sys.exit(2)

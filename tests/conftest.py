@@ -13,6 +13,6 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests fail loudly rather than skip when the HIP library is absent on a GPU box;
+    # GPU tests fail loudly rather than skip when the HIP library is absent on a GPU machine;
     # on a CPU-only machine they are deselected by -m "not gpu".
     pass
