@@ -160,6 +160,74 @@ __device__ __forceinline__ void attend_one_token(WaveAttn<D>& st, const u32x4 (&
   tile_update<D>(st, k, v, qf, 1, 1, scale_log2, lg);
 }
 
+// Walk over the 32-token tiles of one (sequence, KV head) of bf16 pools, starting at token
+// tok_begin (a multiple of B): per-lane operand addresses and the block ids of the chunk being
+// walked. Block ids come one chunk of up to 64 logical blocks at a time: lane i holds the id of
+// block chunk_lb + i (clamped to the last block that holds tokens); tiles read them with
+// readlane, so block addresses stay wave-uniform and the tile loop issues no other vector load.
+template <int D, int B>
+struct TileWalk {
+  static constexpr int KK = D / 32;
+  static constexpr int DT = D / 16;
+  static constexpr int TILE = B * D;  // elements of one (block, head) tile
+  static constexpr int kChunkTiles = 64 * B / 32;  // tiles whose block ids fit one VGPR
+  const uint16_t* kpool;
+  const uint16_t* vpool;
+  int tok_begin;
+  int nblk;
+  int koff[2];
+  int ksel;
+  int vsel;
+  int voff;
+  int64_t head_off;
+  int64_t blk_stride;
+  int chunk_lb = 0;
+  int my_id = 0;
+
+  __device__ __forceinline__ TileWalk(const uint16_t* kp, const uint16_t* vp, int n, int g,
+                                      int Hkv, int tb)
+      : kpool(kp), vpool(vp), tok_begin(tb), nblk((n + B - 1) / B) {
+    const int lane = threadIdx.x & 63;
+    const int r16 = lane & 15;
+    const int lg = lane >> 4;
+    // K operand row r16 of half hf holds tile token 8*(r16/4) + 4*hf + r16%4.
+    ksel = 0;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int tau = 8 * (r16 >> 2) + 4 * hf + (r16 & 3);
+      koff[hf] = (tau % B) * D + 8 * lg;
+      ksel = tau / B;  // same block for both halves
+    }
+    // V^T operand: row d = 16*dt + r16, tokens 8*lg .. 8*lg+7 of the tile.
+    vsel = (B == 16) ? (lg >> 1) : 0;
+    const int vtok = (B == 16) ? 8 * (lg & 1) : 8 * lg;
+    voff = r16 * B + vtok;
+    head_off = static_cast<int64_t>(g) * TILE;
+    blk_stride = static_cast<int64_t>(Hkv) * TILE;
+  }
+  // Load the block ids of the chunk that starts at tile c0.
+  __device__ __forceinline__ void begin_chunk(const int32_t* __restrict__ bt, int c0) {
+    chunk_lb = (tok_begin + 32 * c0) / B;
+    my_id = bt[min(chunk_lb + static_cast<int>(threadIdx.x & 63), nblk - 1)];
+  }
+  __device__ __forceinline__ int block_id(int lb) const {
+    return __builtin_amdgcn_readlane(my_id, min(lb, nblk - 1) - chunk_lb);
+  }
+  __device__ __forceinline__ void load(KvTile<D, B>& T, int t) const {
+    const int lb0 = (tok_begin + 32 * t) / B;
+    const int id0 = block_id(lb0);
+    const int id1 = (B == 16) ? block_id(lb0 + 1) : id0;
+    const uint16_t* kb = kpool + (ksel ? id1 : id0) * blk_stride + head_off;
+    const uint16_t* vb = vpool + (vsel ? id1 : id0) * blk_stride + head_off;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) T.k[hf][kk] = load16(kb + koff[hf] + 32 * kk);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) T.v[dt] = load16(vb + voff + 16 * dt * B);
+  }
+};
+
 // Attend the wave's 16 head columns (KV head g) to tokens [tok_begin, tok_end) of one
 // sequence with n tokens, walking 32-token tiles from tok_begin (a multiple of B).
 template <int D, int B>
@@ -169,53 +237,9 @@ __device__ __forceinline__ void attend_tiles(WaveAttn<D>& st, const u32x4 (&qf)[
                                              const int32_t* __restrict__ bt, int n, int g,
                                              int Hkv, int tok_begin, int tok_end,
                                              float scale_log2, bool col_used = true) {
-  constexpr int KK = D / 32;
-  constexpr int DT = D / 16;
-  constexpr int TILE = B * D;  // elements of one (block, head) tile
-  const int lane = threadIdx.x & 63;
-  const int r16 = lane & 15;
-  const int lg = lane >> 4;
+  const int lg = (threadIdx.x & 63) >> 4;
   const int ntiles = (tok_end - tok_begin + 31) >> 5;
-  const int nblk = (n + B - 1) / B;
-
-  // K operand row r16 of half hf holds tile token 8*(r16/4) + 4*hf + r16%4.
-  int koff[2];
-  int ksel = 0;
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    const int tau = 8 * (r16 >> 2) + 4 * hf + (r16 & 3);
-    koff[hf] = (tau % B) * D + 8 * lg;
-    ksel = tau / B;  // same block for both halves
-  }
-  // V^T operand: row d = 16*dt + r16, tokens 8*lg .. 8*lg+7 of the tile.
-  const int vsel = (B == 16) ? (lg >> 1) : 0;
-  const int vtok = (B == 16) ? 8 * (lg & 1) : 8 * lg;
-  const int voff = r16 * B + vtok;
-  const int64_t head_off = static_cast<int64_t>(g) * TILE;
-  const int64_t blk_stride = static_cast<int64_t>(Hkv) * TILE;
-
-  // Block ids, one chunk of up to 64 logical blocks at a time: lane i holds the id of block
-  // chunk_lb + i (clamped to the last block that holds tokens). Tiles read them with readlane,
-  // so block addresses stay wave-uniform and the tile loop issues no other vector load.
-  int chunk_lb = 0;
-  int my_id = 0;
-  auto block_id = [&](int lb) -> int {
-    return __builtin_amdgcn_readlane(my_id, min(lb, nblk - 1) - chunk_lb);
-  };
-  auto load_tile = [&](KvTile<D, B>& T, int t) {
-    const int lb0 = (tok_begin + 32 * t) / B;
-    const int id0 = block_id(lb0);
-    const int id1 = (B == 16) ? block_id(lb0 + 1) : id0;
-    const uint16_t* kb = kpool + (ksel ? id1 : id0) * blk_stride + head_off;
-    const uint16_t* vb = vpool + (vsel ? id1 : id0) * blk_stride + head_off;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) T.k[hf][kk] = load16(kb + koff[hf] + 32 * kk);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) T.v[dt] = load16(vb + voff + 16 * dt * B);
-  };
-
+  TileWalk<D, B> wk(kpool, vpool, n, g, Hkv, tok_begin);
   auto compute = [&](KvTile<D, B>& T, int t) {
     const int tok0 = tok_begin + 32 * t;
     tile_update<D>(st, T.k, T.v, qf, tok_end - tok0, n - tok0, scale_log2, lg, col_used);
@@ -224,22 +248,20 @@ __device__ __forceinline__ void attend_tiles(WaveAttn<D>& st, const u32x4 (&qf)[
   // Software pipeline: every compute of tile t runs while the loads of tile t+1 are in
   // flight. Inside a chunk the loop body always issues exactly one tile of loads before each
   // compute, so the wait before a compute leaves the next tile's loads outstanding.
-  constexpr int kChunkTiles = 64 * B / 32;  // tiles whose block ids fit one VGPR
   KvTile<D, B> ta, tb;
-  for (int c0 = 0; c0 < ntiles; c0 += kChunkTiles) {
-    const int c1 = min(ntiles, c0 + kChunkTiles);
-    chunk_lb = (tok_begin + 32 * c0) / B;
-    my_id = bt[min(chunk_lb + lane, nblk - 1)];
-    load_tile(ta, c0);
+  for (int c0 = 0; c0 < ntiles; c0 += TileWalk<D, B>::kChunkTiles) {
+    const int c1 = min(ntiles, c0 + TileWalk<D, B>::kChunkTiles);
+    wk.begin_chunk(bt, c0);
+    wk.load(ta, c0);
     int t = c0;
     for (; t + 2 < c1; t += 2) {
-      load_tile(tb, t + 1);
+      wk.load(tb, t + 1);
       compute(ta, t);
-      load_tile(ta, t + 2);
+      wk.load(ta, t + 2);
       compute(tb, t + 1);
     }
     if (t + 1 < c1) {
-      load_tile(tb, t + 1);
+      wk.load(tb, t + 1);
       compute(ta, t);
       compute(tb, t + 1);
     } else {
@@ -249,7 +271,9 @@ __device__ __forceinline__ void attend_tiles(WaveAttn<D>& st, const u32x4 (&qf)[
 }
 
 // attend_tiles for two 16-column tiles at once (the prefix units): each K/V tile is loaded once
-// and feeds both column tiles' products. Both columns sets see the same tokens.
+// and feeds both column tiles' products; both column tiles see the same tokens. One register
+// set (the prefix kernel is held to 256 VGPRs): a tile's loads, mostly L2 hits, are waited for
+// at once, and the suffix wave that shares the SIMD runs meanwhile.
 template <int D, int B>
 __device__ __forceinline__ void attend_tiles2(WaveAttn<D> (&st)[2],
                                               const u32x4 (&qf)[2][D / 32],
@@ -257,63 +281,21 @@ __device__ __forceinline__ void attend_tiles2(WaveAttn<D> (&st)[2],
                                               const uint16_t* __restrict__ vpool,
                                               const int32_t* __restrict__ bt, int n, int g,
                                               int Hkv, int tok_begin, int tok_end,
-                                              float scale_log2) {
-  constexpr int KK = D / 32;
-  constexpr int DT = D / 16;
-  constexpr int TILE = B * D;
-  const int lane = threadIdx.x & 63;
-  const int r16 = lane & 15;
-  const int lg = lane >> 4;
+                                              float scale_log2, const bool (&col_used)[2]) {
+  const int lg = (threadIdx.x & 63) >> 4;
   const int ntiles = (tok_end - tok_begin + 31) >> 5;
-  const int nblk = (n + B - 1) / B;
-  int koff[2];
-  int ksel = 0;
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    const int tau = 8 * (r16 >> 2) + 4 * hf + (r16 & 3);
-    koff[hf] = (tau % B) * D + 8 * lg;
-    ksel = tau / B;
-  }
-  const int vsel = (B == 16) ? (lg >> 1) : 0;
-  const int vtok = (B == 16) ? 8 * (lg & 1) : 8 * lg;
-  const int voff = r16 * B + vtok;
-  const int64_t head_off = static_cast<int64_t>(g) * TILE;
-  const int64_t blk_stride = static_cast<int64_t>(Hkv) * TILE;
-  int chunk_lb = 0;
-  int my_id = 0;
-  auto block_id = [&](int lb) -> int {
-    return __builtin_amdgcn_readlane(my_id, min(lb, nblk - 1) - chunk_lb);
-  };
-  auto load_tile = [&](KvTile<D, B>& T, int t) {
-    const int lb0 = (tok_begin + 32 * t) / B;
-    const int id0 = block_id(lb0);
-    const int id1 = (B == 16) ? block_id(lb0 + 1) : id0;
-    const uint16_t* kb = kpool + (ksel ? id1 : id0) * blk_stride + head_off;
-    const uint16_t* vb = vpool + (vsel ? id1 : id0) * blk_stride + head_off;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) T.k[hf][kk] = load16(kb + koff[hf] + 32 * kk);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) T.v[dt] = load16(vb + voff + 16 * dt * B);
-  };
-  auto compute = [&](KvTile<D, B>& T, int t) {
-    const int tok0 = tok_begin + 32 * t;
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-      tile_update<D>(st[c], T.k, T.v, qf[c], tok_end - tok0, n - tok0, scale_log2, lg);
-  };
-  // One register set (the kernel is held to 256 VGPRs): a tile's loads, mostly L2 hits, are
-  // waited for at once; the suffix wave that shares the SIMD runs meanwhile.
-  constexpr int kChunkTiles = 64 * B / 32;
+  TileWalk<D, B> wk(kpool, vpool, n, g, Hkv, tok_begin);
   KvTile<D, B> ta;
-  for (int c0 = 0; c0 < ntiles; c0 += kChunkTiles) {
-    const int c1 = min(ntiles, c0 + kChunkTiles);
-    chunk_lb = (tok_begin + 32 * c0) / B;
-    my_id = bt[min(chunk_lb + lane, nblk - 1)];
+  for (int c0 = 0; c0 < ntiles; c0 += TileWalk<D, B>::kChunkTiles) {
+    const int c1 = min(ntiles, c0 + TileWalk<D, B>::kChunkTiles);
+    wk.begin_chunk(bt, c0);
     for (int t = c0; t < c1; ++t) {
-      load_tile(ta, t);
-      compute(ta, t);
+      wk.load(ta, t);
+      const int tok0 = tok_begin + 32 * t;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        tile_update<D>(st[c], ta.k, ta.v, qf[c], tok_end - tok0, n - tok0, scale_log2, lg,
+                       col_used[c]);
     }
   }
 }
@@ -808,8 +790,8 @@ __device__ __forceinline__ void balanced_body(
 }
 
 // KvT: uint16_t for bf16 pools, uint8_t for E4M3 pools (out_scale = the V scale).
-// Four waves per workgroup (one per SIMD of a compute unit): a quarter of the workgroup
-// dispatches of one wave per workgroup, so the grid is in place sooner.
+// Four waves per workgroup, one per SIMD of a compute unit (a quarter of the workgroup
+// dispatches of one wave per workgroup).
 constexpr int kBalancedWavesPerGroup = 4;
 template <int D, int B, typename OutT, typename KvT>
 __global__ __launch_bounds__(64 * kBalancedWavesPerGroup) void decode_balanced_kernel(
@@ -894,7 +876,7 @@ __device__ __forceinline__ void prefix_unit(
   if constexpr (kFp8)
     attend_tiles_fp8<D, B, 2>(st[0], qf[0], kpool, vpool, bt, pre, g, Hkv, tok0, te, scale_log2);
   else
-    attend_tiles2<D, B>(st, qf, kpool, vpool, bt, pre, g, Hkv, tok0, te, scale_log2);
+    attend_tiles2<D, B>(st, qf, kpool, vpool, bt, pre, g, Hkv, tok0, te, scale_log2, valid);
 #pragma unroll
   for (int k = 0; k < NCW; ++k) {
     // Each lane's column is its own row: reduce l over the 4 row groups only (lanes ^16, ^32).
