@@ -50,6 +50,9 @@ WORKLOADS = {
     # the decode batches through the fused write-and-decode call (one launch per step)
     "decode-8b-fused": 2,
     "decode-70b-fused": 3,
+    # one GPU's share of the 70B-shaped batch split by KV head over 8 GPUs: 1 KV head, 8 query
+    # heads, the same sequences (what each GPU runs under 8-way tensor parallelism)
+    "decode-70b-tp8": 3,
 }
 # Block-copy workloads, all on the decode-8b pool: copy-on-write of one block per sequence (a
 # fork of every sequence), a device-to-device migration of the blocks of half the sequences,
@@ -266,7 +269,8 @@ def run(args):
     fp8 = args.workload.endswith("-fp8")
     grouped = args.workload.startswith("shared-prefix-grouped")
     fused = args.workload.endswith("-fused")
-    w = wl.make_config(cfg, kv_dtype="fp8" if fp8 else "")
+    tp = 8 if args.workload.endswith("-tp8") else 1
+    w = wl.make_config(cfg, kv_dtype="fp8" if fp8 else "", tp=tp)
     log(f"workload {args.workload} ({wl.CONFIG_NAMES[cfg]}): S={w.num_seqs} "
         f"sum(n)={int(w.context_lens.sum())} NB={w.num_blocks}")
     dev = torch.device("cuda:0")
@@ -401,6 +405,7 @@ def run(args):
                  "shared-prefix-grouped-fp8": "shared-prefix, prefix-aware, 8B-shaped, fp8 KV",
                  "decode-8b-fused": "8B-shaped, fused write+decode",
                  "decode-70b-fused": "70B-shaped, fused write+decode",
+                 "decode-70b-tp8": "70B-shaped, one GPU's share under 8-way tensor parallelism",
                  }[args.workload]
         result.update(
             metric=f"paged decode KV HBM GB/s (% of peak) and decode tokens/sec/GPU, {shape}",
@@ -701,7 +706,10 @@ def main():
     w = res.pop("_w")
     pairs = res.pop("_pairs", None)
     base = "decode-8b" if blocks else args.workload
-    cfg = {"workload": f"{args.workload}: {CONFIG_NAMES[WORKLOADS[base]]}",
+    desc = CONFIG_NAMES[WORKLOADS[base]]
+    if args.workload.endswith("-tp8"):
+        desc += f"; one GPU's share under 8-way KV-head split ({w.num_q_heads}/{w.num_kv_heads} heads)"
+    cfg = {"workload": f"{args.workload}: {desc}",
            "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
            "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
            "sum_context_tokens": int(w.context_lens.sum()), "seed": WORKLOADS[base]}

@@ -308,28 +308,36 @@ CONFIG_NAMES = {
 }
 
 
-def make_config(k: int, seed: int | None = None, kv_dtype: str = "") -> Workload:
+def make_config(k: int, seed: int | None = None, kv_dtype: str = "", tp: int = 1) -> Workload:
     """The five workloads, k = 1..5, seeded by default with seed = k. kv_dtype "fp8" gives the
-    decode workloads (2, 3, 4) with E4M3 pools and the same lengths and block tables."""
+    decode workloads (2, 3, 4) with E4M3 pools and the same lengths and block tables. tp > 1
+    gives one GPU's share of a decode workload split by KV head over tp GPUs (tensor
+    parallelism): num_kv_heads / tp KV heads and their query heads, the same sequences and
+    lengths."""
     seed = k if seed is None else seed
     if kv_dtype:
         assert k in (2, 3, 4), "E4M3 pools are built for the bf16 decode workloads"
+    if tp != 1:
+        assert k in (2, 3, 4) and 8 % tp == 0, "a KV-head share of the decode workloads"
     rng = np.random.default_rng(seed)
+    hq, hkv = 32 // tp, 8 // tp  # workloads 2 and 4
+    hq70 = 64 // tp              # workload 3 (8 KV heads as well)
     if k == 1:
         return build_decode(seed, 4, 8, 8, 64, 16, [1, 17, 33, 100], "f32", num_blocks=64,
                             max_blocks=7, name="c1", rng=rng)
     if k == 2:
         lens = rng.integers(512, 4097, 64)
-        return build_decode(seed, 64, 32, 8, 128, 16, lens, "bf16", max_blocks=256, name="c2",
+        return build_decode(seed, 64, hq, hkv, 128, 16, lens, "bf16", max_blocks=256, name="c2",
                             rng=rng, kv_dtype=kv_dtype)
     if k == 3:
         lens = np.round(np.exp(rng.uniform(math.log(1024), math.log(32768), 32))).astype(int)
-        return build_decode(seed, 32, 64, 8, 128, 32, lens, "bf16", max_blocks=1024,
+        return build_decode(seed, 32, hq70, hkv, 128, 32, lens, "bf16", max_blocks=1024,
                             name="c3", rng=rng, kv_dtype=kv_dtype)
     if k == 4:
         suffix = rng.integers(16, 513, 64)
-        return build_decode(seed, 64, 32, 8, 128, 16, 2000 + suffix, "bf16", prefix_tokens=2000,
-                            max_blocks=157, name="c4", rng=rng, kv_dtype=kv_dtype)
+        return build_decode(seed, 64, hq, hkv, 128, 16, 2000 + suffix, "bf16",
+                            prefix_tokens=2000, max_blocks=157, name="c4", rng=rng,
+                            kv_dtype=kv_dtype)
     if k == 5:
         prior = rng.integers(0, 8193, 8)
         return build_prefill(seed, 8, 32, 8, 128, 16, prior, [512] * 8, "bf16", max_blocks=544,

@@ -86,6 +86,11 @@ DECODE_CASES = [
     ("g2_d64_b32", 107, 3, 8, 4, 64, 32, [96, 97, 1], "bf16"),
     ("f32_g4_d128", 108, 3, 16, 4, 128, 32, [1, 45, 333], "f32"),
     ("f32_g1_d64_b16", 109, 4, 8, 8, 64, 16, [1, 17, 33, 100], "f32"),
+    # one KV head (a GPU's share under KV-head tensor parallelism), 8 query heads on it
+    ("g8_hkv1_b32", 110, 4, 8, 1, 128, 32, [1, 33, 1500, 4000], "bf16"),
+    # one long context among short ones: rows with 1, 2 and over 64 partials (the reduce's
+    # four-wave form; under fixed partitions of 32 tokens, over a thousand)
+    ("wide_reduce", 111, 4, 16, 2, 128, 32, [1, 40, 2500, 33000], "bf16"),
 ]
 
 
@@ -159,6 +164,19 @@ def test_decode_full_config(k):
     assert_close(values(out), ref, TOL_BF16, f"config {k} (bf16 out)")
     out32 = d.decode(out_dtype=_torch_dtype("f32"))
     assert_close(values(out32), ref, TOL_BF16, f"config {k} (f32 out)")
+
+
+def test_decode_tp8_share_full():
+    """One GPU's share of the 70B-shaped batch under 8-way KV-head tensor parallelism (1 KV
+    head, its 8 query heads, the batch's full context lengths), in the launch configuration the
+    benchmark times, against the oracle."""
+    w = wl.make_config(3, tp=8)
+    kp, vp = _oracle_written(w)
+    ref = orc.decode(w.q, kp, vp, w.block_table, w.context_lens, w.scale, w.dtype)
+    log(f"decode 70B-shaped tp8 share: S={w.num_seqs} heads {w.num_q_heads}/{w.num_kv_heads}")
+    d = Dev(w)
+    d.write()
+    assert_close(values(d.decode()), ref, TOL_BF16, "70B-shaped tp8 share")
 
 
 def test_decode_deterministic():
