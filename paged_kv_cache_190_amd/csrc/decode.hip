@@ -36,6 +36,8 @@
 //
 // fp32 path (vector ALUs): one wave owns (sequence, query head, partition); lanes take one token
 // each for the scores, then one output dimension each for P.V.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -1079,43 +1081,31 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(
     if (k < cnt) wk = (k0 == 0) ? l0 * fast_exp2(m0 - M) : pl[k] * fast_exp2(pm[k] - M);
     const int kn = min(64, cnt - k0);
     const float* pk = po + static_cast<int64_t>(k0) * D;
-    int i = 0;
-    for (; i + 16 <= kn; i += 16) {  // long contexts: sixteen partials' loads in flight together
-      float a[16], b[16], wi[16];
+    // Groups of G partials with their loads in flight together (G = 16 for long rows, 4 for
+    // short ones); the last group is padded with the chunk's last slot at weight 0 (a written
+    // slot, so its values are finite), so no partial waits for the one before it.
+    auto merge = [&](auto group) {
+      constexpr int GS = decltype(group)::value;
+      for (int i = 0; i < kn; i += GS) {
+        float a[GS], b[GS], wi[GS];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        wi[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), i + u));
-        a[u] = pk[static_cast<int64_t>(i + u) * D + tid];
-        b[u] = two ? pk[static_cast<int64_t>(i + u) * D + tid + 64] : 0.f;
-      }
+        for (int u = 0; u < GS; ++u) {
+          const int iu = min(i + u, kn - 1);
+          const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), iu));
+          wi[u] = (i + u < kn) ? w : 0.f;
+          a[u] = pk[static_cast<int64_t>(iu) * D + tid];
+          b[u] = two ? pk[static_cast<int64_t>(iu) * D + tid + 64] : 0.f;
+        }
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        wsum += wi[u];
-        acc0 += wi[u] * a[u];
-        acc1 += wi[u] * b[u];
+        for (int u = 0; u < GS; ++u) {
+          wsum += wi[u];
+          acc0 += wi[u] * a[u];
+          acc1 += wi[u] * b[u];
+        }
       }
-    }
-    for (; i + 4 <= kn; i += 4) {  // four partials' loads in flight together
-      float a[4], b[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        a[u] = pk[static_cast<int64_t>(i + u) * D + tid];
-        b[u] = two ? pk[static_cast<int64_t>(i + u) * D + tid + 64] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), i + u));
-        wsum += wi;
-        acc0 += wi * a[u];
-        acc1 += wi * b[u];
-      }
-    }
-    for (; i < kn; ++i) {
-      const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), i));
-      wsum += wi;
-      acc0 += wi * pk[static_cast<int64_t>(i) * D + tid];
-      if (two) acc1 += wi * pk[static_cast<int64_t>(i) * D + tid + 64];
-    }
+    };
+    if (kn > 4) merge(std::integral_constant<int, 16>{});
+    else merge(std::integral_constant<int, 4>{});
   }
   const float inv = 1.0f / wsum;
   store_out(o + tid, acc0 * inv);
@@ -1124,9 +1114,9 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(
 
 // The same merge for rows that can have many partials (the host picks it when a row may have
 // more than 64, long contexts spread over many waves, and the rows are fewer than the GPU's
-// SIMDs). Four waves per row: the row's maximum
-// over all slots meets in LDS, then each wave merges a quarter of the slots with up to sixteen
-// partials' loads in flight together, and the four waves' sums meet in LDS again.
+// SIMDs). Four waves per row: the row's maximum over all slots meets in LDS, then each wave
+// merges a quarter of the slots, sixteen partials' loads in flight together, and the four
+// waves' sums meet in LDS again.
 template <typename OutT>
 __global__ __launch_bounds__(256) void decode_reduce_wide_kernel(
     OutT* __restrict__ out, const float* __restrict__ part_o, const float* __restrict__ part_m,
@@ -1175,14 +1165,17 @@ __global__ __launch_bounds__(256) void decode_reduce_wide_kernel(
     const float wk = (k < ke) ? pl[k] * fast_exp2(pm[k] - M) : 0.f;
     const int kn = min(64, ke - k0);
     const float* pk = po + static_cast<int64_t>(k0) * D;
-    int i = 0;
-    for (; i + 16 <= kn; i += 16) {
+    // groups of sixteen, the last one padded with the wave's last slot at weight 0 (a written
+    // slot, so its values are finite), so every group's loads are in flight together
+    for (int i = 0; i < kn; i += 16) {
       float a[16], b[16], wi[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
-        wi[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), i + u));
-        a[u] = pk[static_cast<int64_t>(i + u) * D + lane];
-        b[u] = two ? pk[static_cast<int64_t>(i + u) * D + lane + 64] : 0.f;
+        const int iu = min(i + u, kn - 1);
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), iu));
+        wi[u] = (i + u < kn) ? w : 0.f;
+        a[u] = pk[static_cast<int64_t>(iu) * D + lane];
+        b[u] = two ? pk[static_cast<int64_t>(iu) * D + lane + 64] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
@@ -1190,12 +1183,6 @@ __global__ __launch_bounds__(256) void decode_reduce_wide_kernel(
         acc0 += wi[u] * a[u];
         acc1 += wi[u] * b[u];
       }
-    }
-    for (; i < kn; ++i) {
-      const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), i));
-      wsum += wi;
-      acc0 += wi * pk[static_cast<int64_t>(i) * D + lane];
-      if (two) acc1 += wi * pk[static_cast<int64_t>(i) * D + lane + 64];
     }
   }
   s_acc[wv][0][lane] = acc0;
