@@ -326,9 +326,9 @@ int pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_pool,
  *                     ignored for bf16); q is bf16; out_dtype PKV_BF16 or PKV_F32
  *   workspace         pkv_decode_shared_prefix_workspace_size(...) bytes
  * Other arguments as for pkv_paged_attention_decode. Each shared prefix is split into chunks
- * of 256 tokens; a chunk is attended for 16 (member, query head) rows at a time, and the
- * private rest of every context goes through the balanced split; a reduce kernel merges the
- * pieces by log-sum-exp.
+ * of 256 tokens; a chunk is attended for 32 (member, query head) rows at a time over bf16
+ * pools and 16 over E4M3 pools, and the private rest of every context goes through the
+ * balanced split; a reduce kernel merges the pieces by log-sum-exp.
  */
 size_t pkv_decode_shared_prefix_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
                                                int head_dim, int max_context_len,
