@@ -91,6 +91,7 @@ DECODE_CASES = [
     # one long context among short ones: rows with 1, 2 and over 64 partials (the reduce's
     # four-wave form; under fixed partitions of 32 tokens, over a thousand)
     ("wide_reduce", 111, 4, 16, 2, 128, 32, [1, 40, 2500, 33000], "bf16"),
+    ("wide_reduce_d64", 112, 3, 8, 2, 64, 16, [1, 70, 20000], "bf16"),
 ]
 
 
