@@ -42,7 +42,10 @@
  *    enqueues its kernels on `stream` (a hipStream_t passed as void*; NULL = null stream) and
  *    returns. Calls are thread-safe.
  *  - Return value: a pkv_status. Arguments are validated on the host before any HIP call; a
- *    failure returns without launching anything. PKV_ERR_HIP reports a launch failure.
+ *    failure returns without launching anything. PKV_ERR_HIP reports a kernel launch that the
+ *    HIP runtime refused (the status of that launch; a call of two kernels launches the second
+ *    only if the first was accepted). Faults inside a kernel surface later, at the caller's
+ *    next synchronisation, as HIP errors of the caller's own calls.
  *    pkv_last_error() returns a thread-local text for the last non-OK status of the thread.
  *  - dtype PKV_F32 or PKV_BF16 (bf16 = IEEE binary32 truncated to the top 16 bits).
  *    head_dim in {64, 128}; block_size in {16, 32}; num_q_heads % num_kv_heads == 0.
@@ -69,7 +72,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 
 typedef enum {
   PKV_OK = 0,
@@ -236,14 +239,16 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads
  *                         unit.
  *                    0:   bf16 inputs: balanced split -- the batch's 32-token tiles, in
  *                         (sequence, KV head, position) order, are dealt in equal contiguous
- *                         shares to a fixed number of waves (1024 by default; the environment
- *                         variable PKV_DECODE_WAVES overrides it), so every wave does the same
- *                         work whatever the mix of context lengths. fp32 inputs: fixed
- *                         partitions of a default size.
+ *                         shares to num_waves waves, so every wave does the same work whatever
+ *                         the mix of context lengths. fp32 inputs: fixed partitions of a
+ *                         default size.
  *                    A context cut into several pieces is merged by a second kernel: each piece
  *                    leaves (max, sum of exponentials, normalised output) and the merge weighs
  *                    them by log-sum-exp. The result is the same softmax up to floating-point
  *                    rounding.
+ *   num_waves     waves of the balanced split (0 = the default, 1024); fewer are used when the
+ *                 batch has under 8 tiles per wave. Ignored with fixed partitions.
+ *                 Must lie in [0, 2^20].
  *   workspace     device buffer of at least pkv_decode_workspace_size(...) bytes (may be NULL
  *                 when that size is 0); contents on entry are ignored.
  * out_dtype may differ from dtype (e.g. bf16 inputs with an fp32 output); the bf16 output is
@@ -254,8 +259,8 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_pool, con
                                int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                                int block_size, int max_blocks_per_seq, int num_blocks,
                                float scale, int max_context_len, int partition_size,
-                               void* workspace, size_t workspace_bytes, int dtype, int out_dtype,
-                               void* stream);
+                               int num_waves, void* workspace, size_t workspace_bytes, int dtype,
+                               int out_dtype, void* stream);
 
 /*
  * pkv_kv_cache_write_and_decode -- pkv_kv_cache_write of each sequence's new token followed by
@@ -270,8 +275,8 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_pool, con
  *                 n - 1), or negative when the pool already holds every token of s
  *   k_pool, v_pool  read, and written at the new tokens' slots
  *   workspace     pkv_decode_workspace_size(..., partition_size = 0, PKV_BF16) bytes
- * Other arguments, preconditions and errors as for pkv_paged_attention_decode (balanced split;
- * PKV_DECODE_WAVES applies). The attention takes the newest token's K/V from k_new / v_new, and
+ * Other arguments (num_waves included), preconditions and errors as for
+ * pkv_paged_attention_decode with the balanced split. The attention takes the newest token's K/V from k_new / v_new, and
  * the wave that does so also stores them into the pool, so no kernel has to wait for the write.
  */
 int pkv_kv_cache_write_and_decode(void* out, const void* q, const void* k_new,
@@ -280,8 +285,8 @@ int pkv_kv_cache_write_and_decode(void* out, const void* q, const void* k_new,
                                   const int32_t* context_lens, int num_seqs, int num_q_heads,
                                   int num_kv_heads, int head_dim, int block_size,
                                   int max_blocks_per_seq, int num_blocks, float scale,
-                                  int max_context_len, void* workspace, size_t workspace_bytes,
-                                  int out_dtype, void* stream);
+                                  int max_context_len, int num_waves, void* workspace,
+                                  size_t workspace_bytes, int out_dtype, void* stream);
 
 /*
  * pkv_paged_attention_decode_fp8 -- pkv_paged_attention_decode over E4M3 pools.
@@ -290,9 +295,8 @@ int pkv_kv_cache_write_and_decode(void* out, const void* q, const void* k_new,
  * The pools hold E4M3 codes written by pkv_kv_cache_write_fp8 with the same k_scale and
  * v_scale (finite, > 0); K's value is code value * k_scale, V's is code value * v_scale, and
  * with those values the result is pkv_paged_attention_decode's. q is bf16; out_dtype PKV_BF16
- * or PKV_F32. The context is always split the balanced way (1024 waves by default;
- * PKV_DECODE_WAVES overrides it); workspace: pkv_decode_workspace_size(..., dtype =
- * PKV_FP8_E4M3) bytes. Other arguments, preconditions and errors as for
+ * or PKV_F32. The context is always split the balanced way over num_waves waves (0 = the
+ * default, 1024); workspace: pkv_decode_workspace_size(..., dtype = PKV_FP8_E4M3) bytes. Other arguments, preconditions and errors as for
  * pkv_paged_attention_decode. Unwritten slots may hold any code, NaN included.
  */
 int pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_pool,
@@ -301,8 +305,8 @@ int pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_pool,
                                    int num_kv_heads, int head_dim, int block_size,
                                    int max_blocks_per_seq, int num_blocks, float scale,
                                    float k_scale, float v_scale, int max_context_len,
-                                   void* workspace, size_t workspace_bytes, int out_dtype,
-                                   void* stream);
+                                   int num_waves, void* workspace, size_t workspace_bytes,
+                                   int out_dtype, void* stream);
 
 /*
  * pkv_paged_attention_decode_shared_prefix -- decode for batches whose sequences share
@@ -325,7 +329,8 @@ int pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_pool,
  *   kv_dtype          PKV_BF16 or PKV_FP8_E4M3 (then k_scale, v_scale as for the fp8 decode;
  *                     ignored for bf16); q is bf16; out_dtype PKV_BF16 or PKV_F32
  *   workspace         pkv_decode_shared_prefix_workspace_size(...) bytes
- * Other arguments as for pkv_paged_attention_decode. Each shared prefix is split into chunks
+ * Other arguments as for pkv_paged_attention_decode (num_waves: waves of the balanced split of
+ * the private suffixes, 0 = the default). Each shared prefix is split into chunks
  * of 256 tokens; a chunk is attended for 32 (member, query head) rows at a time over bf16
  * pools and 16 over E4M3 pools, and the private rest of every context goes through the
  * balanced split; a reduce kernel merges the pieces by log-sum-exp.
@@ -338,9 +343,9 @@ int pkv_paged_attention_decode_shared_prefix(
     const int32_t* block_table, const int32_t* context_lens, const int32_t* group_start,
     const int32_t* group_prefix_len, int num_groups, int max_group_size, int max_prefix_len,
     int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-    int max_blocks_per_seq, int num_blocks, float scale, int max_context_len, int kv_dtype,
-    float k_scale, float v_scale, void* workspace, size_t workspace_bytes, int out_dtype,
-    void* stream);
+    int max_blocks_per_seq, int num_blocks, float scale, int max_context_len, int num_waves,
+    int kv_dtype, float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+    int out_dtype, void* stream);
 
 /*
  * pkv_paged_attention_prefill_chunk -- a causal chunk of query tokens against the paged cache.

@@ -52,7 +52,7 @@ def lib() -> ctypes.CDLL:
     L.pkv_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     L.pkv_paged_attention_decode.restype = i32
     L.pkv_paged_attention_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
-                                             i32, i32, f32, i32, i32, vp, sz, i32, i32, vp]
+                                             i32, i32, f32, i32, i32, i32, vp, sz, i32, i32, vp]
     L.pkv_paged_attention_prefill_chunk.restype = i32
     L.pkv_paged_attention_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                                     i32, i32, i32, i32, i32, f32, i32, i32, i32,
@@ -69,16 +69,18 @@ def lib() -> ctypes.CDLL:
                                          f32, vp]
     L.pkv_paged_attention_decode_fp8.restype = i32
     L.pkv_paged_attention_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
-                                                 i32, i32, f32, f32, f32, i32, vp, sz, i32, vp]
+                                                 i32, i32, f32, f32, f32, i32, i32, vp, sz, i32,
+                                                 vp]
     L.pkv_decode_shared_prefix_workspace_size.restype = sz
     L.pkv_decode_shared_prefix_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     L.pkv_paged_attention_decode_shared_prefix.restype = i32
     L.pkv_paged_attention_decode_shared_prefix.argtypes = [
         vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, f32,
-        i32, i32, f32, f32, vp, sz, i32, vp]
+        i32, i32, i32, f32, f32, vp, sz, i32, vp]
     L.pkv_kv_cache_write_and_decode.restype = i32
     L.pkv_kv_cache_write_and_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
-                                                i32, i32, i32, i32, f32, i32, vp, sz, i32, vp]
+                                                i32, i32, i32, i32, f32, i32, i32, vp, sz, i32,
+                                                vp]
     L.pkv_kv_cache_copy_blocks.restype = i32
     L.pkv_kv_cache_copy_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                            vp]
@@ -197,9 +199,11 @@ def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_con
 
 
 def paged_attention_decode(out, q, k_pool, v_pool, block_table, context_lens, scale,
-                           max_context_len=0, partition_size=0, workspace=None, stream=None):
+                           max_context_len=0, partition_size=0, workspace=None, stream=None,
+                           num_waves=0):
     """out [S][Hq][D] = softmax(scale * q K^T) V over each sequence's paged context.
-    A workspace (uint8 device tensor) is allocated when needed and not given."""
+    A workspace (uint8 device tensor) is allocated when needed and not given. num_waves: waves
+    of the balanced split (0 = the library's default)."""
     import torch
     S, hq, d = q.shape
     nb, hkv, b, d2 = k_pool.shape
@@ -218,14 +222,14 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_table, context_lens, sc
     _check(lib().pkv_paged_attention_decode(
         _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
         _i32(block_table, "block_table"), _i32(context_lens, "context_lens"), S, hq, hkv, d, b,
-        mb, nb, float(scale), int(max_context_len), int(partition_size), ws_ptr, ws_bytes,
-        _dtype_code(q), _dtype_code(out), _stream(stream)), "paged_attention_decode")
+        mb, nb, float(scale), int(max_context_len), int(partition_size), int(num_waves), ws_ptr,
+        ws_bytes, _dtype_code(q), _dtype_code(out), _stream(stream)), "paged_attention_decode")
     return out
 
 
 def kv_cache_write_and_decode(out, q, k_new, v_new, slot_mapping, k_pool, v_pool, block_table,
                               context_lens, scale, max_context_len=0, workspace=None,
-                              stream=None):
+                              stream=None, num_waves=0):
     """kv_cache_write of each sequence's newest token (k_new / v_new [S][Hkv][D], slot_mapping
     [S], negative = none) and paged_attention_decode over the contexts including it, the write
     folded into the attention kernel (bf16). A workspace is allocated when needed and not
@@ -251,9 +255,9 @@ def kv_cache_write_and_decode(out, q, k_new, v_new, slot_mapping, k_pool, v_pool
         _dev(out, "out"), _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
         _i32(slot_mapping, "slot_mapping"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
         _i32(block_table, "block_table"), _i32(context_lens, "context_lens"), S, hq, hkv, d, b,
-        mb, nb, float(scale), int(max_context_len), ctypes.c_void_p(workspace.data_ptr()),
-        workspace.numel() * workspace.element_size(), _dtype_code(out), _stream(stream)),
-        "kv_cache_write_and_decode")
+        mb, nb, float(scale), int(max_context_len), int(num_waves),
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+        _dtype_code(out), _stream(stream)), "kv_cache_write_and_decode")
     return out
 
 
@@ -277,7 +281,8 @@ def kv_cache_write_fp8(k_new, v_new, k_pool, v_pool, slot_mapping, k_scale, v_sc
 
 
 def paged_attention_decode_fp8(out, q, k_pool, v_pool, block_table, context_lens, scale, k_scale,
-                               v_scale, max_context_len=0, workspace=None, stream=None):
+                               v_scale, max_context_len=0, workspace=None, stream=None,
+                               num_waves=0):
     """paged_attention_decode over E4M3 pools (K value = code * k_scale, V value = code *
     v_scale); q bf16; out bf16 or fp32. A workspace is allocated when needed and not given."""
     import torch
@@ -299,8 +304,9 @@ def paged_attention_decode_fp8(out, q, k_pool, v_pool, block_table, context_lens
         _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
         _i32(block_table, "block_table"), _i32(context_lens, "context_lens"), S, hq, hkv, d, b,
         mb, nb, float(scale), float(k_scale), float(v_scale), int(max_context_len),
-        ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
-        _dtype_code(out), _stream(stream)), "paged_attention_decode_fp8")
+        int(num_waves), ctypes.c_void_p(workspace.data_ptr()),
+        workspace.numel() * workspace.element_size(), _dtype_code(out), _stream(stream)),
+        "paged_attention_decode_fp8")
     return out
 
 
@@ -314,7 +320,8 @@ def decode_shared_prefix_workspace_size(num_seqs, num_q_heads, num_kv_heads, hea
 def paged_attention_decode_shared_prefix(out, q, k_pool, v_pool, block_table, context_lens,
                                          group_start, group_prefix_len, scale, max_group_size,
                                          max_prefix_len, k_scale=1.0, v_scale=1.0,
-                                         max_context_len=0, workspace=None, stream=None):
+                                         max_context_len=0, workspace=None, stream=None,
+                                         num_waves=0):
     """paged_attention_decode (bf16 pools) or paged_attention_decode_fp8 (uint8 E4M3 pools) for
     a batch in groups of consecutive sequences sharing prefixes: group i is sequences
     group_start[i] .. group_start[i+1]-1, sharing their first group_prefix_len[i] tokens (the
@@ -344,7 +351,7 @@ def paged_attention_decode_shared_prefix(out, q, k_pool, v_pool, block_table, co
         _i32(block_table, "block_table"), _i32(context_lens, "context_lens"),
         _i32(group_start, "group_start"), _i32(group_prefix_len, "group_prefix_len"), ng,
         int(max_group_size), int(max_prefix_len), S, hq, hkv, d, b, mb, nb, float(scale),
-        int(max_context_len), kvd, float(k_scale), float(v_scale),
+        int(max_context_len), int(num_waves), kvd, float(k_scale), float(v_scale),
         ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
         _dtype_code(out), _stream(stream)), "paged_attention_decode_shared_prefix")
     return out

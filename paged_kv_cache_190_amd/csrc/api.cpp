@@ -155,26 +155,19 @@ struct BalancedPlan {
   size_t o_off, m_off, l_off, cnt_off, bytes;
 };
 
-int decode_waves_setting(int default_waves) {
-  const char* e = std::getenv("PKV_DECODE_WAVES");
-  if (e) {
-    const int v = std::atoi(e);
-    if (v > 0) return v;
-  }
-  return default_waves;
-}
+// Waves of the balanced split: the caller's count, or the default for the pool type.
+constexpr int kMaxDecodeWaves = 1 << 20;
 
 // extra_slots: partial slots per row ahead of the balanced split's (the prefix chunks).
-BalancedPlan balanced_plan(int S, int Hq, int Hkv, int D, int max_ctx,
-                           int default_waves = kDefaultDecodeWaves, int extra_slots = 0) {
+BalancedPlan balanced_plan(int S, int Hq, int Hkv, int D, int max_ctx, int waves_request,
+                           int extra_slots = 0) {
   BalancedPlan pl{};
   const int G = Hq / Hkv;
   const long long segs = static_cast<long long>(Hkv) * ((G + 15) / 16);
   const long long seg_tiles = (std::max(max_ctx, 1) + 31) / 32;
   const long long t_upper = static_cast<long long>(S) * segs * seg_tiles;
   pl.waves = static_cast<int>(
-      std::max(1LL, std::min<long long>(decode_waves_setting(default_waves),
-                                        t_upper / kMinTilesPerWave)));
+      std::max(1LL, std::min<long long>(waves_request, t_upper / kMinTilesPerWave)));
   pl.kmax = static_cast<int>((seg_tiles + kMinTilesPerWave - 1) / kMinTilesPerWave + 1) +
             extra_slots;
   const size_t rows = static_cast<size_t>(S) * Hq * pl.kmax;
@@ -333,7 +326,8 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads
     return balanced_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                          kDefaultDecodeWavesFp8).bytes;
   if (partition_size == 0 && dtype == PKV_BF16)
-    return balanced_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len).bytes;
+    return balanced_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                         kDefaultDecodeWaves).bytes;
   const int p = resolve_partition(partition_size, num_seqs, num_kv_heads, max_context_len);
   if (p <= 0) return 0;
   return fixed_workspace_bytes(num_seqs, num_q_heads, head_dim,
@@ -347,9 +341,11 @@ namespace {
 // Balanced split set-up: the plan for a's sizes, and the partial buffers carved out of the
 // caller's workspace.
 int setup_balanced(pkv::DecodeArgs& a, void* workspace, size_t workspace_bytes,
-                   int default_waves, int extra_slots = 0) {
-  const BalancedPlan pl =
-      balanced_plan(a.S, a.Hq, a.Hkv, a.D, a.max_ctx, default_waves, extra_slots);
+                   int default_waves, int num_waves, int extra_slots = 0) {
+  if (num_waves < 0 || num_waves > kMaxDecodeWaves)
+    return fail(PKV_ERR_INVALID_ARG, "num_waves %d outside [0, %d]", num_waves, kMaxDecodeWaves);
+  const BalancedPlan pl = balanced_plan(a.S, a.Hq, a.Hkv, a.D, a.max_ctx,
+                                        num_waves > 0 ? num_waves : default_waves, extra_slots);
   if (!workspace || workspace_bytes < pl.bytes)
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.bytes,
                 workspace ? workspace_bytes : static_cast<size_t>(0));
@@ -430,9 +426,9 @@ int pkv_paged_attention_decode_shared_prefix(
     const int32_t* block_table, const int32_t* context_lens, const int32_t* group_start,
     const int32_t* group_prefix_len, int num_groups, int max_group_size, int max_prefix_len,
     int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-    int max_blocks_per_seq, int num_blocks, float scale, int max_context_len, int kv_dtype,
-    float k_scale, float v_scale, void* workspace, size_t workspace_bytes, int out_dtype,
-    void* stream) {
+    int max_blocks_per_seq, int num_blocks, float scale, int max_context_len, int num_waves,
+    int kv_dtype, float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+    int out_dtype, void* stream) {
   if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs = %d is negative", num_seqs);
   if (num_seqs == 0) return PKV_OK;
   pkv::DecodeArgs a{};
@@ -468,7 +464,7 @@ int pkv_paged_attention_decode_shared_prefix(
   const long long waves_p = (units + 7) / 8 * 8;
   const int default_waves =
       kv_dtype == PKV_FP8_E4M3 ? kDefaultDecodeWavesFp8 : kDefaultDecodeWaves;
-  st = setup_balanced(a, workspace, workspace_bytes, default_waves, nch);
+  st = setup_balanced(a, workspace, workspace_bytes, default_waves, num_waves, nch);
   if (st != PKV_OK) return st;
   if (waves_p + a.waves > 0x7fffffffLL)
     return fail(PKV_ERR_UNSUPPORTED, "too many prefix units (%lld)", units);
@@ -493,8 +489,8 @@ int pkv_kv_cache_write_and_decode(void* out, const void* q, const void* k_new,
                                   const int32_t* context_lens, int num_seqs, int num_q_heads,
                                   int num_kv_heads, int head_dim, int block_size,
                                   int max_blocks_per_seq, int num_blocks, float scale,
-                                  int max_context_len, void* workspace, size_t workspace_bytes,
-                                  int out_dtype, void* stream) {
+                                  int max_context_len, int num_waves, void* workspace,
+                                  size_t workspace_bytes, int out_dtype, void* stream) {
   if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs = %d is negative", num_seqs);
   if (num_seqs == 0) return PKV_OK;
   if (!k_new || !v_new || !slot_mapping)
@@ -506,7 +502,7 @@ int pkv_kv_cache_write_and_decode(void* out, const void* q, const void* k_new,
   if (st != PKV_OK) return st;
   if (static_cast<long long>(num_blocks) * block_size > 0x7fffffffLL)
     return fail(PKV_ERR_UNSUPPORTED, "pool of %d blocks exceeds int32 slot numbers", num_blocks);
-  st = setup_balanced(a, workspace, workspace_bytes, kDefaultDecodeWaves);
+  st = setup_balanced(a, workspace, workspace_bytes, kDefaultDecodeWaves, num_waves);
   if (st != PKV_OK) return st;
   a.step = 1;
   a.k_new = k_new;
@@ -524,8 +520,8 @@ int pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_pool,
                                    int num_kv_heads, int head_dim, int block_size,
                                    int max_blocks_per_seq, int num_blocks, float scale,
                                    float k_scale, float v_scale, int max_context_len,
-                                   void* workspace, size_t workspace_bytes, int out_dtype,
-                                   void* stream) {
+                                   int num_waves, void* workspace, size_t workspace_bytes,
+                                   int out_dtype, void* stream) {
   if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs = %d is negative", num_seqs);
   if (num_seqs == 0) return PKV_OK;
   pkv::DecodeArgs a{};
@@ -537,7 +533,7 @@ int pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_pool,
     return fail(PKV_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
   if (!std::isfinite(scale * k_scale))
     return fail(PKV_ERR_INVALID_ARG, "scale * k_scale is not finite");
-  st = setup_balanced(a, workspace, workspace_bytes, kDefaultDecodeWavesFp8);
+  st = setup_balanced(a, workspace, workspace_bytes, kDefaultDecodeWavesFp8, num_waves);
   if (st != PKV_OK) return st;
   a.fp8_kv = 1;
   a.k_scale = k_scale;
@@ -553,8 +549,8 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_pool, con
                                int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                                int block_size, int max_blocks_per_seq, int num_blocks,
                                float scale, int max_context_len, int partition_size,
-                               void* workspace, size_t workspace_bytes, int dtype, int out_dtype,
-                               void* stream) {
+                               int num_waves, void* workspace, size_t workspace_bytes, int dtype,
+                               int out_dtype, void* stream) {
   if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs = %d is negative", num_seqs);
   if (num_seqs == 0) return PKV_OK;
   pkv::DecodeArgs a{};
@@ -568,7 +564,7 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_pool, con
                 "partition_size %d must be a non-negative multiple of 16 and of block_size",
                 partition_size);
   if (partition_size == 0 && dtype == PKV_BF16) {
-    st = setup_balanced(a, workspace, workspace_bytes, kDefaultDecodeWaves);
+    st = setup_balanced(a, workspace, workspace_bytes, kDefaultDecodeWaves, num_waves);
     if (st != PKV_OK) return st;
   } else {
     const int P = resolve_partition(partition_size, num_seqs, num_kv_heads, max_ctx);

@@ -39,11 +39,10 @@ hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream) {
   const int64_t words = static_cast<int64_t>(a.Hkv) * a.B * a.D * a.elem_bytes / 16;
   const int64_t groups = (words + 4 * 256 - 1) / (4 * 256);  // about four words per thread
   dim3 grid(static_cast<unsigned>(groups < 64 ? groups : 64), a.n_pairs);
-  (void)launch_kernel(K_COPY_BLOCKS, copy_blocks_kernel, grid, dim3(256), stream,
+  return launch_kernel(K_COPY_BLOCKS, copy_blocks_kernel, grid, dim3(256), stream,
                       static_cast<const u32x4*>(a.src_k), static_cast<const u32x4*>(a.src_v),
                       static_cast<u32x4*>(a.dst_k), static_cast<u32x4*>(a.dst_v), a.pairs,
                       words);
-  return hipGetLastError();
 }
 
 }  // namespace pkv

@@ -1201,35 +1201,32 @@ __global__ __launch_bounds__(256) void decode_reduce_wide_kernel(
 // ------------------------------------------------------------------------------ launchers
 
 template <int D, int B, typename OutT>
-static void launch_bf16(const DecodeArgs& a, hipStream_t st) {
+static hipError_t launch_bf16(const DecodeArgs& a, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   const int HG = (G + 15) / 16;
   const int groups = (a.waves + kBalancedWavesPerGroup - 1) / kBalancedWavesPerGroup;
   if (a.fp8_kv) {
-    (void)launch_kernel(K_DECODE_PARTITION, decode_balanced_kernel<D, B, OutT, uint8_t>,
+    return launch_kernel(K_DECODE_PARTITION, decode_balanced_kernel<D, B, OutT, uint8_t>,
         dim3(groups), dim3(64 * kBalancedWavesPerGroup), st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l,
         a.seg_count, static_cast<const uint16_t*>(a.q), static_cast<const uint8_t*>(a.k_pool),
         static_cast<const uint8_t*>(a.v_pool), a.block_table, a.context_lens, a.S, a.Hq, a.Hkv, G,
         HG, a.MB, a.KMAX, a.min_tiles, a.scale * a.k_scale * kLog2e, a.v_scale);
-    return;
   }
   if (a.balanced) {
-    (void)launch_kernel(K_DECODE_PARTITION, decode_balanced_kernel<D, B, OutT, uint16_t>,
+    return launch_kernel(K_DECODE_PARTITION, decode_balanced_kernel<D, B, OutT, uint16_t>,
         dim3(groups), dim3(64 * kBalancedWavesPerGroup), st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l,
         a.seg_count, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
         static_cast<const uint16_t*>(a.v_pool), a.block_table, a.context_lens, a.S, a.Hq, a.Hkv, G,
         HG, a.MB, a.KMAX, a.min_tiles, a.scale * kLog2e, 1.0f);
-    return;
   }
   dim3 grid(a.Hkv * HG, a.S, a.NP);
   if (a.NP > 1)
-    (void)launch_kernel(K_DECODE_PARTITION, decode_fixed_kernel<D, B, true, OutT>, dim3(grid), dim3(64),
+    return launch_kernel(K_DECODE_PARTITION, decode_fixed_kernel<D, B, true, OutT>, dim3(grid), dim3(64),
         st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l,
         static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
         static_cast<const uint16_t*>(a.v_pool), a.block_table, a.context_lens, a.Hq, a.Hkv, G, HG,
         a.MB, a.P, a.NP, a.scale * kLog2e);
-  else
-    (void)launch_kernel(K_DECODE_PARTITION, decode_fixed_kernel<D, B, false, OutT>, dim3(grid), dim3(64),
+  return launch_kernel(K_DECODE_PARTITION, decode_fixed_kernel<D, B, false, OutT>, dim3(grid), dim3(64),
         st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l,
         static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
         static_cast<const uint16_t*>(a.v_pool), a.block_table, a.context_lens, a.Hq, a.Hkv, G, HG,
@@ -1237,11 +1234,11 @@ static void launch_bf16(const DecodeArgs& a, hipStream_t st) {
 }
 
 template <int D, int B, typename OutT, typename KvT>
-static void launch_prefix_t(const DecodeArgs& a, hipStream_t st) {
+static hipError_t launch_prefix_t(const DecodeArgs& a, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   const int HG = (G + 15) / 16;
   const float sl = a.scale * (a.fp8_kv ? a.k_scale : 1.0f) * kLog2e;
-  (void)launch_kernel(K_DECODE_PARTITION, decode_prefix_kernel<D, B, OutT, KvT>,
+  return launch_kernel(K_DECODE_PARTITION, decode_prefix_kernel<D, B, OutT, KvT>,
       dim3(a.prefix_waves + a.waves), dim3(64), st, static_cast<OutT*>(a.out), a.part_o,
       a.part_m, a.part_l, a.seg_count, static_cast<const uint16_t*>(a.q),
       static_cast<const KvT*>(a.k_pool), static_cast<const KvT*>(a.v_pool), a.block_table,
@@ -1251,10 +1248,10 @@ static void launch_prefix_t(const DecodeArgs& a, hipStream_t st) {
 }
 
 template <int D, int B, typename OutT>
-static void launch_step_t(const DecodeArgs& a, hipStream_t st) {
+static hipError_t launch_step_t(const DecodeArgs& a, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   const int HG = (G + 15) / 16;
-  (void)launch_kernel(K_DECODE_PARTITION, decode_step_kernel<D, B, OutT>,
+  return launch_kernel(K_DECODE_PARTITION, decode_step_kernel<D, B, OutT>,
       dim3((a.waves + kBalancedWavesPerGroup - 1) / kBalancedWavesPerGroup),
       dim3(64 * kBalancedWavesPerGroup), st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l, a.seg_count,
       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_new),
@@ -1265,44 +1262,34 @@ static void launch_step_t(const DecodeArgs& a, hipStream_t st) {
 }
 
 template <int D, int B, bool SPLIT, typename OutT>
-static void launch_f32(const DecodeArgs& a, hipStream_t st) {
+static hipError_t launch_f32(const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.S, a.Hq, a.NP);
-  (void)launch_kernel(K_DECODE_PARTITION, attn_f32_kernel<D, B, SPLIT, false, OutT>, dim3(grid), dim3(64),
+  return launch_kernel(K_DECODE_PARTITION, attn_f32_kernel<D, B, SPLIT, false, OutT>, dim3(grid), dim3(64),
       st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l, static_cast<const float*>(a.q),
       static_cast<const float*>(a.k_pool), static_cast<const float*>(a.v_pool), a.block_table,
       a.context_lens, nullptr, a.S, a.Hq, a.Hkv, a.MB, a.P, a.NP, a.scale * kLog2e);
 }
 
 template <int D, int B, typename OutT>
-static void dispatch_out_t(const DecodeArgs& a, hipStream_t st) {
-  if (a.step) {
-    launch_step_t<D, B, OutT>(a, st);
-  } else if (a.num_groups > 0) {
-    if (a.fp8_kv) launch_prefix_t<D, B, OutT, uint8_t>(a, st);
-    else launch_prefix_t<D, B, OutT, uint16_t>(a, st);
-  } else if (a.bf16_in || a.fp8_kv) {
-    launch_bf16<D, B, OutT>(a, st);
-  } else {
-    if (a.NP > 1) launch_f32<D, B, true, OutT>(a, st);
-    else launch_f32<D, B, false, OutT>(a, st);
-  }
+static hipError_t dispatch_out_t(const DecodeArgs& a, hipStream_t st) {
+  if (a.step) return launch_step_t<D, B, OutT>(a, st);
+  if (a.num_groups > 0)
+    return a.fp8_kv ? launch_prefix_t<D, B, OutT, uint8_t>(a, st)
+                    : launch_prefix_t<D, B, OutT, uint16_t>(a, st);
+  if (a.bf16_in || a.fp8_kv) return launch_bf16<D, B, OutT>(a, st);
+  return a.NP > 1 ? launch_f32<D, B, true, OutT>(a, st) : launch_f32<D, B, false, OutT>(a, st);
 }
 
 template <int D, int B>
-static void dispatch_out(const DecodeArgs& a, hipStream_t st) {
-  if (a.bf16_out) dispatch_out_t<D, B, uint16_t>(a, st);
-  else dispatch_out_t<D, B, float>(a, st);
+static hipError_t dispatch_out(const DecodeArgs& a, hipStream_t st) {
+  return a.bf16_out ? dispatch_out_t<D, B, uint16_t>(a, st) : dispatch_out_t<D, B, float>(a, st);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
-  if (a.D == 128) {
-    if (a.B == 16) dispatch_out<128, 16>(a, st);
-    else dispatch_out<128, 32>(a, st);
-  } else {
-    if (a.B == 16) dispatch_out<64, 16>(a, st);
-    else dispatch_out<64, 32>(a, st);
-  }
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  if (a.D == 128) e = a.B == 16 ? dispatch_out<128, 16>(a, st) : dispatch_out<128, 32>(a, st);
+  else e = a.B == 16 ? dispatch_out<64, 16>(a, st) : dispatch_out<64, 32>(a, st);
+  // no merge after a refused partition launch (its partials were never written)
   if (e != hipSuccess || (!a.balanced && a.NP <= 1)) return e;
   const int G = a.Hq / a.Hkv;
   const int HG = (G + 15) / 16;
@@ -1311,27 +1298,23 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.Hq, a.S);
   // Rows that may have many partials, and fewer rows than the GPU has SIMDs: four waves per
   // row. (With more rows than SIMDs the one-wave form is faster: 2048 rows of the 70B-shaped
-  // batch took 4.9 µs with it and 8.3 µs with four waves per row.)
+  // batch took 4.9 us with it and 8.3 us with four waves per row.)
   if (kmax > 64 && static_cast<int64_t>(a.S) * a.Hq < 1024) {
     if (a.bf16_out)
-      (void)launch_kernel(K_DECODE_REDUCE, decode_reduce_wide_kernel<uint16_t>, dim3(grid),
+      return launch_kernel(K_DECODE_REDUCE, decode_reduce_wide_kernel<uint16_t>, dim3(grid),
           dim3(256), st, static_cast<uint16_t*>(a.out), a.part_o, a.part_m, a.part_l,
           a.context_lens, cnt, a.Hq, G, HG, a.D, a.P, kmax);
-    else
-      (void)launch_kernel(K_DECODE_REDUCE, decode_reduce_wide_kernel<float>, dim3(grid),
-          dim3(256), st, static_cast<float*>(a.out), a.part_o, a.part_m, a.part_l,
-          a.context_lens, cnt, a.Hq, G, HG, a.D, a.P, kmax);
-  } else if (a.bf16_out) {
-    (void)launch_kernel(K_DECODE_REDUCE, decode_reduce_kernel<uint16_t>, dim3(grid), dim3(64), st,
-        static_cast<uint16_t*>(a.out), a.part_o, a.part_m, a.part_l, a.context_lens, cnt, a.Hq, G,
-        HG, a.D, a.P, kmax);
-  } else {
-    (void)launch_kernel(K_DECODE_REDUCE, decode_reduce_kernel<float>, dim3(grid), dim3(64), st,
-        static_cast<float*>(a.out), a.part_o, a.part_m, a.part_l, a.context_lens, cnt, a.Hq, G, HG,
-        a.D, a.P, kmax);
+    return launch_kernel(K_DECODE_REDUCE, decode_reduce_wide_kernel<float>, dim3(grid),
+        dim3(256), st, static_cast<float*>(a.out), a.part_o, a.part_m, a.part_l,
+        a.context_lens, cnt, a.Hq, G, HG, a.D, a.P, kmax);
   }
-  e = hipGetLastError();
-  return e;
+  if (a.bf16_out)
+    return launch_kernel(K_DECODE_REDUCE, decode_reduce_kernel<uint16_t>, dim3(grid), dim3(64),
+        st, static_cast<uint16_t*>(a.out), a.part_o, a.part_m, a.part_l, a.context_lens, cnt,
+        a.Hq, G, HG, a.D, a.P, kmax);
+  return launch_kernel(K_DECODE_REDUCE, decode_reduce_kernel<float>, dim3(grid), dim3(64), st,
+      static_cast<float*>(a.out), a.part_o, a.part_m, a.part_l, a.context_lens, cnt, a.Hq, G, HG,
+      a.D, a.P, kmax);
 }
 
 // fp32 prefill runs on the same vector kernel: chunk row i of a sequence is a decode row whose
@@ -1339,29 +1322,23 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st);
 
 template <int D, int B, typename OutT>
-static void launch_prefill_f32_t(const PrefillArgs& a, hipStream_t st) {
+static hipError_t launch_prefill_f32_t(const PrefillArgs& a, hipStream_t st) {
   dim3 grid(a.total_q, a.Hq, 1);
-  (void)launch_kernel(K_PREFILL, attn_f32_kernel<D, B, false, true, OutT>, dim3(grid), dim3(64), st,
+  return launch_kernel(K_PREFILL, attn_f32_kernel<D, B, false, true, OutT>, dim3(grid), dim3(64), st,
       static_cast<OutT*>(a.out), nullptr, nullptr, nullptr, static_cast<const float*>(a.q),
       static_cast<const float*>(a.k_pool), static_cast<const float*>(a.v_pool), a.block_table,
       a.context_lens, a.cu_q_lens, a.S, a.Hq, a.Hkv, a.MB, 1 << 30, 1, a.scale * kLog2e);
 }
 
 template <int D, int B>
-static void prefill_f32_out(const PrefillArgs& a, hipStream_t st) {
-  if (a.bf16_out) launch_prefill_f32_t<D, B, uint16_t>(a, st);
-  else launch_prefill_f32_t<D, B, float>(a, st);
+static hipError_t prefill_f32_out(const PrefillArgs& a, hipStream_t st) {
+  return a.bf16_out ? launch_prefill_f32_t<D, B, uint16_t>(a, st)
+                    : launch_prefill_f32_t<D, B, float>(a, st);
 }
 
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st) {
-  if (a.D == 128) {
-    if (a.B == 16) prefill_f32_out<128, 16>(a, st);
-    else prefill_f32_out<128, 32>(a, st);
-  } else {
-    if (a.B == 16) prefill_f32_out<64, 16>(a, st);
-    else prefill_f32_out<64, 32>(a, st);
-  }
-  return hipGetLastError();
+  if (a.D == 128) return a.B == 16 ? prefill_f32_out<128, 16>(a, st) : prefill_f32_out<128, 32>(a, st);
+  return a.B == 16 ? prefill_f32_out<64, 16>(a, st) : prefill_f32_out<64, 32>(a, st);
 }
 
 }  // namespace pkv

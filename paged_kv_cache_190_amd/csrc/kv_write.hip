@@ -127,17 +127,16 @@ hipError_t launch_kv_write_fp8(const KvWriteArgs& a, int in_bf16, float k_scale,
   const dim3 grid((a.T + kWriteGroup - 1) / kWriteGroup, a.Hkv);
   const dim3 block(kWriteGroup * (a.D / 16));
   if (in_bf16) {
-    (void)launch_kernel(K_KV_WRITE, kv_write_fp8_kernel<uint16_t>, grid, block, stream,
+    return launch_kernel(K_KV_WRITE, kv_write_fp8_kernel<uint16_t>, grid, block, stream,
         static_cast<const uint16_t*>(a.k_new), static_cast<const uint16_t*>(a.v_new),
         static_cast<uint8_t*>(a.k_pool), static_cast<uint8_t*>(a.v_pool), a.slot_mapping, a.T,
         a.Hkv, a.D, a.B, k_scale, v_scale);
   } else {
-    (void)launch_kernel(K_KV_WRITE, kv_write_fp8_kernel<float>, grid, block, stream,
+    return launch_kernel(K_KV_WRITE, kv_write_fp8_kernel<float>, grid, block, stream,
         static_cast<const float*>(a.k_new), static_cast<const float*>(a.v_new),
         static_cast<uint8_t*>(a.k_pool), static_cast<uint8_t*>(a.v_pool), a.slot_mapping, a.T,
         a.Hkv, a.D, a.B, k_scale, v_scale);
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream) {
@@ -146,17 +145,16 @@ hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream) {
   const dim3 grid((a.T + kWriteGroup - 1) / kWriteGroup, a.Hkv);
   const dim3 block(kWriteGroup * (a.D / vec));
   if (a.elem_bytes == 2) {
-    (void)launch_kernel(K_KV_WRITE, kv_write_kernel<uint16_t>, grid, block, stream,
+    return launch_kernel(K_KV_WRITE, kv_write_kernel<uint16_t>, grid, block, stream,
         static_cast<const uint16_t*>(a.k_new), static_cast<const uint16_t*>(a.v_new),
         static_cast<uint16_t*>(a.k_pool), static_cast<uint16_t*>(a.v_pool), a.slot_mapping, a.T,
         a.Hkv, a.D, a.B);
   } else {
-    (void)launch_kernel(K_KV_WRITE, kv_write_kernel<float>, grid, block, stream,
+    return launch_kernel(K_KV_WRITE, kv_write_kernel<float>, grid, block, stream,
         static_cast<const float*>(a.k_new), static_cast<const float*>(a.v_new),
         static_cast<float*>(a.k_pool), static_cast<float*>(a.v_pool), a.slot_mapping, a.T, a.Hkv,
         a.D, a.B);
   }
-  return hipGetLastError();
 }
 
 }  // namespace pkv

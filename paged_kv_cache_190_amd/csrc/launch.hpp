@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <tuple>
+
 namespace pkv {
 
 // Kernel ids for the timing registry (api.cpp owns the registry).
@@ -29,14 +31,27 @@ struct TimingEvents {
 TimingEvents timing_events(int id);
 
 // Every kernel of the library is launched through here: hipExtLaunchKernel takes the timing
-// events with the dispatch itself, so timing adds no packets between kernels.
+// events with the dispatch itself, so timing adds no packets between kernels. The status is the
+// one this launch returned (a launch the runtime refuses, e.g. no code object for the device or
+// an invalid configuration); on failure the runtime's sticky copy of the error is cleared, since
+// the caller reports it.
 template <typename... KArgs, typename... Args>
 hipError_t launch_kernel(int id, void (*kernel)(KArgs...), dim3 grid, dim3 block,
                          hipStream_t stream, Args... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
   const TimingEvents ev = timing_events(id);
-  hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev.start, ev.stop, 0,
-                        static_cast<KArgs>(args)...);
-  return hipGetLastError();
+  std::tuple<KArgs...> vals{static_cast<KArgs>(args)...};
+  void* argv[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
+  std::apply(
+      [&argv](auto&... v) {
+        int i = 0;
+        ((argv[i++] = static_cast<void*>(&v)), ...);
+      },
+      vals);
+  const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block,
+                                          argv, 0, stream, ev.start, ev.stop, 0);
+  if (e != hipSuccess) (void)hipGetLastError();
+  return e;
 }
 
 struct KvWriteArgs {

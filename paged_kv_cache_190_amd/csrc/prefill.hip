@@ -377,14 +377,14 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
 // The kernel takes a positive scale (a negative one flips q; zero becomes a tiny positive value,
 // which keeps masked scores at -inf and gives the uniform softmax of a zero scale).
 template <int D, int B, typename OutT>
-static void launch_t(const PrefillArgs& a, hipStream_t st) {
+static hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   const int HW = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
   const int WGT = 32 * (kPrefillWaves / HW);
   const int n_tiles = (a.max_q_len + WGT - 1) / WGT;
   const int n_groups = G / HW;
   dim3 grid(n_tiles, a.Hkv * n_groups, a.S);
-  (void)launch_kernel(K_PREFILL, prefill_bf16_kernel<D, B, OutT>, dim3(grid),
+  return launch_kernel(K_PREFILL, prefill_bf16_kernel<D, B, OutT>, dim3(grid),
       dim3(64 * kPrefillWaves), st,
       static_cast<OutT*>(a.out), static_cast<const uint16_t*>(a.q), a.cu_q_lens, a.context_lens,
       static_cast<const uint16_t*>(a.k_pool), static_cast<const uint16_t*>(a.v_pool), a.block_table,
@@ -393,27 +393,16 @@ static void launch_t(const PrefillArgs& a, hipStream_t st) {
 }
 
 template <int D, int B>
-static void launch_out(const PrefillArgs& a, hipStream_t st) {
-  if (a.bf16_out) launch_t<D, B, uint16_t>(a, st);
-  else launch_t<D, B, float>(a, st);
+static hipError_t launch_out(const PrefillArgs& a, hipStream_t st) {
+  if (a.bf16_out) return launch_t<D, B, uint16_t>(a, st);
+  return launch_t<D, B, float>(a, st);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   if (a.total_q == 0 || a.max_q_len == 0) return hipSuccess;
-  hipError_t e;
-  if (!a.bf16_in) {
-    e = launch_prefill_f32(a, st);
-  } else {
-    if (a.D == 128) {
-      if (a.B == 16) launch_out<128, 16>(a, st);
-      else launch_out<128, 32>(a, st);
-    } else {
-      if (a.B == 16) launch_out<64, 16>(a, st);
-      else launch_out<64, 32>(a, st);
-    }
-    e = hipGetLastError();
-  }
-  return e;
+  if (!a.bf16_in) return launch_prefill_f32(a, st);
+  if (a.D == 128) return a.B == 16 ? launch_out<128, 16>(a, st) : launch_out<128, 32>(a, st);
+  return a.B == 16 ? launch_out<64, 16>(a, st) : launch_out<64, 32>(a, st);
 }
 
 }  // namespace pkv

@@ -55,7 +55,8 @@ class Dev:
     def write(self):
         bd.kv_cache_write(self.k_new, self.v_new, self.k_pool, self.v_pool, self.slots)
 
-    def decode(self, out_dtype=None, partition_size=0, max_context_len=None, out=None):
+    def decode(self, out_dtype=None, partition_size=0, max_context_len=None, out=None,
+               num_waves=0):
         import torch
         dt = self.q.dtype if out_dtype is None else out_dtype
         if out is None:
@@ -63,7 +64,7 @@ class Dev:
         mc = self.w.max_context_len if max_context_len is None else max_context_len
         bd.paged_attention_decode(out, self.q, self.k_pool, self.v_pool, self.bt, self.ctx,
                                   self.w.scale, max_context_len=mc,
-                                  partition_size=partition_size)
+                                  partition_size=partition_size, num_waves=num_waves)
         return out
 
     def prefill(self, out_dtype=None):

@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_strings():
     L = bd.lib()
-    assert L.pkv_abi_version() == 1
+    assert L.pkv_abi_version() == 2
     for st in range(6):
         assert L.pkv_status_string(st) != b"unknown status"
     assert L.pkv_status_string(99) == b"unknown status"
@@ -38,15 +38,15 @@ def test_version_and_strings():
 
 def _decode(**kw):
     args = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, ctx=FAKE, S=4, Hq=8, Hkv=8, D=64,
-                B=16, MB=8, NB=64, scale=0.125, max_ctx=0, P=0, ws=None, ws_bytes=0, dt=1,
-                odt=1, stream=None)
+                B=16, MB=8, NB=64, scale=0.125, max_ctx=0, P=0, nw=0, ws=None, ws_bytes=0,
+                dt=1, odt=1, stream=None)
     args.update(kw)
     a = args
     return bd.lib().pkv_paged_attention_decode(a["out"], a["q"], a["k"], a["v"], a["bt"],
                                                a["ctx"], a["S"], a["Hq"], a["Hkv"], a["D"],
                                                a["B"], a["MB"], a["NB"], a["scale"],
-                                               a["max_ctx"], a["P"], a["ws"], a["ws_bytes"],
-                                               a["dt"], a["odt"], a["stream"])
+                                               a["max_ctx"], a["P"], a["nw"], a["ws"],
+                                               a["ws_bytes"], a["dt"], a["odt"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -67,6 +67,8 @@ def _decode(**kw):
     (dict(P=16), bd.PKV_ERR_WORKSPACE),                      # 8 partitions need partials
     (dict(P=0), bd.PKV_ERR_WORKSPACE),                       # balanced split needs one too
     (dict(P=16, ws=FAKE, ws_bytes=10), bd.PKV_ERR_WORKSPACE),
+    (dict(nw=-1, ws=FAKE, ws_bytes=1 << 30), bd.PKV_ERR_INVALID_ARG),
+    (dict(nw=(1 << 20) + 1, ws=FAKE, ws_bytes=1 << 30), bd.PKV_ERR_INVALID_ARG),
     (dict(S=0, q=None), bd.PKV_OK),                          # empty batch: nothing to do
 ])
 def test_decode_validation(kw, status):
@@ -132,12 +134,12 @@ def test_fp8_decode_validation():
 
     def call(**kw):
         a = dict(S=4, Hq=32, Hkv=8, D=128, B=16, MB=8, NB=64, scale=0.088, ks=0.0625, vs=0.0625,
-                 mc=0, ws=None, wsb=0, odt=bd.PKV_BF16, q=FAKE)
+                 mc=0, nw=0, ws=None, wsb=0, odt=bd.PKV_BF16, q=FAKE)
         a.update(kw)
         return L.pkv_paged_attention_decode_fp8(
             FAKE, a["q"], FAKE, FAKE, FAKE, FAKE, a["S"], a["Hq"], a["Hkv"], a["D"], a["B"],
-            a["MB"], a["NB"], a["scale"], a["ks"], a["vs"], a["mc"], a["ws"], a["wsb"], a["odt"],
-            None)
+            a["MB"], a["NB"], a["scale"], a["ks"], a["vs"], a["mc"], a["nw"], a["ws"], a["wsb"],
+            a["odt"], None)
 
     assert call(S=0, q=None) == bd.PKV_OK
     assert call(q=None) == bd.PKV_ERR_INVALID_ARG
@@ -151,19 +153,20 @@ def test_fp8_decode_validation():
     need = L.pkv_decode_workspace_size(4, 32, 8, 128, 128, 0, bd.PKV_FP8_E4M3)
     assert need > 0
     assert call(ws=FAKE, wsb=need - 1) == bd.PKV_ERR_WORKSPACE
+    assert call(ws=FAKE, wsb=need, nw=-3) == bd.PKV_ERR_INVALID_ARG
 
 
 def test_shared_prefix_validation():
     L = bd.lib()
 
     def call(**kw):
-        a = dict(S=4, Hq=32, Hkv=8, D=128, B=16, MB=8, NB=64, ng=2, mgs=2, mpl=32, mc=0,
+        a = dict(S=4, Hq=32, Hkv=8, D=128, B=16, MB=8, NB=64, ng=2, mgs=2, mpl=32, mc=0, nw=0,
                  kvd=bd.PKV_BF16, ks=1.0, vs=1.0, ws=None, wsb=0, gs=FAKE, odt=bd.PKV_BF16)
         a.update(kw)
         return L.pkv_paged_attention_decode_shared_prefix(
             FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["gs"], FAKE, a["ng"], a["mgs"], a["mpl"], a["S"],
-            a["Hq"], a["Hkv"], a["D"], a["B"], a["MB"], a["NB"], 0.088, a["mc"], a["kvd"],
-            a["ks"], a["vs"], a["ws"], a["wsb"], a["odt"], None)
+            a["Hq"], a["Hkv"], a["D"], a["B"], a["MB"], a["NB"], 0.088, a["mc"], a["nw"],
+            a["kvd"], a["ks"], a["vs"], a["ws"], a["wsb"], a["odt"], None)
 
     assert call(S=0) == bd.PKV_OK
     assert call(gs=None) == bd.PKV_ERR_INVALID_ARG
@@ -179,6 +182,7 @@ def test_shared_prefix_validation():
     pre = L.pkv_decode_shared_prefix_workspace_size(4, 32, 8, 128, 128, 32, bd.PKV_BF16)
     assert pre > plain                                    # one more partial slot per row
     assert call(ws=FAKE, wsb=pre - 1) == bd.PKV_ERR_WORKSPACE
+    assert call(ws=FAKE, wsb=pre, nw=-1) == bd.PKV_ERR_INVALID_ARG
 
 
 def test_prefill_validation():
@@ -269,3 +273,45 @@ def test_binding_refuses_mismatched_dtypes():
     cu = torch.tensor([0, 1, 2], dtype=torch.int32)
     with pytest.raises(TypeError):
         bd.paged_attention_prefill_chunk(out, q, cu, ctx, k8, v8, bt, 0.1)
+
+
+def _no_gpu():
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="only meaningful where the HIP runtime has no device: "
+                    "these calls pass fake pointers that a real launch would dereference")
+def test_refused_launches_report_hip_errors():
+    """Every entry point that launches returns PKV_ERR_HIP, with the runtime's text, when the
+    runtime refuses the launch (here: no device at all). The arguments are valid, so validation
+    passes and the launch is attempted; a decode call stops after the first refused launch."""
+    L = bd.lib()
+    big = 1 << 30
+    calls = {
+        "kv_cache_write": lambda: L.pkv_kv_cache_write(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 8, 64, 16,
+                                                       4, 1, None),
+        "kv_cache_write_fp8": lambda: L.pkv_kv_cache_write_fp8(
+            FAKE, FAKE, FAKE, FAKE, FAKE, 3, 8, 128, 16, 10, bd.PKV_BF16, 0.5, 2.0, None),
+        "decode_balanced": lambda: _decode(ws=FAKE, ws_bytes=big),
+        "decode_fixed": lambda: _decode(P=16, ws=FAKE, ws_bytes=big),
+        "decode_fp8": lambda: L.pkv_paged_attention_decode_fp8(
+            FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 32, 8, 128, 16, 8, 64, 0.088, 0.0625, 0.0625,
+            0, 0, FAKE, big, bd.PKV_BF16, None),
+        "decode_shared_prefix": lambda: L.pkv_paged_attention_decode_shared_prefix(
+            FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 32, 4, 32, 8, 128, 16, 8, 64,
+            0.088, 0, 0, bd.PKV_BF16, 1.0, 1.0, FAKE, big, bd.PKV_BF16, None),
+        "write_and_decode": lambda: L.pkv_kv_cache_write_and_decode(
+            FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 32, 8, 128, 16, 8, 64, 0.088,
+            0, 0, FAKE, big, bd.PKV_BF16, None),
+        "prefill": lambda: L.pkv_paged_attention_prefill_chunk(
+            FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 10, 8, 2, 128, 16, 4, 9, 0.1, 0, 0, 1, 1,
+            None),
+        "prefill_f32": lambda: L.pkv_paged_attention_prefill_chunk(
+            FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 10, 8, 2, 128, 16, 4, 9, 0.1, 0, 0, 0, 0,
+            None),
+    }
+    for name, call in calls.items():
+        st = call()
+        assert st == bd.PKV_ERR_HIP, f"{name}: status {st} ({L.pkv_last_error()})"
+        assert L.pkv_last_error(), name

@@ -33,14 +33,14 @@ def _write(w, kp, vp):
                           w.k_scale, w.v_scale)
 
 
-def _decode(w, kp, vp, out_dtype, max_context_len=None):
+def _decode(w, kp, vp, out_dtype, max_context_len=None, num_waves=0):
     import torch
     td = torch.bfloat16 if out_dtype == "bf16" else torch.float32
     out = torch.full(w.q.shape, float("nan"), dtype=td, device="cuda")
     mc = w.max_context_len if max_context_len is None else max_context_len
     bd.paged_attention_decode_fp8(out, to_dev(w.q), kp, vp, to_dev(w.block_table),
                                   to_dev(w.context_lens), w.scale, w.k_scale, w.v_scale,
-                                  max_context_len=mc)
+                                  max_context_len=mc, num_waves=num_waves)
     return out
 
 
@@ -153,11 +153,10 @@ def test_decode_fp8_small(name, out_dtype):
 
 
 @pytest.mark.parametrize("waves", [1, 7, 333, 4096])
-def test_decode_fp8_wave_counts(waves, monkeypatch):
-    monkeypatch.setenv("PKV_DECODE_WAVES", str(waves))
+def test_decode_fp8_wave_counts(waves):
     w, kp, vp, ref = _case("g4_edges")
     tk, tv = to_dev(kp), to_dev(vp)
-    out = _decode(w, tk, tv, "f32")
+    out = _decode(w, tk, tv, "f32", num_waves=waves)
     assert_close(values(out), ref, TOL_BF16, f"decode_fp8 waves={waves}")
 
 

@@ -51,14 +51,13 @@ def _out(w, dtype="f32"):
 
 
 @pytest.mark.parametrize("waves", [0, 97, 3000])
-def test_decode_200_sequences(waves, monkeypatch):
-    if waves:
-        monkeypatch.setenv("PKV_DECODE_WAVES", str(waves))
+def test_decode_200_sequences(waves):
     w, kp, vp, ref = _plain("")
     log(f"decode 200 seqs, waves={waves or 'default'}")
     out = _out(w)
     bd.paged_attention_decode(out, to_dev(w.q), to_dev(kp), to_dev(vp), to_dev(w.block_table),
-                              to_dev(w.context_lens), w.scale, max_context_len=w.max_context_len)
+                              to_dev(w.context_lens), w.scale, max_context_len=w.max_context_len,
+                              num_waves=waves)
     assert_close(values(out), ref, TOL_BF16, f"decode 200 seqs waves={waves}")
 
 

@@ -349,25 +349,25 @@ def test_prefill_full_config5_sampled():
 
 
 @pytest.mark.parametrize("waves", [1, 2, 7, 64, 333, 4096])
-def test_decode_balanced_wave_counts(waves, monkeypatch):
+def test_decode_balanced_wave_counts(waves):
     """The balanced split deals the batch's 32-token tiles to `waves` waves; segments that
     waves share are merged by the reduce. Every wave count must give the oracle's result,
     including empty contexts between non-empty ones."""
-    monkeypatch.setenv("PKV_DECODE_WAVES", str(waves))
     w = wl.build_decode(120, 7, 32, 8, 128, 16, [700, 0, 1, 33, 2000, 0, 257], "bf16")
     kp, vp = _oracle_written(w)
     ref = orc.decode(w.q, kp, vp, w.block_table, w.context_lens, w.scale, "bf16")
     d = Dev(w)
     d.write()
     log(f"balanced decode, {waves} waves")
-    assert_close(values(d.decode(out_dtype=_torch_dtype("f32"))), ref, TOL_BF16,
+    assert_close(values(d.decode(out_dtype=_torch_dtype("f32"), num_waves=waves)), ref, TOL_BF16,
                  f"balanced split, {waves} waves")
     w2 = wl.build_decode(121, 3, 64, 4, 64, 32, [3000, 95, 1500], "bf16")  # G = 16, D = 64, B = 32
     kp, vp = _oracle_written(w2)
     ref2 = orc.decode(w2.q, kp, vp, w2.block_table, w2.context_lens, w2.scale, "bf16")
     d2 = Dev(w2)
     d2.write()
-    assert_close(values(d2.decode()), ref2, TOL_BF16, f"balanced split G=16, {waves} waves")
+    assert_close(values(d2.decode(num_waves=waves)), ref2, TOL_BF16,
+                 f"balanced split G=16, {waves} waves")
 
 
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 1.7])

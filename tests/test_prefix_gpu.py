@@ -36,7 +36,7 @@ def _oracle(w):
     return ref
 
 
-def _run(w, group_start, group_prefix_len, out_dtype="bf16"):
+def _run(w, group_start, group_prefix_len, out_dtype="bf16", num_waves=0):
     import torch
     tk, tv = to_dev(w.k_pool), to_dev(w.v_pool)
     kn, vn, sl = to_dev(w.k_new), to_dev(w.v_new), to_dev(w.slot_mapping)
@@ -51,7 +51,7 @@ def _run(w, group_start, group_prefix_len, out_dtype="bf16"):
     bd.paged_attention_decode_shared_prefix(
         out, to_dev(w.q), tk, tv, to_dev(w.block_table), to_dev(w.context_lens), to_dev(gs),
         to_dev(gp), w.scale, int(np.diff(gs).max()), int(gp.max()), k_scale=w.k_scale,
-        v_scale=w.v_scale, max_context_len=w.max_context_len)
+        v_scale=w.v_scale, max_context_len=w.max_context_len, num_waves=num_waves)
     return values(out)
 
 
@@ -95,10 +95,9 @@ def test_shared_prefix_without_sharing_equals_plain():
 
 
 @pytest.mark.parametrize("waves", [1, 7, 333])
-def test_shared_prefix_wave_counts(waves, monkeypatch):
-    monkeypatch.setenv("PKV_DECODE_WAVES", str(waves))
+def test_shared_prefix_wave_counts(waves):
     w, ref = _grouped("mixed")
-    got = _run(w, w.meta["group_start"], w.meta["group_prefix_len"], "f32")
+    got = _run(w, w.meta["group_start"], w.meta["group_prefix_len"], "f32", num_waves=waves)
     assert_close(got, ref, TOL_BF16, f"shared prefix waves={waves}")
 
 

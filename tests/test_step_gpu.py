@@ -47,7 +47,7 @@ def _ref(w):
     return kp, vp, orc.decode(w.q, kp, vp, w.block_table, w.context_lens, w.scale, "bf16")
 
 
-def _step(w, out_dtype="bf16", workspace=None, pools=None):
+def _step(w, out_dtype="bf16", workspace=None, pools=None, num_waves=0):
     import torch
     tk, tv = pools if pools is not None else (to_dev(w.k_pool), to_dev(w.v_pool))
     td = torch.bfloat16 if out_dtype == "bf16" else torch.float32
@@ -55,7 +55,8 @@ def _step(w, out_dtype="bf16", workspace=None, pools=None):
     bd.kv_cache_write_and_decode(out, to_dev(w.q), to_dev(w.k_new), to_dev(w.v_new),
                                  to_dev(w.slot_mapping), tk, tv, to_dev(w.block_table),
                                  to_dev(w.context_lens), w.scale,
-                                 max_context_len=max(w.max_context_len, 1), workspace=workspace)
+                                 max_context_len=max(w.max_context_len, 1), workspace=workspace,
+                                 num_waves=num_waves)
     return out, tk, tv
 
 
@@ -77,13 +78,12 @@ def test_step_small(name, out_dtype):
 
 
 @pytest.mark.parametrize("waves", [1, 7, 64, 333, 4096])
-def test_step_wave_counts(waves, monkeypatch):
+def test_step_wave_counts(waves):
     """Few waves (long pieces) and many (rows split into many merged pieces)."""
-    monkeypatch.setenv("PKV_DECODE_WAVES", str(waves))
     w, (kp, vp, ref) = _case("g8_b32")
     ws = _workspace(w)
     for rep in range(3):  # the same workspace, reused
-        out, tk, tv = _step(w, "f32", ws)
+        out, tk, tv = _step(w, "f32", ws, num_waves=waves)
         assert_close(values(out), ref, TOL_BF16, f"waves={waves} call {rep}")
 
 
