@@ -117,25 +117,29 @@ def prefill_bytes(w):
 
 # ---------------------------------------------------------------------------- device side
 
-def run_blocks(args):
+def block_sources(w, workload):
+    """Source blocks of a block-copy workload: each sequence's last block for cow-fork (the one
+    a forked child writes next), else every block of the first half of the sequences."""
+    import numpy as np
+    b = w.block_size
+    nblk = (w.context_lens.astype(np.int64) + b - 1) // b
+    if workload == "cow-fork":
+        return np.asarray([w.block_table[s, nblk[s] - 1] for s in range(w.num_seqs)], np.int32)
+    half = w.num_seqs // 2
+    return np.concatenate([w.block_table[s, :nblk[s]] for s in range(half)]).astype(np.int32)
+
+
+def run_blocks(args, w):
     """Time kv_cache_copy_blocks on the decode-8b pool (see BLOCK_WORKLOADS)."""
     import numpy as np
     import torch
 
     from paged_kv_cache_190_amd import binding as bd
-    from paged_kv_cache_190_amd import workloads as wl
 
-    w = wl.make_config(WORKLOADS["decode-8b"])
     dev = torch.device("cuda:0")
     k0, v0 = to_dev(w.k_pool), to_dev(w.v_pool)
     b = w.block_size
-    nblk = (w.context_lens.astype(np.int64) + b - 1) // b
-    if args.workload == "cow-fork":
-        # each sequence's last block (the one a forked child writes next) to a fresh block
-        src = np.asarray([w.block_table[s, nblk[s] - 1] for s in range(w.num_seqs)], np.int32)
-    else:
-        half = w.num_seqs // 2
-        src = np.concatenate([w.block_table[s, :nblk[s]] for s in range(half)]).astype(np.int32)
+    src = block_sources(w, args.workload)
     n = len(src)
     block_bytes = 2 * w.num_kv_heads * b * w.head_dim * 2  # K and V of one block, bf16
     host = args.workload in ("swap-out", "swap-in")
@@ -219,19 +223,18 @@ def run_blocks(args):
                               "algorithmic_bytes_per_launch": hbm}
         result.update(metric=f"{args.workload}: KV block copy HBM GB/s (read + write)",
                       value=round(hbm / (ms_per_step * 1e-3) / 1e9, 1), unit="GB/s")
-    result["_w"] = w
-    result["_pairs"] = pairs
     return result
 
 
-def cpu_baseline_blocks(w, pairs, budget_s):
-    """The oracle's block copy timed on the host, over growing prefixes of the same pairs."""
+def cpu_baseline_blocks(w, src, budget_s):
+    """The oracle's block copy timed on the host (one thread), over growing prefixes of the
+    same source blocks, copied into a host pool of their own."""
     import numpy as np
 
     from oracle import paged_attention as orc
-    dk = np.empty((len(pairs),) + w.k_pool.shape[1:], w.k_pool.dtype)
-    dv = np.empty((len(pairs),) + w.v_pool.shape[1:], w.v_pool.dtype)
-    local = np.stack([pairs[:, 0], np.arange(len(pairs), dtype=np.int32)], 1)
+    dk = np.empty((len(src),) + w.k_pool.shape[1:], w.k_pool.dtype)
+    dv = np.empty((len(src),) + w.v_pool.shape[1:], w.v_pool.dtype)
+    local = np.stack([src, np.arange(len(src), dtype=np.int32)], 1)
     t0 = time.perf_counter()
     done = 0
     while done < len(local) and time.perf_counter() - t0 < budget_s:
@@ -240,9 +243,9 @@ def cpu_baseline_blocks(w, pairs, budget_s):
     dt = time.perf_counter() - t0
     per = 2 * w.k_pool[0].nbytes
     return {"value": round(done * per / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"oracle block copy of {done} of {len(pairs)} blocks in calls of 256 "
-                      f"({dt:.2f} s, NumPy); bytes of the blocks copied / time"}
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"oracle block copy of {done} of {len(src)} blocks in calls of 256 "
+                      f"({dt:.2f} s, NumPy, one thread); bytes of the blocks copied / time"}
 
 def to_dev(a):
     import numpy as np
@@ -258,21 +261,36 @@ class Replica:
         self.v_pool = v_pool
 
 
-def run(args):
-    import numpy as np
-    import torch
-
-    from paged_kv_cache_190_amd import binding as bd
+def make_workload(args):
+    """The seeded synthetic inputs of --workload (host arrays; no GPU involved)."""
     from paged_kv_cache_190_amd import workloads as wl
-
+    if args.workload in BLOCK_WORKLOADS:
+        return wl.make_config(WORKLOADS["decode-8b"])
     cfg = WORKLOADS[args.workload]
     fp8 = args.workload.endswith("-fp8")
-    grouped = args.workload.startswith("shared-prefix-grouped")
-    fused = args.workload.endswith("-fused")
     tp = 8 if args.workload.endswith("-tp8") else 1
     w = wl.make_config(cfg, kv_dtype="fp8" if fp8 else "", tp=tp)
     log(f"workload {args.workload} ({wl.CONFIG_NAMES[cfg]}): S={w.num_seqs} "
         f"sum(n)={int(w.context_lens.sum())} NB={w.num_blocks}")
+    return w
+
+
+def _percentiles(us):
+    import numpy as np
+    a = np.asarray(us, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 2), "p10": round(float(np.percentile(a, 10)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2), "n": int(a.size)}
+
+
+def run(args, w):
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_190_amd import binding as bd
+
+    fp8 = args.workload.endswith("-fp8")
+    grouped = args.workload.startswith("shared-prefix-grouped")
+    fused = args.workload.endswith("-fused")
     dev = torch.device("cuda:0")
     q = to_dev(w.q)
     k_new, v_new = to_dev(w.k_new), to_dev(w.v_new)
@@ -301,12 +319,14 @@ def run(args):
         P_eff = 0 if (fp8 or grouped or fused) else bd.decode_partition_size(
             P, w.num_seqs, w.num_kv_heads, w.max_context_len, code)
 
+    nw = args.waves
+
     def step(i):
         r = reps[i % replicas]
         if fused:
             bd.kv_cache_write_and_decode(out, q, k_new, v_new, slots, r.k_pool, r.v_pool, bt, ctx,
                                          w.scale, max_context_len=w.max_context_len,
-                                         workspace=ws)
+                                         workspace=ws, num_waves=nw)
             return
         if grouped:
             if fp8:
@@ -317,19 +337,20 @@ def run(args):
             bd.paged_attention_decode_shared_prefix(
                 out, q, r.k_pool, r.v_pool, bt, ctx, gstart, gpre, w.scale, w.num_seqs,
                 w.prefix_tokens, k_scale=w.k_scale, v_scale=w.v_scale,
-                max_context_len=w.max_context_len, workspace=ws)
+                max_context_len=w.max_context_len, workspace=ws, num_waves=nw)
             return
         if fp8:
             bd.kv_cache_write_fp8(k_new, v_new, r.k_pool, r.v_pool, slots, w.k_scale, w.v_scale)
             bd.paged_attention_decode_fp8(out, q, r.k_pool, r.v_pool, bt, ctx, w.scale,
                                           w.k_scale, w.v_scale,
-                                          max_context_len=w.max_context_len, workspace=ws)
+                                          max_context_len=w.max_context_len, workspace=ws,
+                                          num_waves=nw)
             return
         bd.kv_cache_write(k_new, v_new, r.k_pool, r.v_pool, slots)
         if w.kind == "decode":
             bd.paged_attention_decode(out, q, r.k_pool, r.v_pool, bt, ctx, w.scale,
                                       max_context_len=w.max_context_len, partition_size=P,
-                                      workspace=ws)
+                                      workspace=ws, num_waves=nw)
         else:
             bd.paged_attention_prefill_chunk(out, q, cu, ctx, r.k_pool, r.v_pool, bt, w.scale,
                                              max_q_len=w.max_q_len,
@@ -370,11 +391,51 @@ def run(args):
         bd.profile_enable(False)
         return start.elapsed_time(stop) / args.steps, kern
 
-    # Pass 1 gives the throughput; pass 2 (same steps, kernels timed) the per-kernel durations.
+    def per_step(first):
+        """Each step between its own pair of torch events on the launch stream (median, p10,
+        p90 of the step times)."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(evs):
+            a.record()
+            step(first + i)
+            b.record()
+        torch.cuda.synchronize()
+        return _percentiles([1e3 * a.elapsed_time(b) for a, b in evs])
+
+    # Pass 1 gives the throughput; pass 2 (same steps, kernels timed) the per-kernel durations;
+    # pass 3 the distribution of single-step times.
     ms_per_step, _ = timed(args.warmup, False)
     ms_instr, kern = timed(args.warmup + args.steps, True)
+    step_dist = per_step(args.warmup + 2 * args.steps)
     log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step "
-        f"({ms_instr * 1e3:.1f} us/step with kernel timing); kernels: {kern}")
+        f"({ms_instr * 1e3:.1f} us/step with kernel timing); kernels: {kern}; "
+        f"single steps: {step_dist}")
+
+    probe = None
+    if (w.kind == "decode" and w.dtype == "bf16" and not (fp8 or grouped or fused)
+            and P == 0):
+        # The read probe: the decode's waves reading exactly its tiles without the arithmetic,
+        # over the same rotation of pool copies, timed the same way as the kernels above.
+        sink = torch.empty(bd.lib().pkv_decode_read_probe_sink_size(
+            w.num_seqs, w.num_q_heads, w.num_kv_heads, w.max_context_len, nw) // 4,
+            dtype=torch.int32, device=dev)
+        for i in range(args.warmup):
+            r = reps[i % replicas]
+            bd.decode_read_probe(r.k_pool, r.v_pool, bt, ctx, w.num_q_heads,
+                                 max_context_len=w.max_context_len, num_waves=nw, sink=sink)
+        bd.profile_enable(True, kernels=["read_probe"])
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            r = reps[i % replicas]
+            bd.decode_read_probe(r.k_pool, r.v_pool, bt, ctx, w.num_q_heads,
+                                 max_context_len=w.max_context_len, num_waves=nw, sink=sink)
+        torch.cuda.synchronize()
+        pms, pcnt = bd.profile_read("read_probe")
+        bd.profile_enable(False)
+        probe = {"avg_us": 1e3 * pms / pcnt, "launches": pcnt}
+        log(f"read probe: {probe['avg_us']:.1f} us per launch")
 
     result = {}
     if w.kind == "decode":
@@ -418,6 +479,22 @@ def run(args):
         if w.prefix_tokens:
             roof["logical_bytes_per_launch"] = logical_bytes
             roof["logical_achieved"] = round(logical_bytes / (dom_us * 1e-6) / 1e9, 1)
+        # The decode call as the method defines it: the partition kernel plus the merge (both
+        # event-timed per launch), over the call's algorithmic bytes (q, K/V, ids, out).
+        call_us = dom_us + kern.get("decode_reduce", {}).get("avg_us", 0.0)
+        call_bytes = dom_bytes if "decode_reduce" not in kern else dom_bytes + b["out"]
+        result["decode_call"] = {
+            "avg_us": round(call_us, 2), "achieved": round(call_bytes / (call_us * 1e-6) / 1e9, 1),
+            "frac": round(call_bytes / (call_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "kernels": [k for k in ("decode_partition", "decode_reduce") if k in kern]}
+        if probe is not None:
+            pgbs = dom_bytes / (probe["avg_us"] * 1e-6) / 1e9
+            result["read_probe"] = {
+                "avg_us": round(probe["avg_us"], 2), "achieved": round(pgbs, 1),
+                "frac_of_peak": round(pgbs / HBM_PEAK_GBS, 4),
+                "decode_pct_of_probe": round(100 * probe["avg_us"] / dom_us, 2),
+                "what": "the decode's waves reading exactly its K/V tiles with its loads, "
+                        "no attention arithmetic (pkv_decode_read_probe)"}
     else:
         flops = prefill_flops(w)
         dom = "prefill_chunk"
@@ -436,7 +513,7 @@ def run(args):
     result["roofline"] = roof
     result["ms_per_step"] = round(ms_per_step, 4)
     result["ms_per_step_kernel_timing_on"] = round(ms_instr, 4)
-    result["_w"] = w
+    result["step_us"] = step_dist
     return result
 
 
@@ -470,11 +547,83 @@ def kernel_sources_sha():
 
 # ------------------------------------------------------------------------------ CPU baseline
 
-def cpu_baseline(w, budget_s):
-    """The oracle, unchanged, timed on the host with BLAS limited to one thread, on the first
-    sequences of the same batch until about budget_s seconds of work; scaled to GB/s (decode)
-    or TFLOP/s (prefill) with the same algorithmic byte / flop counts as the GPU."""
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None where there is none)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def host_cores():
+    """Cores this process may use: its CPU affinity, capped by OMP_NUM_THREADS when that is set
+    (the share of the host a GPU job is given)."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    return max(1, min(n, int(env))) if env.isdigit() and int(env) > 0 else n
+
+
+# State shared with the oracle's worker processes: set before the pool forks, so each worker
+# sees the same arrays without copying them.
+_CPU = {}
+
+
+def _cpu_decode_worker(args):
+    """One worker of the all-cores leg: whole sequences of the batch (its share, in turn) until
+    the deadline; returns (KV bytes attended, sequences done, seconds)."""
     from threadpoolctl import threadpool_limits
+
+    from oracle import paged_attention as orc
+    widx, nworkers, deadline = args
+    w, kp, vp = _CPU["w"], _CPU["kp"], _CPU["vp"]
+    per_tok = 2 * w.num_kv_heads * w.head_dim * _pool_esz(w)
+    work = done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        s = widx
+        while time.time() < deadline:
+            sq = s % w.num_seqs
+            orc.decode(w.q[sq:sq + 1], kp, vp, w.block_table[sq:sq + 1],
+                       w.context_lens[sq:sq + 1], w.scale, w.dtype,
+                       kv_dtype=w.kv_dtype or None, k_scale=w.k_scale, v_scale=w.v_scale)
+            work += int(w.context_lens[sq]) * per_tok
+            done += 1
+            s += nworkers
+    return work, done, time.perf_counter() - t0
+
+
+def _cpu_prefill_worker(args):
+    """All-cores leg of the prefill: this worker's share of the shuffled (row, head) outputs
+    until the deadline; returns (flops, outputs done, seconds)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import paged_attention as orc
+    widx, nworkers, deadline = args
+    w, kp, vp, rows, pos = _CPU["w"], _CPU["kp"], _CPU["vp"], _CPU["rows"], _CPU["pos"]
+    flops = done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        for t, h in rows[widx::nworkers]:
+            if time.time() >= deadline:
+                break
+            orc.prefill_chunk(w.q, w.cu_q_lens, w.context_lens, kp, vp, w.block_table, w.scale,
+                              w.dtype, rows=[(t, h)])
+            flops += 4 * w.head_dim * pos[t]
+            done += 1
+    return flops, done, time.perf_counter() - t0
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle, unchanged, timed on the host on a bounded sample of the same batch, twice:
+    with BLAS limited to one thread (one core), and as a pool of single-threaded worker processes
+    over the host's cores (all cores), each for about budget_s seconds. Scaled to GB/s (decode)
+    or TFLOP/s (prefill) with the GPU's algorithmic byte / flop counts. Runs before the process
+    touches the GPU, so the pool forks a process with no GPU state."""
+    import multiprocessing as mp
+    import random
 
     from oracle import paged_attention as orc
     if w.pool_dtype == "fp8":
@@ -483,47 +632,43 @@ def cpu_baseline(w, budget_s):
     else:
         kp, vp = orc.kv_cache_write(w.k_pool, w.v_pool, w.k_new, w.v_new, w.slot_mapping,
                                     w.block_size)
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        done = 0
-        if w.kind == "decode":
-            work = 0
-            per_tok = 2 * w.num_kv_heads * w.head_dim * _pool_esz(w)
-            # whole passes over the batch (sequence by sequence) until the budget is spent
-            while time.perf_counter() - t0 < budget_s:
-                s = done % w.num_seqs
-                orc.decode(w.q[s:s + 1], kp, vp, w.block_table[s:s + 1],
-                           w.context_lens[s:s + 1], w.scale, w.dtype,
-                           kv_dtype=w.kv_dtype or None, k_scale=w.k_scale, v_scale=w.v_scale)
-                work += int(w.context_lens[s]) * per_tok
-                done += 1
-            dt = time.perf_counter() - t0
-            return {"value": round(work / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-                    "kind": "oracle",
-                    "sample": f"oracle decode of {done} sequences ({done / w.num_seqs:.1f} passes "
-                              f"over the {w.num_seqs}-sequence batch, all {w.num_q_heads} query "
-                              f"heads; {dt:.1f} s; float64 NumPy, BLAS limited to 1 thread); "
-                              f"KV bytes of the sample / time"}
-        rows, flops = [], 0
-        rng_rows = [(t, h) for t in range(w.total_q) for h in range(w.num_q_heads)]
-        import random
-        random.Random(0).shuffle(rng_rows)
+    _CPU.update(w=w, kp=kp, vp=vp)
+    cores = host_cores()
+    model = cpu_model()
+    if w.kind == "decode":
+        one = _cpu_decode_worker((0, 1, time.time() + budget_s))
+        unit, scale = "GB/s", 1e9
+        what = (f"oracle decode of whole sequences, all {w.num_q_heads} query heads, passes over "
+                f"the {w.num_seqs}-sequence batch (float64 NumPy); KV bytes of the sample / time")
+    else:
+        rows = [(t, h) for t in range(w.total_q) for h in range(w.num_q_heads)]
+        random.Random(0).shuffle(rows)
         pos = {}
         for s in range(w.num_seqs):
             for t in range(int(w.cu_q_lens[s]), int(w.cu_q_lens[s + 1])):
                 pos[t] = int(w.context_lens[s]) - int(w.cu_q_lens[s + 1]) + t + 1
-        for t, h in rng_rows:
-            if time.perf_counter() - t0 >= budget_s:
-                break
-            orc.prefill_chunk(w.q, w.cu_q_lens, w.context_lens, kp, vp, w.block_table, w.scale,
-                              w.dtype, rows=[(t, h)])
-            flops += 4 * w.head_dim * pos[t]
-            done += 1
-        dt = time.perf_counter() - t0
-        return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
-                "kind": "oracle",
-                "sample": f"oracle prefill of {done} random (row, head) outputs ({dt:.1f} s; "
-                          f"float64 NumPy, BLAS limited to 1 thread)"}
+        _CPU.update(rows=rows, pos=pos)
+        one = _cpu_prefill_worker((0, 1, time.time() + budget_s))
+        unit, scale = "TFLOP/s", 1e12
+        what = ("oracle prefill of random (row, head) outputs, one at a time (float64 NumPy); "
+                "flops of the sample / time")
+    t0 = time.perf_counter()
+    ctx = mp.get_context("fork")
+    worker = _cpu_decode_worker if w.kind == "decode" else _cpu_prefill_worker
+    deadline = time.time() + budget_s
+    with ctx.Pool(cores) as pool:
+        parts = pool.map(worker, [(i, cores, deadline) for i in range(cores)])
+    wall = time.perf_counter() - t0
+    all_work = sum(p[0] for p in parts)
+    all_done = sum(p[1] for p in parts)
+    digits = 4 if unit == "GB/s" else 6
+    return {"value": round(all_work / wall / scale, digits), "unit": unit, "cores": cores,
+            "kind": "oracle", "cpu_model": model,
+            "sample": f"{what}; all cores: {cores} single-threaded processes, {all_done} items in "
+                      f"{wall:.1f} s",
+            "one_core": {"value": round(one[0] / one[2] / scale, digits), "unit": unit,
+                         "cores": 1, "sample": f"{one[1]} items in {one[2]:.1f} s, BLAS "
+                                               f"limited to one thread"}}
 
 
 # ------------------------------------------------------------------- rocprofv3 summaries
@@ -667,7 +812,9 @@ def main():
     ap.add_argument("--replicas", type=int, default=0,
                     help="pool copies the steps rotate over (0: enough for 2 GB)")
     ap.add_argument("--partition-size", type=int, default=0)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--waves", type=int, default=0,
+                    help="waves of the balanced decode split (0: the library's default)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a 256 MiB device copy first (scale for rocprofv3 byte counters)")
@@ -696,15 +843,23 @@ def main():
               "multi-GPU runs are out of scope here)", file=sys.stderr)
         sys.exit(2)
 
+    # Inputs and the CPU baseline first: the oracle's worker pool forks before this process
+    # touches the GPU.
+    from paged_kv_cache_190_amd.workloads import CONFIG_NAMES
+    blocks = args.workload in BLOCK_WORKLOADS
+    w = make_workload(args)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host ...")
+        cpu = (cpu_baseline_blocks(w, block_sources(w, args.workload), args.cpu_seconds)
+               if blocks else cpu_baseline(w, args.cpu_seconds))
+        log(f"oracle: {cpu}")
+
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    from paged_kv_cache_190_amd.workloads import CONFIG_NAMES
-    blocks = args.workload in BLOCK_WORKLOADS
-    res = run_blocks(args) if blocks else run(args)
-    w = res.pop("_w")
-    pairs = res.pop("_pairs", None)
+    res = run_blocks(args, w) if blocks else run(args, w)
     base = "decode-8b" if blocks else args.workload
     desc = CONFIG_NAMES[WORKLOADS[base]]
     if args.workload.endswith("-tp8"):
@@ -713,6 +868,8 @@ def main():
            "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
            "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
            "sum_context_tokens": int(w.context_lens.sum()), "seed": WORKLOADS[base]}
+    if args.waves:
+        cfg["num_waves"] = args.waves
     line = {"metric": res.pop("metric"), "value": res.pop("value"), "unit": res.pop("unit"),
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": res.pop("ms_per_step"), "higher_is_better": True, "scaling": "weak",
@@ -720,12 +877,7 @@ def main():
     if w.kv_dtype:
         line["kv_dtype"] = w.kv_dtype
     line["roofline"] = res.pop("roofline")
-    if args.no_cpu_baseline:
-        line["cpu_baseline"] = None
-    else:
-        log("timing the oracle on the host ...")
-        line["cpu_baseline"] = (cpu_baseline_blocks(w, pairs, args.cpu_seconds) if blocks
-                                else cpu_baseline(w, args.cpu_seconds))
+    line["cpu_baseline"] = cpu
     line.update(res)
     print(json.dumps(line), flush=True)
 

@@ -377,6 +377,24 @@ int pkv_paged_attention_prefill_chunk(void* out, const void* q, const int32_t* c
                                       int out_dtype, void* stream);
 
 /*
+ * pkv_decode_read_probe -- measurement only, not part of the attention path. Launches the
+ * balanced split of pkv_paged_attention_decode (bf16 pools, the same num_waves rule) with the
+ * same waves reading the same K/V tiles with the same loads, but without the attention
+ * arithmetic: each lane folds the words it loaded into one XOR and stores it to sink. The
+ * decode's time over this probe's, on the same arguments, is how close the decode comes to a
+ * bare read of exactly the bytes it must read [Shootout 1.1: decode is bound by memory
+ * bandwidth]. Arguments as for pkv_paged_attention_decode; sink: device buffer of at least
+ * pkv_decode_read_probe_sink_size(...) bytes (contents written are meaningless).
+ */
+size_t pkv_decode_read_probe_sink_size(int num_seqs, int num_q_heads, int num_kv_heads,
+                                       int max_context_len, int num_waves);
+int pkv_decode_read_probe(const void* k_pool, const void* v_pool, const int32_t* block_table,
+                          const int32_t* context_lens, int num_seqs, int num_q_heads,
+                          int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                          int num_blocks, int max_context_len, int num_waves, void* sink,
+                          size_t sink_bytes, void* stream);
+
+/*
  * Kernel timing (library plumbing, for benchmarks). For every kernel selected by the mask, the
  * library passes a pair of HIP events to the kernel launch itself (hipExtLaunchKernel), so the
  * events bracket exactly that kernel on the stream it runs on and add nothing between kernels;

@@ -258,7 +258,11 @@ def prefill_chunk(q, cu_q_lens, context_lens, k_pool, v_pool, block_table, scale
     [Serving Engines, "How vLLM works"]: chunked prefill runs a slice of a prompt. Reading:
     sequence s holds n = context_lens[s] tokens, the last c = cu[s+1] - cu[s] of which are this
     chunk; chunk row i is at position r + i (r = n - c) and attends to keys 0 .. r + i.
-    `rows`, if given, is a list of (token_row, head) pairs: only those are computed.
+    Without `rows`, each (sequence, head) is the textbook masked attention of the whole chunk:
+    scores of every chunk row against every key, the causal mask (key j kept for row i iff
+    j <= r + i, aligned to the end of the context), a row-wise softmax, then the product with V.
+    `rows`, if given, is a list of (token_row, head) pairs: only those are computed, one row at
+    a time over its visible keys.
     """
     tq, hq, d = q.shape
     hkv, b = k_pool.shape[1], k_pool.shape[2]
@@ -276,6 +280,14 @@ def prefill_chunk(q, cu_q_lens, context_lens, k_pool, v_pool, block_table, scale
         if wanted is not None and not any(lo <= t < hi for t, _ in wanted):
             continue
         k, v = gather(k_pool, v_pool, block_table[s], n, b, dtype)
+        if wanted is None:
+            keep = np.arange(n)[None, :] <= (r + np.arange(c))[:, None]  # [c][n] causal mask
+            for h in range(hq):
+                g = h // group
+                a = np.where(keep, scale * (qf[lo:hi, h] @ k[g].T), -np.inf)
+                p = np.exp(a - a.max(axis=1, keepdims=True))
+                out[lo:hi, h] = (p @ v[g]) / p.sum(axis=1, keepdims=True)
+            continue
         for i in range(c):
             for h in range(hq):
                 if wanted is not None and (lo + i, h) not in wanted:

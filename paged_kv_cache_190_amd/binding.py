@@ -57,6 +57,11 @@ def lib() -> ctypes.CDLL:
     L.pkv_paged_attention_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                                     i32, i32, i32, i32, i32, f32, i32, i32, i32,
                                                     i32, vp]
+    L.pkv_decode_read_probe_sink_size.restype = sz
+    L.pkv_decode_read_probe_sink_size.argtypes = [i32, i32, i32, i32, i32]
+    L.pkv_decode_read_probe.restype = i32
+    L.pkv_decode_read_probe.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                        i32, vp, sz, vp]
     L.pkv_profile_enable.restype = i32
     L.pkv_profile_enable.argtypes = [i32]
     L.pkv_profile_reset.restype = i32
@@ -407,6 +412,29 @@ def kv_cache_copy_blocks(src_k, src_v, dst_k, dst_v, block_pairs, stream=None) -
         nbs, nbd, _pool_code(src_k), _stream(stream)), "kv_cache_copy_blocks")
 
 
+def decode_read_probe(k_pool, v_pool, block_table, context_lens, num_q_heads,
+                      max_context_len=0, num_waves=0, sink=None, stream=None):
+    """Measurement only: the balanced decode's waves read exactly the decode's K/V tiles (bf16
+    pools) without the attention arithmetic. Returns the sink tensor it wrote."""
+    import torch
+    nb, hkv, b, d = k_pool.shape
+    S = context_lens.shape[0]
+    if v_pool.shape != (nb, hkv, d, b) or block_table.dim() != 2 or block_table.shape[0] != S:
+        raise ValueError("inconsistent shapes")
+    _bf16("k_pool and v_pool", k_pool, v_pool)
+    mb = block_table.shape[1]
+    ctx = max_context_len if max_context_len else mb * b
+    need = lib().pkv_decode_read_probe_sink_size(S, num_q_heads, hkv, ctx, int(num_waves))
+    if sink is None:
+        sink = torch.empty(max(need // 4, 1), dtype=torch.int32, device=k_pool.device)
+    _check(lib().pkv_decode_read_probe(
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _i32(block_table, "block_table"),
+        _i32(context_lens, "context_lens"), S, num_q_heads, hkv, d, b, mb, nb,
+        int(max_context_len), int(num_waves), _dev(sink, "sink"),
+        sink.numel() * sink.element_size(), _stream(stream)), "decode_read_probe")
+    return sink
+
+
 # ------------------------------------------------------------------------------ block manager
 
 class BlockManager:
@@ -478,7 +506,7 @@ class BlockManager:
 # ------------------------------------------------------------------------------ timing
 
 KERNEL_NAMES = ("kv_cache_write", "decode_partition", "decode_reduce", "prefill_chunk",
-                "copy_blocks")
+                "copy_blocks", "read_probe")
 
 
 def profile_enable(on: bool = True, kernels=None) -> None:

@@ -95,6 +95,7 @@ const char* kernel_name(int id) {
     case K_DECODE_REDUCE: return "decode_reduce";
     case K_PREFILL: return "prefill_chunk";
     case K_COPY_BLOCKS: return "copy_blocks";
+    case K_READ_PROBE: return "read_probe";
     default: return "?";
   }
 }
@@ -591,6 +592,56 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_pool, con
                     "paged_attention_decode");
 }
 
+}  // extern "C"
+
+namespace {
+// The probe launches whole workgroups of kBalancedWavesPerGroup waves, and every launched wave
+// may store its 64 words.
+size_t probe_sink_bytes(int waves) {
+  const size_t per = pkv::kBalancedWavesPerGroup;
+  const size_t launched = (static_cast<size_t>(waves) + per - 1) / per * per;
+  return launched * 64 * sizeof(uint32_t);
+}
+}  // namespace
+
+extern "C" {
+
+size_t pkv_decode_read_probe_sink_size(int num_seqs, int num_q_heads, int num_kv_heads,
+                                       int max_context_len, int num_waves) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || num_waves < 0 || num_waves > kMaxDecodeWaves)
+    return 0;
+  const BalancedPlan pl = balanced_plan(num_seqs, num_q_heads, num_kv_heads, 64,
+                                        max_context_len,
+                                        num_waves > 0 ? num_waves : kDefaultDecodeWaves);
+  return probe_sink_bytes(pl.waves);
+}
+
+int pkv_decode_read_probe(const void* k_pool, const void* v_pool, const int32_t* block_table,
+                          const int32_t* context_lens, int num_seqs, int num_q_heads,
+                          int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                          int num_blocks, int max_context_len, int num_waves, void* sink,
+                          size_t sink_bytes, void* stream) {
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs = %d is negative", num_seqs);
+  if (num_seqs == 0) return PKV_OK;
+  pkv::DecodeArgs a{};
+  int st = check_decode(a, sink, sink, k_pool, v_pool, block_table, context_lens, num_seqs,
+                        num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                        num_blocks, 1.0f, max_context_len, PKV_BF16, PKV_BF16);
+  if (st != PKV_OK) return st;
+  if (num_waves < 0 || num_waves > kMaxDecodeWaves)
+    return fail(PKV_ERR_INVALID_ARG, "num_waves %d outside [0, %d]", num_waves, kMaxDecodeWaves);
+  const BalancedPlan pl = balanced_plan(a.S, a.Hq, a.Hkv, a.D, a.max_ctx,
+                                        num_waves > 0 ? num_waves : kDefaultDecodeWaves);
+  const size_t need = probe_sink_bytes(pl.waves);
+  if (!sink || sink_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "sink of %zu bytes needed, %zu given", need, sink_bytes);
+  pkv::ReadProbeArgs r{static_cast<uint32_t*>(sink), k_pool, v_pool, block_table, context_lens,
+                       a.S, a.Hq, a.Hkv, a.D, a.B, a.MB, pl.waves, kMinTilesPerWave};
+  return hip_status(pkv::launch_read_probe(r, static_cast<hipStream_t>(stream)),
+                    "decode_read_probe");
+}
+
 int pkv_paged_attention_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
                                       const int32_t* context_lens, const void* k_pool,
                                       const void* v_pool, const int32_t* block_table,
@@ -681,7 +732,7 @@ int pkv_profile_read(const char* kernel_name, double* total_ms, long long* launc
 }
 
 const char* pkv_profile_kernel_names(void) {
-  return "kv_cache_write,decode_partition,decode_reduce,prefill_chunk,copy_blocks";
+  return "kv_cache_write,decode_partition,decode_reduce,prefill_chunk,copy_blocks,read_probe";
 }
 
 }  // extern "C"

@@ -302,6 +302,50 @@ __device__ __forceinline__ void attend_tiles2(WaveAttn<D> (&st)[2],
   }
 }
 
+// Read probe (measurement only): the tiles attend_tiles would read for the same arguments,
+// loaded by the same lanes through the same two-register-set pipeline, with the attention
+// arithmetic replaced by an XOR of the loaded words (so no load can be dropped). Its time
+// against the decode's separates the cost of reading the tile list from the cost of the math.
+template <int D, int B>
+__device__ __forceinline__ uint32_t probe_tiles(const uint16_t* __restrict__ kpool,
+                                                const uint16_t* __restrict__ vpool,
+                                                const int32_t* __restrict__ bt, int n, int g,
+                                                int Hkv, int tok_begin, int tok_end) {
+  const int ntiles = (tok_end - tok_begin + 31) >> 5;
+  TileWalk<D, B> wk(kpool, vpool, n, g, Hkv, tok_begin);
+  uint32_t acc = 0;
+  auto fold = [&](const KvTile<D, B>& T) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) acc ^= T.k[hf][kk][0] ^ T.k[hf][kk][1] ^
+                                                 T.k[hf][kk][2] ^ T.k[hf][kk][3];
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) acc ^= T.v[dt][0] ^ T.v[dt][1] ^ T.v[dt][2] ^ T.v[dt][3];
+  };
+  KvTile<D, B> ta, tb;
+  for (int c0 = 0; c0 < ntiles; c0 += TileWalk<D, B>::kChunkTiles) {
+    const int c1 = min(ntiles, c0 + TileWalk<D, B>::kChunkTiles);
+    wk.begin_chunk(bt, c0);
+    wk.load(ta, c0);
+    int t = c0;
+    for (; t + 2 < c1; t += 2) {
+      wk.load(tb, t + 1);
+      fold(ta);
+      wk.load(ta, t + 2);
+      fold(tb);
+    }
+    if (t + 1 < c1) {
+      wk.load(tb, t + 1);
+      fold(ta);
+      fold(tb);
+    } else {
+      fold(ta);
+    }
+  }
+  return acc;
+}
+
 // ----------------------------------------------------------------------------- E4M3 pools
 
 template <int D, int B>
@@ -644,16 +688,18 @@ struct StepInfo {
 // With PREFIX, a sequence's tiles start after its group's prefix, partial slots after the prefix
 // chunks' (KSTRIDE slots per row in all), and a segment with prefix chunks is never final.
 // With STEP (bf16 only), the new tokens are handled as described at StepInfo.
-template <int D, int B, typename OutT, typename KvT, bool PREFIX, bool STEP = false>
+template <int D, int B, typename OutT, typename KvT, bool PREFIX, bool STEP = false,
+          bool PROBE = false>
 __device__ __forceinline__ void balanced_body(
     int w, int W, OutT* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_m,
     float* __restrict__ part_l, int32_t* __restrict__ seg_count, const uint16_t* __restrict__ q,
     const KvT* __restrict__ kpool, const KvT* __restrict__ vpool,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ context_lens, int S,
     int Hq, int Hkv, int G, int HG, int MB, int KSTRIDE, int min_tiles, float scale_log2,
-    float out_scale, PrefixInfo pf, StepInfo sp = StepInfo{}) {
+    float out_scale, PrefixInfo pf, StepInfo sp = StepInfo{}, uint32_t* probe_sink = nullptr) {
   constexpr bool kFp8 = sizeof(KvT) == 1;
   static_assert(!STEP || (!PREFIX && !kFp8), "the fused step is built for plain bf16 decode");
+  static_assert(!PROBE || (!PREFIX && !STEP && !kFp8), "the read probe walks plain bf16 decode");
   const int lane = threadIdx.x & 63;
   const int lg = lane >> 4;
   const int segs = Hkv * HG;
@@ -670,7 +716,7 @@ __device__ __forceinline__ void balanced_body(
   // wave that owns tile x: the largest w with floor(w*T/Weff) <= x
   auto wave_of = [&](int64_t x) -> int64_t { return (x * Weff + Weff - 1) / T; };
 
-  if (w == 0) {  // partial counts per segment, for the reduce
+  if (!PROBE && w == 0) {  // partial counts per segment, for the reduce
     int64_t cum = 0;
     for (int base = 0; base < S; base += 64) {
       const int s = base + lane;
@@ -721,6 +767,7 @@ __device__ __forceinline__ void balanced_body(
   int ts = (n - pre + 31) >> 5;
   int j = static_cast<int>((x0 - sstart) / ts);
   int64_t x = x0;
+  uint32_t probe_acc = 0;
   while (x < x1) {
     const int64_t a = sstart + static_cast<int64_t>(j) * ts;  // first tile of segment (s, j)
     const int t_begin = static_cast<int>(x - a);
@@ -737,7 +784,9 @@ __device__ __forceinline__ void balanced_body(
     const int32_t* bt = block_table + static_cast<int64_t>(s) * MB;
     const int tb = pre + 32 * t_begin;
     const int te = min(pre + 32 * t_end, n);
-    if constexpr (kFp8) {
+    if constexpr (PROBE) {
+      probe_acc ^= probe_tiles<D, B>(kpool, vpool, bt, n, g, Hkv, tb, te);
+    } else if constexpr (kFp8) {
       load_q_fp8<D>(qf, q + row * D, hvalid, lg);
       // the prefix kernel is held to 256 VGPRs: two register sets there
       attend_tiles_fp8<D, B, PREFIX ? 2 : 3>(st, qf, kpool, vpool, bt, n, g, Hkv, tb, te,
@@ -770,7 +819,7 @@ __device__ __forceinline__ void balanced_body(
     const int64_t wl = wave_of(a + ts - 1);
     const int pc = PREFIX ? (pre + kPrefixChunk - 1) / kPrefixChunk : 0;
     const float osc = kFp8 ? out_scale : 1.0f;
-    if (hvalid) {
+    if (!PROBE && hvalid) {
       if (pc == 0 && wf == wl) write_final<D>(out + row * D, st, l_total, lg, osc);
       else if (pc + (w - wf) < KSTRIDE)  // always true when context_lens respect max_context_len
         write_partial<D>(part_o, part_m, part_l, row * KSTRIDE + pc + (w - wf), st, l_total, lg,
@@ -789,12 +838,12 @@ __device__ __forceinline__ void balanced_body(
       if (s >= S) break;
     }
   }
+  if constexpr (PROBE) probe_sink[static_cast<int64_t>(w) * 64 + lane] = probe_acc;
 }
 
 // KvT: uint16_t for bf16 pools, uint8_t for E4M3 pools (out_scale = the V scale).
-// Four waves per workgroup, one per SIMD of a compute unit (a quarter of the workgroup
-// dispatches of one wave per workgroup).
-constexpr int kBalancedWavesPerGroup = 4;
+// kBalancedWavesPerGroup (launch.hpp): four waves per workgroup, one per SIMD of a compute unit
+// (a quarter of the workgroup dispatches of one wave per workgroup).
 template <int D, int B, typename OutT, typename KvT>
 __global__ __launch_bounds__(64 * kBalancedWavesPerGroup) void decode_balanced_kernel(
     OutT* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_m,
@@ -826,6 +875,21 @@ __global__ __launch_bounds__(64 * kBalancedWavesPerGroup) void decode_step_kerne
       gridDim.x * kBalancedWavesPerGroup, out, part_o, part_m, part_l, seg_count, q, kpool, vpool,
       block_table, context_lens, S, Hq, Hkv, G, HG, MB, KMAX, min_tiles, scale_log2, 1.0f,
       PrefixInfo{nullptr, nullptr, 0}, StepInfo{k_new, v_new, slots, kpool, vpool});
+}
+
+// Read probe kernel: the balanced decode's launch shape and tile walk (see probe_tiles); each
+// lane leaves its XOR in sink[wave][lane].
+template <int D, int B>
+__global__ __launch_bounds__(64 * kBalancedWavesPerGroup) void decode_read_probe_kernel(
+    uint32_t* __restrict__ sink, const uint16_t* __restrict__ kpool,
+    const uint16_t* __restrict__ vpool, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ context_lens, int S, int Hq, int Hkv, int G, int HG, int MB,
+    int min_tiles) {
+  balanced_body<D, B, float, uint16_t, false, false, true>(
+      blockIdx.x * kBalancedWavesPerGroup + (threadIdx.x >> 6),
+      gridDim.x * kBalancedWavesPerGroup, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+      kpool, vpool, block_table, context_lens, S, Hq, Hkv, G, HG, MB, 0, min_tiles, 0.f, 1.0f,
+      PrefixInfo{nullptr, nullptr, 0}, StepInfo{}, sink);
 }
 
 // One prefix unit (see PrefixInfo). Units are numbered (group, KV head, chunk, column tile),
@@ -1315,6 +1379,23 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   return launch_kernel(K_DECODE_REDUCE, decode_reduce_kernel<float>, dim3(grid), dim3(64), st,
       static_cast<float*>(a.out), a.part_o, a.part_m, a.part_l, a.context_lens, cnt, a.Hq, G, HG,
       a.D, a.P, kmax);
+}
+
+template <int D, int B>
+static hipError_t launch_probe_t(const ReadProbeArgs& a, hipStream_t st) {
+  const int G = a.Hq / a.Hkv;
+  const int HG = (G + 15) / 16;
+  return launch_kernel(K_READ_PROBE, decode_read_probe_kernel<D, B>,
+                       dim3((a.waves + kBalancedWavesPerGroup - 1) / kBalancedWavesPerGroup),
+                       dim3(64 * kBalancedWavesPerGroup), st, a.sink,
+                       static_cast<const uint16_t*>(a.k_pool),
+                       static_cast<const uint16_t*>(a.v_pool), a.block_table, a.context_lens, a.S,
+                       a.Hq, a.Hkv, G, HG, a.MB, a.min_tiles);
+}
+
+hipError_t launch_read_probe(const ReadProbeArgs& a, hipStream_t st) {
+  if (a.D == 128) return a.B == 16 ? launch_probe_t<128, 16>(a, st) : launch_probe_t<128, 32>(a, st);
+  return a.B == 16 ? launch_probe_t<64, 16>(a, st) : launch_probe_t<64, 32>(a, st);
 }
 
 // fp32 prefill runs on the same vector kernel: chunk row i of a sequence is a decode row whose

@@ -18,7 +18,8 @@ enum KernelId {
   K_DECODE_REDUCE = 2,
   K_PREFILL = 3,
   K_COPY_BLOCKS = 4,
-  K_COUNT = 5
+  K_READ_PROBE = 5,
+  K_COUNT = 6
 };
 const char* kernel_name(int id);
 
@@ -124,7 +125,24 @@ struct DecodeArgs {
   const int32_t* slot_mapping;
 };
 constexpr int kPrefixChunkTokens = 256;  // tokens of the shared prefix per prefix unit
+// Waves per workgroup of the balanced split's kernels; a launch of W waves runs
+// kBalancedWavesPerGroup * ceil(W / kBalancedWavesPerGroup) of them.
+constexpr int kBalancedWavesPerGroup = 4;
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// Read probe (measurement only): the balanced decode's waves and tiles, loads without the
+// attention arithmetic; each of `waves` waves leaves 64 words in sink.
+struct ReadProbeArgs {
+  uint32_t* sink;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  int S, Hq, Hkv, D, B, MB;
+  int waves;
+  int min_tiles;
+};
+hipError_t launch_read_probe(const ReadProbeArgs& a, hipStream_t stream);
 
 struct PrefillArgs {
   void* out;

@@ -160,19 +160,29 @@ def test_decode_fp8_wave_counts(waves):
     assert_close(values(out), ref, TOL_BF16, f"decode_fp8 waves={waves}")
 
 
+def _requantised(codes, old_scale, new_scale):
+    """The same values held at another pool scale: each code's value (code value * old_scale)
+    re-encoded as the E4M3 code of value / new_scale (float32 quotient), by the oracle's
+    encoder. NaN codes (the never-written slots) stay NaN."""
+    vals = (orc.fp8_e4m3_value(codes) * old_scale).astype(np.float32)
+    return orc.fp8_e4m3_encode(vals / np.float32(new_scale))
+
+
 def test_decode_fp8_scales():
-    """Non-power-of-two scales on the same codes: k_scale changes the softmax, v_scale the
-    output."""
+    """Non-power-of-two pool scales, with K and V at the workload's magnitudes: the pools'
+    values are re-encoded at each (k_scale, v_scale), so the result stays the size of the
+    workload's and the absolute bf16 tolerance applies unchanged. A k_scale or v_scale folded in
+    wrongly (or not at all) changes the result by a factor, far beyond the tolerance."""
     w, kp, vp, _ = _case("g8_b32")
-    tk, tv = to_dev(kp), to_dev(vp)
-    for ks, vs in [(0.3, 0.7), (0.011, 5.0)]:
+    for ks, vs in [(0.3, 0.7), (0.011, 5.0), (1.0 / 3.0, 1.0 / 7.0)]:
+        kq = _requantised(kp, w.k_scale, ks)
+        vq = _requantised(vp, w.v_scale, vs)
         w2 = wl.Workload(**{**w.__dict__, "k_scale": ks, "v_scale": vs})
-        ref = orc.decode(w.q, kp, vp, w.block_table, w.context_lens, w.scale, "bf16",
+        ref = orc.decode(w.q, kq, vq, w.block_table, w.context_lens, w.scale, "bf16",
                          kv_dtype="fp8", k_scale=ks, v_scale=vs)
-        # the bf16 tolerance holds for the workload's V magnitudes (scale 1/16); the error of
-        # the bf16 P and output roundings grows with |V|, i.e. with vs / w.v_scale
-        tol = TOL_BF16 * max(1.0, vs / w.v_scale)
-        assert_close(values(_decode(w2, tk, tv, "f32")), ref, tol, f"scales {ks}, {vs}")
+        assert np.abs(ref).max() < 4.0  # the workload's magnitudes
+        got = values(_decode(w2, to_dev(kq), to_dev(vq), "f32"))
+        assert_close(got, ref, TOL_BF16, f"scales {ks}, {vs}")
 
 
 @pytest.mark.parametrize("k", [2, 3, 4])

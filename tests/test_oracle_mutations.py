@@ -49,6 +49,19 @@ MUTANTS = [
     ("fp8_v_scale_from_k", "return k * k_scale, v * v_scale", "return k * k_scale, v * k_scale"),
     ("prefill_rows_selection", "if wanted is not None and (lo + i, h) not in wanted:",
      "if wanted is not None and (i, h) not in wanted:"),
+    # the whole-chunk (matrix) form of the prefill
+    ("chunk_mask_off_by_one", "np.arange(n)[None, :] <= (r + np.arange(c))[:, None]",
+     "np.arange(n)[None, :] < (r + np.arange(c))[:, None]"),
+    ("chunk_mask_top_left", "np.arange(n)[None, :] <= (r + np.arange(c))[:, None]",
+     "np.arange(n)[None, :] <= np.arange(c)[:, None]"),
+    ("chunk_gqa_mod", "                g = h // group\n                a = np.where",
+     "                g = h % hkv\n                a = np.where"),
+    ("chunk_scale_dropped", "np.where(keep, scale * (qf[lo:hi, h] @ k[g].T), -np.inf)",
+     "np.where(keep, qf[lo:hi, h] @ k[g].T, -np.inf)"),
+    ("chunk_normalise_by_max", "(p @ v[g]) / p.sum(axis=1, keepdims=True)",
+     "(p @ v[g]) / p.max(axis=1, keepdims=True)"),
+    ("chunk_softmax_over_rows", "p = np.exp(a - a.max(axis=1, keepdims=True))",
+     "p = np.exp(a - a.max(axis=0, keepdims=True))"),
 ]
 
 

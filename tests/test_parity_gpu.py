@@ -325,27 +325,44 @@ def test_prefill_single_row_equals_decode():
     assert_close(dec, ref, TOL_BF16, "decode vs oracle")
 
 
-def test_prefill_full_config5_sampled():
-    """Config 5 at full size; the oracle computes a sample of rows one by one."""
+@functools.lru_cache(maxsize=None)
+def _config5_ref():
     w = _config(5)
     kp, vp, _ = _config_ref(5)
-    log(f"prefill config 5: prior {list(w.meta['prior_lens'])}")
+    return orc.prefill_chunk(w.q, w.cu_q_lens, w.context_lens, kp, vp, w.block_table, w.scale,
+                             "bf16")
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_prefill_full_config5(out_dtype):
+    """Config 5 at full size, in the launch configuration the benchmark times: every one of the
+    4096 x 32 (row, head) outputs against the oracle."""
+    w = _config(5)
+    kp, vp, _ = _config_ref(5)
+    log(f"prefill config 5 ({out_dtype} out): prior {list(w.meta['prior_lens'])}")
     d = Dev(w)
     d.write()
     assert np.array_equal(bits(d.k_pool), kp) and np.array_equal(bits(d.v_pool), vp)
-    out = values(d.prefill())
-    assert not np.isnan(out).any()
-    rng = np.random.default_rng(55)
-    rows = []
-    for s in range(w.num_seqs):
-        lo, hi = int(w.cu_q_lens[s]), int(w.cu_q_lens[s + 1])
-        for t in [lo, lo + 1, lo + 31, lo + 32, hi - 1] + list(rng.integers(lo, hi, 3)):
-            rows.append((int(t), int(rng.integers(0, w.num_q_heads))))
+    out = values(d.prefill(out_dtype=_torch_dtype(out_dtype)))
+    assert_close(out, _config5_ref(), TOL_BF16, f"config 5, all rows and heads, {out_dtype} out")
+
+
+@pytest.mark.parametrize("b,prior,chunk", [(16, 33000, 100), (32, 66000, 70)])
+def test_prefill_past_the_block_id_window(b, prior, chunk):
+    """Contexts of more than 2048 blocks: the prefill kernel stages block ids in LDS 2048 at a
+    time, so these move the window once partway through the tile loop (33,100 tokens are 2069
+    blocks at B = 16; 66,070 are 2065 blocks at B = 32), in both row tiles of the chunk. A
+    second sequence with a short context shares the launch."""
+    w = wl.build_prefill(215 + b, 2, 8, 2, 64, b, [prior, 40], [chunk, 30], "bf16")
+    kp, vp = _oracle_written(w)
+    assert -(-int(w.context_lens[0]) // b) > 2048
     ref = orc.prefill_chunk(w.q, w.cu_q_lens, w.context_lens, kp, vp, w.block_table, w.scale,
-                            "bf16", rows=rows)
-    got = np.stack([out[t, h] for t, h in rows])
-    want = np.stack([ref[t, h] for t, h in rows])
-    assert_close(got, want, TOL_BF16, f"config 5 ({len(rows)} sampled rows)")
+                            "bf16")
+    log(f"prefill past the id window: B={b} contexts {list(w.context_lens)}")
+    d = Dev(w)
+    d.write()
+    assert_close(values(d.prefill(out_dtype=_torch_dtype("f32"))), ref, TOL_BF16,
+                 f"prefill, {int(w.context_lens[0])}-token context, B={b}")
 
 
 @pytest.mark.parametrize("waves", [1, 2, 7, 64, 333, 4096])
