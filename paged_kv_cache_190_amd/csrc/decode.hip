@@ -76,6 +76,35 @@ __device__ __forceinline__ void load_q(u32x4 (&qf)[D / 32], const uint16_t* qrow
     qf[kk] = hvalid ? load16(qrow + 32 * kk + 8 * lg) : u32x4{0u, 0u, 0u, 0u};
 }
 
+// The online-softmax update of one tile for a lane's 8 scores x (log2 units, masked ones -inf)
+// whose column maximum is tmax; leaves the bf16 weights of the P.V product in pb.
+// Lazy rescaling: the running maximum m moves only when a column's scores exceed it by more
+// than 2^8 (then acc and l are rescaled, a wave-uniform branch); otherwise the weights are taken
+// against the stale m and are at most 2^8. That is exact: l and acc always refer to the same m,
+// and the output (acc / l) and the partials (m, l, acc / l) only ever combine them consistently.
+template <int D>
+__device__ __forceinline__ void softmax_step(WaveAttn<D>& st, const float (&x)[8], float tmax,
+                                             u32x4& pb) {
+  const bool grow = tmax > st.m + 8.0f;
+  if (__builtin_amdgcn_ballot_w64(grow)) {
+    const float mnew = grow ? tmax : st.m;
+    const float alpha = fast_exp2(st.m - mnew);
+    st.m = mnew;
+    st.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) st.acc[dt] *= alpha;
+  }
+  float psum = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float p0 = fast_exp2(x[2 * w] - st.m);
+    const float p1 = fast_exp2(x[2 * w + 1] - st.m);
+    psum += p0 + p1;
+    pb[w] = pack_bf16x2(p0, p1);
+  }
+  st.l += psum;
+}
+
 // One 32-token tile's step of the online softmax, bf16 operands already in registers: scores
 // by MFMA, running max / sum / rescale, then P.V by MFMA. Tile tokens at or past lim get no
 // weight; V words of tokens at or past vlim are cleared first (stale slots may hold NaN, and
@@ -102,28 +131,17 @@ __device__ __forceinline__ void tile_update(WaveAttn<D>& st, const u32x4 (&k)[2]
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int tt = 8 * lg + 4 * hf + e;
-        x[4 * hf + e] = (tt < lim) ? sc[hf][e] * scale_log2 : -INFINITY;
-      }
+      for (int e = 0; e < 4; ++e) x[4 * hf + e] = sc[hf][e] * scale_log2;
+    if (lim < 32) {  // wave-uniform: only a context's last tile has tokens to mask
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (8 * lg + 4 * (i >> 2) + (i & 3) >= lim) x[i] = -INFINITY;
+    }
     float tmax = x[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
     tmax = xor32_max(xor16_max(tmax));
-    const float mnew = fmaxf(st.m, tmax);
-    const float alpha = fast_exp2(st.m - mnew);
-    st.m = mnew;
-    float psum = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float p0 = fast_exp2(x[2 * w] - mnew);
-      const float p1 = fast_exp2(x[2 * w + 1] - mnew);
-      psum += p0 + p1;
-      pb[w] = pack_bf16x2(p0, p1);
-    }
-    st.l = st.l * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) st.acc[dt] *= alpha;
+    softmax_step(st, x, tmax, pb);
   }
   if (vlim < 32) {
 #pragma unroll
@@ -182,7 +200,7 @@ struct TileWalk {
   int vsel;
   int voff;
   int64_t head_off;
-  int64_t blk_stride;
+  uint32_t blk_stride;  // elements of one block of a pool (Hkv * B * D < 2^32)
   int chunk_lb = 0;
   int my_id = 0;
 
@@ -205,7 +223,7 @@ struct TileWalk {
     const int vtok = (B == 16) ? 8 * (lg & 1) : 8 * lg;
     voff = r16 * B + vtok;
     head_off = static_cast<int64_t>(g) * TILE;
-    blk_stride = static_cast<int64_t>(Hkv) * TILE;
+    blk_stride = static_cast<uint32_t>(Hkv) * TILE;
   }
   // Load the block ids of the chunk that starts at tile c0.
   __device__ __forceinline__ void begin_chunk(const int32_t* __restrict__ bt, int c0) {
@@ -215,24 +233,34 @@ struct TileWalk {
   __device__ __forceinline__ int block_id(int lb) const {
     return __builtin_amdgcn_readlane(my_id, min(lb, nblk - 1) - chunk_lb);
   }
+  // STREAM: non-temporal loads (tiles read once); without it the lines stay cached for the
+  // units that read the same tile again (shared prefixes).
+  template <bool STREAM = true>
   __device__ __forceinline__ void load(KvTile<D, B>& T, int t) const {
     const int lb0 = (tok_begin + 32 * t) / B;
-    const int id0 = block_id(lb0);
-    const int id1 = (B == 16) ? block_id(lb0 + 1) : id0;
-    const uint16_t* kb = kpool + (ksel ? id1 : id0) * blk_stride + head_off;
-    const uint16_t* vb = vpool + (vsel ? id1 : id0) * blk_stride + head_off;
+    // both candidate block offsets are wave-uniform (block ids are non-negative); a lane
+    // selects the one its rows lie in
+    const uint64_t o0 = static_cast<uint64_t>(static_cast<uint32_t>(block_id(lb0))) * blk_stride;
+    const uint64_t o1 =
+        (B == 16) ? static_cast<uint64_t>(static_cast<uint32_t>(block_id(lb0 + 1))) * blk_stride
+                  : o0;
+    const uint16_t* kb = kpool + (ksel ? o1 : o0) + head_off;
+    const uint16_t* vb = vpool + (vsel ? o1 : o0) + head_off;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) T.k[hf][kk] = load16(kb + koff[hf] + 32 * kk);
+      for (int kk = 0; kk < KK; ++kk)
+        T.k[hf][kk] = STREAM ? load16_stream(kb + koff[hf] + 32 * kk) : load16(kb + koff[hf] + 32 * kk);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) T.v[dt] = load16(vb + voff + 16 * dt * B);
+    for (int dt = 0; dt < DT; ++dt)
+      T.v[dt] = STREAM ? load16_stream(vb + voff + 16 * dt * B) : load16(vb + voff + 16 * dt * B);
   }
 };
 
 // Attend the wave's 16 head columns (KV head g) to tokens [tok_begin, tok_end) of one
 // sequence with n tokens, walking 32-token tiles from tok_begin (a multiple of B).
-template <int D, int B>
+// STREAM: the tiles' loads are non-temporal (see TileWalk::load).
+template <int D, int B, bool STREAM = true>
 __device__ __forceinline__ void attend_tiles(WaveAttn<D>& st, const u32x4 (&qf)[D / 32],
                                              const uint16_t* __restrict__ kpool,
                                              const uint16_t* __restrict__ vpool,
@@ -254,16 +282,16 @@ __device__ __forceinline__ void attend_tiles(WaveAttn<D>& st, const u32x4 (&qf)[
   for (int c0 = 0; c0 < ntiles; c0 += TileWalk<D, B>::kChunkTiles) {
     const int c1 = min(ntiles, c0 + TileWalk<D, B>::kChunkTiles);
     wk.begin_chunk(bt, c0);
-    wk.load(ta, c0);
+    wk.template load<STREAM>(ta, c0);
     int t = c0;
     for (; t + 2 < c1; t += 2) {
-      wk.load(tb, t + 1);
+      wk.template load<STREAM>(tb, t + 1);
       compute(ta, t);
-      wk.load(ta, t + 2);
+      wk.template load<STREAM>(ta, t + 2);
       compute(tb, t + 1);
     }
     if (t + 1 < c1) {
-      wk.load(tb, t + 1);
+      wk.template load<STREAM>(tb, t + 1);
       compute(ta, t);
       compute(tb, t + 1);
     } else {
@@ -292,7 +320,7 @@ __device__ __forceinline__ void attend_tiles2(WaveAttn<D> (&st)[2],
     const int c1 = min(ntiles, c0 + TileWalk<D, B>::kChunkTiles);
     wk.begin_chunk(bt, c0);
     for (int t = c0; t < c1; ++t) {
-      wk.load(ta, t);
+      wk.template load<false>(ta, t);
       const int tok0 = tok_begin + 32 * t;
 #pragma unroll
       for (int c = 0; c < 2; ++c)
@@ -306,7 +334,7 @@ __device__ __forceinline__ void attend_tiles2(WaveAttn<D> (&st)[2],
 // loaded by the same lanes through the same two-register-set pipeline, with the attention
 // arithmetic replaced by an XOR of the loaded words (so no load can be dropped). Its time
 // against the decode's separates the cost of reading the tile list from the cost of the math.
-template <int D, int B>
+template <int D, int B, bool STREAM = true>
 __device__ __forceinline__ uint32_t probe_tiles(const uint16_t* __restrict__ kpool,
                                                 const uint16_t* __restrict__ vpool,
                                                 const int32_t* __restrict__ bt, int n, int g,
@@ -327,16 +355,16 @@ __device__ __forceinline__ uint32_t probe_tiles(const uint16_t* __restrict__ kpo
   for (int c0 = 0; c0 < ntiles; c0 += TileWalk<D, B>::kChunkTiles) {
     const int c1 = min(ntiles, c0 + TileWalk<D, B>::kChunkTiles);
     wk.begin_chunk(bt, c0);
-    wk.load(ta, c0);
+    wk.template load<STREAM>(ta, c0);
     int t = c0;
     for (; t + 2 < c1; t += 2) {
-      wk.load(tb, t + 1);
+      wk.template load<STREAM>(tb, t + 1);
       fold(ta);
-      wk.load(ta, t + 2);
+      wk.template load<STREAM>(ta, t + 2);
       fold(tb);
     }
     if (t + 1 < c1) {
-      wk.load(tb, t + 1);
+      wk.template load<STREAM>(tb, t + 1);
       fold(ta);
       fold(tb);
     } else {
@@ -381,7 +409,8 @@ __device__ __forceinline__ u32x2 load8(const void* p) {
 // attend_tiles for E4M3 pools: the same tiles, token-to-row assignment, softmax and pipeline;
 // only the loads (bytes) and the widening before each product differ.
 // DEPTH: register sets in the tile pipeline (3, or 2 where registers are tighter).
-template <int D, int B, int DEPTH = 3>
+// STREAM: non-temporal loads (see TileWalk::load).
+template <int D, int B, int DEPTH = 3, bool STREAM = true>
 __device__ __forceinline__ void attend_tiles_fp8(WaveAttn<D>& st, const u32x4 (&qf)[D / 32],
                                                  const uint8_t* __restrict__ kpool,
                                                  const uint8_t* __restrict__ vpool,
@@ -410,7 +439,7 @@ __device__ __forceinline__ void attend_tiles_fp8(WaveAttn<D>& st, const u32x4 (&
   const int vtok = (B == 16) ? 8 * (lg & 1) : 8 * lg;
   const int voff = r16 * B + vtok;
   const int64_t head_off = static_cast<int64_t>(g) * TILE;
-  const int64_t blk_stride = static_cast<int64_t>(Hkv) * TILE;
+  const uint32_t blk_stride = static_cast<uint32_t>(Hkv) * TILE;  // < 2^32
 
   int chunk_lb = 0;
   int my_id = 0;
@@ -419,16 +448,20 @@ __device__ __forceinline__ void attend_tiles_fp8(WaveAttn<D>& st, const u32x4 (&
   };
   auto load_tile = [&](KvTile8<D, B>& T, int t) {
     const int lb0 = (tok_begin + 32 * t) / B;
-    const int id0 = block_id(lb0);
-    const int id1 = (B == 16) ? block_id(lb0 + 1) : id0;
-    const uint8_t* kb = kpool + (ksel ? id1 : id0) * blk_stride + head_off;
-    const uint8_t* vb = vpool + (vsel ? id1 : id0) * blk_stride + head_off;
+    const uint64_t o0 = static_cast<uint64_t>(static_cast<uint32_t>(block_id(lb0))) * blk_stride;
+    const uint64_t o1 =
+        (B == 16) ? static_cast<uint64_t>(static_cast<uint32_t>(block_id(lb0 + 1))) * blk_stride
+                  : o0;
+    const uint8_t* kb = kpool + (ksel ? o1 : o0) + head_off;
+    const uint8_t* vb = vpool + (vsel ? o1 : o0) + head_off;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int j = 0; j < KL; ++j) T.k[hf][j] = load16(kb + koff[hf] + 16 * j);
+      for (int j = 0; j < KL; ++j)
+        T.k[hf][j] = STREAM ? load16_stream(kb + koff[hf] + 16 * j) : load16(kb + koff[hf] + 16 * j);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) T.v[dt] = load8(vb + voff + 16 * dt * B);
+    for (int dt = 0; dt < DT; ++dt)
+      T.v[dt] = STREAM ? load8_stream(vb + voff + 16 * dt * B) : load8(vb + voff + 16 * dt * B);
   };
 
   auto compute = [&](KvTile8<D, B>& T, int t) {
@@ -449,29 +482,18 @@ __device__ __forceinline__ void attend_tiles_fp8(WaveAttn<D>& st, const u32x4 (&
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int tt = 8 * lg + 4 * hf + e;
-        x[4 * hf + e] = (tt < lim) ? sc[hf][e] * scale_log2 : -INFINITY;
-      }
+      for (int e = 0; e < 4; ++e) x[4 * hf + e] = sc[hf][e] * scale_log2;
+    if (lim < 32) {  // wave-uniform: only a context's last tile has tokens to mask
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (8 * lg + 4 * (i >> 2) + (i & 3) >= lim) x[i] = -INFINITY;
+    }
     float tmax = x[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, x[i]);
     tmax = xor32_max(xor16_max(tmax));
-    const float mnew = fmaxf(st.m, tmax);
-    const float alpha = fast_exp2(st.m - mnew);
-    st.m = mnew;
-    float psum = 0.f;
     u32x4 pb;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float p0 = fast_exp2(x[2 * w] - mnew);
-      const float p1 = fast_exp2(x[2 * w + 1] - mnew);
-      psum += p0 + p1;
-      pb[w] = pack_bf16x2(p0, p1);
-    }
-    st.l = st.l * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) st.acc[dt] *= alpha;
+    softmax_step(st, x, tmax, pb);
     u32x4 vv[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) vv[dt] = e4m3x8_to_bf16x8(T.v[dt][0], T.v[dt][1]);
@@ -583,6 +605,22 @@ __device__ __forceinline__ void write_zero(OutT* __restrict__ o, int lg) {
     for (int e = 0; e < 4; ++e) store_out(o + 16 * dt + 4 * lg + e, 0.0f);
 }
 
+// Cache policy of a segment's tile loads. Tiles read once per call are streamed (non-temporal
+// loads). A block that several sequences' tables name (a shared prompt prefix, as prefix caching
+// and copy-on-write forks produce) is read again by those sequences' waves and should stay
+// cached instead. Sharing is detected cheaply, per sequence: its first block also starts the
+// table of the previous or the next sequence of the batch (the entry is read even when that
+// neighbour's context is empty: it lies inside the table, and the outcome only picks a policy).
+// Only the load hints depend on it, never the result.
+__device__ __forceinline__ bool shares_first_block(const int32_t* __restrict__ block_table,
+                                                   int s, int S, int MB) {
+  const int64_t row = static_cast<int64_t>(s) * MB;
+  const int first = block_table[row];
+  const int prev = s > 0 ? block_table[row - MB] : -1;
+  const int next = s + 1 < S ? block_table[row + MB] : -1;
+  return first == prev || first == next;
+}
+
 // Fixed partitions of P tokens: grid (KV head x head group, sequence, partition). The
 // partition index is the slowest, so the dispatcher hands out every sequence's first (full)
 // partitions before the shorter last ones, and the launch ends on small work units.
@@ -614,8 +652,13 @@ __global__ __launch_bounds__(64) void decode_fixed_kernel(
   load_q<D>(qf, q + row * D, hvalid, lg);
   WaveAttn<D> st;
   attn_init(st);
-  attend_tiles<D, B>(st, qf, kpool, vpool, block_table + static_cast<int64_t>(s) * MB, n, g,
-                     Hkv, start, min(start + P, n), scale_log2);
+  const int32_t* bt = block_table + static_cast<int64_t>(s) * MB;
+  if (!shares_first_block(block_table, s, gridDim.y, MB))
+    attend_tiles<D, B, true>(st, qf, kpool, vpool, bt, n, g, Hkv, start, min(start + P, n),
+                             scale_log2);
+  else
+    attend_tiles<D, B, false>(st, qf, kpool, vpool, bt, n, g, Hkv, start, min(start + P, n),
+                              scale_log2);
   const float l_total = xor32_sum(xor16_sum(st.l));
   if (!hvalid) return;
   if constexpr (!SPLIT) write_final<D>(out + row * D, st, l_total, lg);
@@ -784,19 +827,34 @@ __device__ __forceinline__ void balanced_body(
     const int32_t* bt = block_table + static_cast<int64_t>(s) * MB;
     const int tb = pre + 32 * t_begin;
     const int te = min(pre + 32 * t_end, n);
+    // the prefix kernel's suffix waves run beside prefix units re-reading their tiles from
+    // cache: cacheable loads there (measured faster than streamed ones)
+    const bool stream = !PREFIX && !shares_first_block(block_table, s, S, MB);
     if constexpr (PROBE) {
-      probe_acc ^= probe_tiles<D, B>(kpool, vpool, bt, n, g, Hkv, tb, te);
+      probe_acc ^= stream ? probe_tiles<D, B, true>(kpool, vpool, bt, n, g, Hkv, tb, te)
+                          : probe_tiles<D, B, false>(kpool, vpool, bt, n, g, Hkv, tb, te);
     } else if constexpr (kFp8) {
       load_q_fp8<D>(qf, q + row * D, hvalid, lg);
       // the prefix kernel is held to 256 VGPRs: two register sets there
-      attend_tiles_fp8<D, B, PREFIX ? 2 : 3>(st, qf, kpool, vpool, bt, n, g, Hkv, tb, te,
-                                            scale_log2);
+      if constexpr (PREFIX)
+        attend_tiles_fp8<D, B, 2, false>(st, qf, kpool, vpool, bt, n, g, Hkv, tb, te,
+                                         scale_log2);
+      else if (stream)
+        attend_tiles_fp8<D, B, 3, true>(st, qf, kpool, vpool, bt, n, g, Hkv, tb, te,
+                                        scale_log2);
+      else
+        attend_tiles_fp8<D, B, 3, false>(st, qf, kpool, vpool, bt, n, g, Hkv, tb, te,
+                                         scale_log2);
     } else if constexpr (STEP) {
       load_q<D>(qf, q + row * D, hvalid, lg);
       const int slot = sp.slots[s];
       const int np = slot >= 0 ? n - 1 : n;  // tokens read from the pool
-      attend_tiles<D, B>(st, qf, kpool, vpool, bt, np, g, Hkv, tb, min(te, np), scale_log2,
-                         hvalid);
+      if (stream)
+        attend_tiles<D, B, true>(st, qf, kpool, vpool, bt, np, g, Hkv, tb, min(te, np),
+                                 scale_log2, hvalid);
+      else
+        attend_tiles<D, B, false>(st, qf, kpool, vpool, bt, np, g, Hkv, tb, min(te, np),
+                                  scale_log2, hvalid);
       if (slot >= 0 && te == n) {
         const int64_t src = (static_cast<int64_t>(s) * Hkv + g) * D;
         attend_one_token<D>(st, qf, sp.k_new + src, sp.v_new + src, scale_log2);
@@ -812,7 +870,12 @@ __device__ __forceinline__ void balanced_body(
       }
     } else {
       load_q<D>(qf, q + row * D, hvalid, lg);
-      attend_tiles<D, B>(st, qf, kpool, vpool, bt, n, g, Hkv, tb, te, scale_log2, hvalid);
+      if (stream)
+        attend_tiles<D, B, true>(st, qf, kpool, vpool, bt, n, g, Hkv, tb, te, scale_log2,
+                                 hvalid);
+      else
+        attend_tiles<D, B, false>(st, qf, kpool, vpool, bt, n, g, Hkv, tb, te, scale_log2,
+                                  hvalid);
     }
     const float l_total = xor32_sum(xor16_sum(st.l));
     const int64_t wf = wave_of(a);
@@ -940,7 +1003,8 @@ __device__ __forceinline__ void prefix_unit(
     else load_q<D>(qf[k], q + row[k] * D, valid[k], lg);
   }
   if constexpr (kFp8)
-    attend_tiles_fp8<D, B, 2>(st[0], qf[0], kpool, vpool, bt, pre, g, Hkv, tok0, te, scale_log2);
+    attend_tiles_fp8<D, B, 2, false>(st[0], qf[0], kpool, vpool, bt, pre, g, Hkv, tok0, te,
+                                     scale_log2);
   else
     attend_tiles2<D, B>(st, qf, kpool, vpool, bt, pre, g, Hkv, tok0, te, scale_log2, valid);
 #pragma unroll
