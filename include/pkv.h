@@ -377,6 +377,30 @@ int pkv_paged_attention_prefill_chunk(void* out, const void* q, const int32_t* c
                                       int out_dtype, void* stream);
 
 /*
+ * pkv_paged_attention_decode_noalloc -- pkv_paged_attention_decode (bf16 inputs, balanced
+ * split) for callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation. It takes no workspace and allocates nothing:
+ * the partials live in a static device array of the library, 128 MiB per GPU (held from the
+ * first use of the library on that GPU until the process ends), whose address is looked up once
+ * per device on the first call made with it current.
+ *   Arguments as for pkv_paged_attention_decode with dtype = PKV_BF16 and partition_size = 0;
+ *   the results are the same bit for bit.
+ *   Returns PKV_ERR_WORKSPACE, before any HIP call, when these sizes would need more than the
+ *   128 MiB (pkv_decode_workspace_size(..., 0, PKV_BF16) bytes; e.g. 64 sequences of up to 4096
+ *   tokens with 32/8 heads need 17 MiB, 32 of up to 32768 tokens with 64/8 heads 120 MiB).
+ *   Every call on one GPU uses that GPU's one array, and the array keeps the last call's
+ *   contents (nothing in it has to start at zero): calls that overlap on one GPU (other streams,
+ *   other threads) race and give wrong results; calls in order on one stream do not.
+ */
+int pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_pool,
+                                       const void* v_pool, const int32_t* block_table,
+                                       const int32_t* context_lens, int num_seqs,
+                                       int num_q_heads, int num_kv_heads, int head_dim,
+                                       int block_size, int max_blocks_per_seq, int num_blocks,
+                                       float scale, int max_context_len, int num_waves,
+                                       int out_dtype, void* stream);
+
+/*
  * pkv_decode_read_probe -- measurement only, not part of the attention path. Launches the
  * balanced split of pkv_paged_attention_decode (bf16 pools, the same num_waves rule) with the
  * same waves reading the same K/V tiles with the same loads, but without the attention

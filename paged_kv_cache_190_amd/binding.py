@@ -57,6 +57,9 @@ def lib() -> ctypes.CDLL:
     L.pkv_paged_attention_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                                     i32, i32, i32, i32, i32, f32, i32, i32, i32,
                                                     i32, vp]
+    L.pkv_paged_attention_decode_noalloc.restype = i32
+    L.pkv_paged_attention_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                                     i32, i32, i32, f32, i32, i32, i32, vp]
     L.pkv_decode_read_probe_sink_size.restype = sz
     L.pkv_decode_read_probe_sink_size.argtypes = [i32, i32, i32, i32, i32]
     L.pkv_decode_read_probe.restype = i32

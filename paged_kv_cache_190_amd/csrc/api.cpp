@@ -606,6 +606,43 @@ size_t probe_sink_bytes(int waves) {
 
 extern "C" {
 
+int pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_pool,
+                                       const void* v_pool, const int32_t* block_table,
+                                       const int32_t* context_lens, int num_seqs,
+                                       int num_q_heads, int num_kv_heads, int head_dim,
+                                       int block_size, int max_blocks_per_seq, int num_blocks,
+                                       float scale, int max_context_len, int num_waves,
+                                       int out_dtype, void* stream) {
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs = %d is negative", num_seqs);
+  if (num_seqs == 0) return PKV_OK;
+  pkv::DecodeArgs a{};
+  int st = check_decode(a, out, q, k_pool, v_pool, block_table, context_lens, num_seqs,
+                        num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                        num_blocks, scale, max_context_len, PKV_BF16, out_dtype);
+  if (st != PKV_OK) return st;
+  if (num_waves < 0 || num_waves > kMaxDecodeWaves)
+    return fail(PKV_ERR_INVALID_ARG, "num_waves %d outside [0, %d]", num_waves, kMaxDecodeWaves);
+  // the size check is made before any HIP call
+  const size_t need =
+      balanced_plan(a.S, a.Hq, a.Hkv, a.D, a.max_ctx,
+                    num_waves > 0 ? num_waves : kDefaultDecodeWaves).bytes;
+  if (need > pkv::kNoAllocScratchBytes)
+    return fail(PKV_ERR_WORKSPACE,
+                "these sizes need %zu bytes of scratch; the library's static scratch holds %zu "
+                "(use pkv_paged_attention_decode with a workspace)",
+                need, pkv::kNoAllocScratchBytes);
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (int hs = hip_status(pkv::noalloc_scratch(&ws, &ws_bytes), "decode_noalloc scratch"))
+    return hs;
+  st = setup_balanced(a, ws, ws_bytes, kDefaultDecodeWaves, num_waves);
+  if (st != PKV_OK) return st;
+  a.bf16_in = 1;
+  a.bf16_out = out_dtype == PKV_BF16;
+  return hip_status(pkv::launch_decode(a, static_cast<hipStream_t>(stream)),
+                    "paged_attention_decode_noalloc");
+}
+
 size_t pkv_decode_read_probe_sink_size(int num_seqs, int num_q_heads, int num_kv_heads,
                                        int max_context_len, int num_waves) {
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||

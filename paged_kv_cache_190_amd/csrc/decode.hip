@@ -36,6 +36,7 @@
 //
 // fp32 path (vector ALUs): one wave owns (sequence, query head, partition); lanes take one token
 // each for the scores, then one output dimension each for P.V.
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -1327,6 +1328,33 @@ __global__ __launch_bounds__(256) void decode_reduce_wide_kernel(
 }
 
 // ------------------------------------------------------------------------------ launchers
+
+// The scratch of pkv_paged_attention_decode_noalloc (see kNoAllocScratchBytes). In host code
+// `scratch` names a host-side stand-in, not device memory: kernels get the address that
+// hipGetSymbolAddress returns for the current device, looked up on the first call made with
+// that device current and kept per device.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr, size_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* per_device[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!per_device[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  *bytes = kNoAllocScratchBytes;
+  return hipSuccess;
+}
 
 template <int D, int B, typename OutT>
 static hipError_t launch_bf16(const DecodeArgs& a, hipStream_t st) {

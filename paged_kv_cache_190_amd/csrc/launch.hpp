@@ -128,6 +128,13 @@ constexpr int kPrefixChunkTokens = 256;  // tokens of the shared prefix per pref
 // Waves per workgroup of the balanced split's kernels; a launch of W waves runs
 // kBalancedWavesPerGroup * ceil(W / kBalancedWavesPerGroup) of them.
 constexpr int kBalancedWavesPerGroup = 4;
+
+// Scratch of pkv_paged_attention_decode_noalloc: the balanced split's partials and segment
+// counts in a file-scope device array of this many bytes (one per GPU, held until the process
+// ends). noalloc_scratch returns the current device's copy: its address is looked up once per
+// device and kept; nothing is allocated.
+constexpr size_t kNoAllocScratchBytes = static_cast<size_t>(128) << 20;
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 // Read probe (measurement only): the balanced decode's waves and tiles, loads without the
