@@ -58,6 +58,12 @@
  *      0 <= context_lens[s] <= max_blocks_per_seq*B, and <= max_context_len when one is given;
  *      non-negative slots in slot_mapping are < num_blocks*B and pairwise distinct.
  *    Block-table entries past ceil(context_lens[s]/B) are never read.
+ *    Debug builds (libpkv_debug.so, compiled with PKV_DEBUG=1) check them on the device: every
+ *    call first runs check kernels over the arrays it was handed (block ids it would read,
+ *    context lengths, slots, chunk bounds, prefix groups, copy pairs; the distinctness of slots
+ *    is not checked), waits for them (so debug calls synchronise their stream), and launches its
+ *    own kernels only if nothing was found; otherwise it returns PKV_ERR_DEVICE_ARG, launches
+ *    nothing and leaves every output untouched. pkv_debug_found() gives what was found.
  *  - Sharing: several block tables may name the same physical block (shared prefixes,
  *    [Inference Engines "PagedAttention"; Serving Engines]). The attention calls only read the
  *    pools; writing into a shared block is the caller's error (fork it first).
@@ -80,7 +86,8 @@ typedef enum {
   PKV_ERR_UNSUPPORTED = 2, /* dtype / head_dim / block_size / grouping not built */
   PKV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
   PKV_ERR_HIP = 4,         /* a HIP runtime call failed; see pkv_last_error() */
-  PKV_ERR_OUT_OF_BLOCKS = 5 /* block manager: not enough free blocks (nothing was changed) */
+  PKV_ERR_OUT_OF_BLOCKS = 5, /* block manager: not enough free blocks (nothing was changed) */
+  PKV_ERR_DEVICE_ARG = 6     /* debug builds: a device array breaks a precondition (see above) */
 } pkv_status;
 
 /* PKV_FP8_E4M3: pools only (pkv_kv_cache_write_fp8, pkv_paged_attention_decode_fp8,
@@ -93,6 +100,13 @@ typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 } pkv_dtype;
 int pkv_abi_version(void);
 const char* pkv_status_string(int status);
 const char* pkv_last_error(void);
+/* 1 in a debug build (device-array checks before every call, see above), else 0. */
+int pkv_debug_build(void);
+/* Debug builds: what the checks of this thread's last call found, as a mask -- 1 block id
+ * outside the pool, 2 context length out of range, 4 slot outside the pool, 8 chunk bounds
+ * (cu_q_lens) invalid, 16 prefix groups invalid, 32 copy pair outside its pool; 0 when the call
+ * was clean. Release builds: 0. */
+unsigned pkv_debug_found(void);
 
 /*
  * pkv_kv_cache_write -- scatter new K/V rows into pool slots through a slot mapping.

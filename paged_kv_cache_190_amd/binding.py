@@ -16,12 +16,15 @@ import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "lib", "libpkv.so")
+# The library built with PKV_DEBUG=1: device-array checks before every call (see include/pkv.h).
+DEBUG_LIB_PATH = os.path.join(PKG, "lib", "libpkv_debug.so")
 
 (PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP,
- PKV_ERR_OUT_OF_BLOCKS) = range(6)
+ PKV_ERR_OUT_OF_BLOCKS, PKV_ERR_DEVICE_ARG) = range(7)
 PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 
 _lib = None
+_debug_lib = None
 
 
 class PkvError(RuntimeError):
@@ -33,13 +36,27 @@ class PkvError(RuntimeError):
 def lib() -> ctypes.CDLL:
     """The loaded libpkv (loaded once)."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+    if _lib is None:
+        _lib = _load(LIB_PATH)
+    return _lib
+
+
+def debug_lib() -> ctypes.CDLL:
+    """The debug build of libpkv (loaded once), with the same C ABI."""
+    global _debug_lib
+    if _debug_lib is None:
+        _debug_lib = _load(DEBUG_LIB_PATH)
+    return _debug_lib
+
+
+def _load(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
                            "`python -m paged_kv_cache_190_amd.build`")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     vp, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    L.pkv_debug_build.restype = i32
+    L.pkv_debug_found.restype = ctypes.c_uint
     L.pkv_abi_version.restype = i32
     L.pkv_status_string.restype = ctypes.c_char_p
     L.pkv_status_string.argtypes = [i32]
@@ -113,7 +130,6 @@ def lib() -> ctypes.CDLL:
     L.pkv_bm_block_table.argtypes = [vp, i64, pi32, i32, pint]
     L.pkv_bm_refcount.restype = i32
     L.pkv_bm_refcount.argtypes = [vp, i32, pint]
-    _lib = L
     return L
 
 

@@ -13,11 +13,19 @@
 #include <string>
 #include <vector>
 
+#include "checks.hpp"
 #include "errors.hpp"
 #include "launch.hpp"
 
+// PKV_DEBUG=1 builds check the device arrays of every call on the device before launching it.
+#ifndef PKV_DEBUG
+#define PKV_DEBUG 0
+#endif
+
 namespace {
 thread_local std::string g_last_error;
+thread_local unsigned g_debug_found = 0;  // DebugBits of this thread's last checked call
+constexpr bool kDebugBuild = PKV_DEBUG != 0;
 }  // namespace
 
 int pkv::fail(int status, const char* fmt, ...) {
@@ -37,6 +45,42 @@ using pkv::fail;
 int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return PKV_OK;
   return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Debug builds: the call's device arrays are checked on the device first (debug.hip); a call
+// whose arrays break the documented preconditions launches nothing and returns
+// PKV_ERR_DEVICE_ARG. Release builds: nothing.
+int debug_gate(const pkv::DebugCheckArgs& d, void* stream, const char* what) {
+  if constexpr (!kDebugBuild) {
+    (void)d, (void)stream, (void)what;
+    return PKV_OK;
+  } else {
+    unsigned bits = 0;
+    if (int st = hip_status(pkv::debug_check(d, static_cast<hipStream_t>(stream), &bits), what))
+      return st;
+    g_debug_found = bits;
+    if (!bits) return PKV_OK;
+    std::string names;
+    const char* labels[] = {"block id", "context length", "slot", "chunk", "group", "pair"};
+    for (int i = 0; i < 6; ++i)
+      if (bits & (1u << i)) names += std::string(names.empty() ? "" : ", ") + labels[i];
+    return fail(PKV_ERR_DEVICE_ARG,
+                "%s: device arrays break the documented preconditions (found: %s); nothing "
+                "was launched", what, names.c_str());
+  }
+}
+
+pkv::DebugCheckArgs tables_check(const int32_t* bt, const int32_t* ctx, int S, int MB, int B,
+                                 int NB, int max_ctx) {
+  pkv::DebugCheckArgs d;
+  d.block_table = bt;
+  d.context_lens = ctx;
+  d.S = S;
+  d.MB = MB;
+  d.B = B;
+  d.NB = NB;
+  d.max_ctx = max_ctx;
+  return d;
 }
 
 bool supported_dtype(int d) { return d == PKV_F32 || d == PKV_BF16; }
@@ -96,6 +140,7 @@ const char* kernel_name(int id) {
     case K_PREFILL: return "prefill_chunk";
     case K_COPY_BLOCKS: return "copy_blocks";
     case K_READ_PROBE: return "read_probe";
+    case K_DEBUG_CHECK: return "debug_check";
     default: return "?";
   }
 }
@@ -208,11 +253,16 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_HIP: return "HIP runtime error";
     case PKV_ERR_OUT_OF_BLOCKS: return "not enough free blocks";
+    case PKV_ERR_DEVICE_ARG: return "device array breaks a precondition (debug build)";
     default: return "unknown status";
   }
 }
 
 const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+int pkv_debug_build(void) { return kDebugBuild ? 1 : 0; }
+
+unsigned pkv_debug_found(void) { return g_debug_found; }
 
 int pkv_kv_cache_write(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
                        const int32_t* slot_mapping, int T, int num_kv_heads, int head_dim,
@@ -234,6 +284,12 @@ int pkv_kv_cache_write(const void* k_new, const void* v_new, void* k_pool, void*
     return fail(PKV_ERR_UNSUPPORTED, "pool of %d blocks exceeds int32 slot numbers", num_blocks);
   pkv::KvWriteArgs a{k_new, v_new, k_pool, v_pool, slot_mapping, T, num_kv_heads, head_dim,
                      block_size, num_blocks, elem_bytes(dtype)};
+  pkv::DebugCheckArgs d;
+  d.slots = slot_mapping;
+  d.T = T;
+  d.slot_NB = num_blocks;
+  d.B = block_size;
+  if (int st = debug_gate(d, stream, "kv_cache_write")) return st;
   return hip_status(pkv::launch_kv_write(a, static_cast<hipStream_t>(stream)), "kv_cache_write");
 }
 
@@ -261,6 +317,12 @@ int pkv_kv_cache_write_fp8(const void* k_new, const void* v_new, void* k_pool, v
     return fail(PKV_ERR_UNSUPPORTED, "pool of %d blocks exceeds int32 slot numbers", num_blocks);
   pkv::KvWriteArgs a{k_new, v_new, k_pool, v_pool, slot_mapping, T, num_kv_heads, head_dim,
                      block_size, num_blocks, elem_bytes(in_dtype)};
+  pkv::DebugCheckArgs d;
+  d.slots = slot_mapping;
+  d.T = T;
+  d.slot_NB = num_blocks;
+  d.B = block_size;
+  if (int st = debug_gate(d, stream, "kv_cache_write_fp8")) return st;
   return hip_status(pkv::launch_kv_write_fp8(a, in_dtype == PKV_BF16, k_scale, v_scale,
                                              static_cast<hipStream_t>(stream)),
                     "kv_cache_write_fp8");
@@ -308,6 +370,12 @@ int pkv_kv_cache_copy_blocks(const void* src_k, const void* src_v, void* dst_k, 
     if (int st = check_kernel_visible(ptrs[i], names[i])) return st;
   pkv::CopyBlocksArgs a{src_k, src_v, dst_k, dst_v, block_pairs, n_pairs, num_kv_heads,
                         head_dim, block_size, elem_bytes(dtype)};
+  pkv::DebugCheckArgs d;
+  d.pairs = block_pairs;
+  d.n_pairs = n_pairs;
+  d.src_nb = src_num_blocks;
+  d.dst_nb = dst_num_blocks;
+  if (int st = debug_gate(d, stream, "kv_cache_copy_blocks")) return st;
   return hip_status(pkv::launch_copy_blocks(a, static_cast<hipStream_t>(stream)),
                     "kv_cache_copy_blocks");
 }
@@ -480,6 +548,12 @@ int pkv_paged_attention_decode_shared_prefix(
   a.v_scale = a.fp8_kv ? v_scale : 1.0f;
   a.bf16_in = 1;
   a.bf16_out = out_dtype == PKV_BF16;
+  pkv::DebugCheckArgs d = tables_check(block_table, context_lens, a.S, a.MB, a.B, a.NB, a.max_ctx);
+  d.group_start = group_start;
+  d.group_prefix_len = group_prefix_len;
+  d.NG = num_groups;
+  d.max_prefix = max_prefix_len;
+  if (int dst = debug_gate(d, stream, "paged_attention_decode_shared_prefix")) return dst;
   return hip_status(pkv::launch_decode(a, static_cast<hipStream_t>(stream)),
                     "paged_attention_decode_shared_prefix");
 }
@@ -511,6 +585,11 @@ int pkv_kv_cache_write_and_decode(void* out, const void* q, const void* k_new,
   a.slot_mapping = slot_mapping;
   a.bf16_in = 1;
   a.bf16_out = out_dtype == PKV_BF16;
+  pkv::DebugCheckArgs d = tables_check(block_table, context_lens, a.S, a.MB, a.B, a.NB, a.max_ctx);
+  d.slots = slot_mapping;
+  d.T = num_seqs;
+  d.slot_NB = num_blocks;
+  if (int dst = debug_gate(d, stream, "kv_cache_write_and_decode")) return dst;
   return hip_status(pkv::launch_decode(a, static_cast<hipStream_t>(stream)),
                     "kv_cache_write_and_decode");
 }
@@ -541,6 +620,9 @@ int pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_pool,
   a.v_scale = v_scale;
   a.bf16_in = 1;
   a.bf16_out = out_dtype == PKV_BF16;
+  if (int dst = debug_gate(tables_check(block_table, context_lens, a.S, a.MB, a.B, a.NB,
+                                        a.max_ctx), stream, "paged_attention_decode_fp8"))
+    return dst;
   return hip_status(pkv::launch_decode(a, static_cast<hipStream_t>(stream)),
                     "paged_attention_decode_fp8");
 }
@@ -588,6 +670,9 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_pool, con
   }
   a.bf16_in = dtype == PKV_BF16;
   a.bf16_out = out_dtype == PKV_BF16;
+  if (int dst = debug_gate(tables_check(block_table, context_lens, a.S, a.MB, a.B, a.NB,
+                                        a.max_ctx), stream, "paged_attention_decode"))
+    return dst;
   return hip_status(pkv::launch_decode(a, static_cast<hipStream_t>(stream)),
                     "paged_attention_decode");
 }
@@ -639,6 +724,9 @@ int pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_p
   if (st != PKV_OK) return st;
   a.bf16_in = 1;
   a.bf16_out = out_dtype == PKV_BF16;
+  if (int dst = debug_gate(tables_check(block_table, context_lens, a.S, a.MB, a.B, a.NB,
+                                        a.max_ctx), stream, "paged_attention_decode_noalloc"))
+    return dst;
   return hip_status(pkv::launch_decode(a, static_cast<hipStream_t>(stream)),
                     "paged_attention_decode_noalloc");
 }
@@ -675,6 +763,9 @@ int pkv_decode_read_probe(const void* k_pool, const void* v_pool, const int32_t*
     return fail(PKV_ERR_WORKSPACE, "sink of %zu bytes needed, %zu given", need, sink_bytes);
   pkv::ReadProbeArgs r{static_cast<uint32_t*>(sink), k_pool, v_pool, block_table, context_lens,
                        a.S, a.Hq, a.Hkv, a.D, a.B, a.MB, pl.waves, kMinTilesPerWave};
+  if (int dst = debug_gate(tables_check(block_table, context_lens, a.S, a.MB, a.B, a.NB,
+                                        a.max_ctx), stream, "decode_read_probe"))
+    return dst;
   return hip_status(pkv::launch_read_probe(r, static_cast<hipStream_t>(stream)),
                     "decode_read_probe");
 }
@@ -729,6 +820,10 @@ int pkv_paged_attention_prefill_chunk(void* out, const void* q, const int32_t* c
   a.max_ctx = max_context_len > 0 ? max_context_len : static_cast<int>(cap);
   a.bf16_in = dtype == PKV_BF16;
   a.bf16_out = out_dtype == PKV_BF16;
+  pkv::DebugCheckArgs d = tables_check(block_table, context_lens, a.S, a.MB, a.B, a.NB, a.max_ctx);
+  d.cu_q_lens = cu_q_lens;
+  d.total_q = total_q;
+  if (int dst = debug_gate(d, stream, "paged_attention_prefill_chunk")) return dst;
   return hip_status(pkv::launch_prefill(a, static_cast<hipStream_t>(stream)),
                     "paged_attention_prefill_chunk");
 }
@@ -769,7 +864,8 @@ int pkv_profile_read(const char* kernel_name, double* total_ms, long long* launc
 }
 
 const char* pkv_profile_kernel_names(void) {
-  return "kv_cache_write,decode_partition,decode_reduce,prefill_chunk,copy_blocks,read_probe";
+  return "kv_cache_write,decode_partition,decode_reduce,prefill_chunk,copy_blocks,read_probe,"
+         "debug_check";
 }
 
 }  // extern "C"

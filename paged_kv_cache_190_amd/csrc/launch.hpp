@@ -19,7 +19,8 @@ enum KernelId {
   K_PREFILL = 3,
   K_COPY_BLOCKS = 4,
   K_READ_PROBE = 5,
-  K_COUNT = 6
+  K_DEBUG_CHECK = 6,
+  K_COUNT = 7
 };
 const char* kernel_name(int id);
 
@@ -150,6 +151,25 @@ struct ReadProbeArgs {
   int min_tiles;
 };
 hipError_t launch_read_probe(const ReadProbeArgs& a, hipStream_t stream);
+
+// Debug builds (PKV_DEBUG=1): which device arrays a call hands over, for the check kernels of
+// debug.hip. Null pointers and zero counts skip a check. debug_check launches the checks on the
+// stream, waits for them and returns the OR of the DebugBits (checks.hpp) they found in *bits.
+struct DebugCheckArgs {
+  const int32_t* block_table = nullptr;
+  const int32_t* context_lens = nullptr;
+  int S = 0, MB = 0, B = 0, NB = 0, max_ctx = 0;
+  const int32_t* slots = nullptr;
+  int T = 0, slot_NB = 0;
+  const int32_t* cu_q_lens = nullptr;
+  int total_q = 0;
+  const int32_t* group_start = nullptr;
+  const int32_t* group_prefix_len = nullptr;
+  int NG = 0, max_prefix = 0;
+  const int32_t* pairs = nullptr;
+  int n_pairs = 0, src_nb = 0, dst_nb = 0;
+};
+hipError_t debug_check(const DebugCheckArgs& a, hipStream_t stream, unsigned* bits);
 
 struct PrefillArgs {
   void* out;

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 def test_version_and_strings():
     L = bd.lib()
     assert L.pkv_abi_version() == 2
-    for st in range(6):
+    for st in range(7):
         assert L.pkv_status_string(st) != b"unknown status"
     assert L.pkv_status_string(99) == b"unknown status"
 
