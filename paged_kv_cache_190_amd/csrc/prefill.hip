@@ -16,12 +16,12 @@
 // with keys 16*hb .. 16*hb+15, in order: then its P values are the B operand of the second
 // product as they stand, and its V^T operand is 16 contiguous bytes of the dim-major V tile.
 // K/V tiles go from HBM straight into LDS (global_load_lds: each lane's 16 bytes land at its own
-// place in the wave's 1 KiB of LDS, no register round trip) through a ring of six stages, so
-// five tiles are in flight while one is multiplied (104 KB of LDS: one workgroup per CU, two
-// waves per SIMD). Waits count those DMAs only (explicit
-// s_waitcnt and a bare barrier per tile); LDS rows are XOR-swizzled instead of padded, so that
-// the 128-bit LDS reads are free of bank conflicts. Tiles wholly above a wave's causal diagonal
-// are skipped; only diagonal tiles apply the mask.
+// place in the wave's 1 KiB of LDS, no register round trip) through a ring of eight stages
+// (128 KB of LDS: one workgroup per CU, two waves per SIMD). The ring advances two tiles per
+// workgroup barrier, with up to six tiles in flight. Waits count those DMAs only (explicit
+// s_waitcnt; block ids come through scalar loads, which count elsewhere); LDS rows are
+// XOR-swizzled instead of padded, so that the 128-bit LDS reads are free of bank conflicts.
+// Tiles wholly above a wave's causal diagonal are skipped; only diagonal tiles apply the mask.
 // Workgroups are numbered so that the XCDs (the GPU deals consecutive workgroups round-robin to
 // its eight XCDs, each with its own L2) get equal shares of the work, with the row tiles of one
 // (sequence, KV head) on the same XCD and the tiles with the most keys first.
@@ -58,6 +58,8 @@ __device__ __forceinline__ int kswz(int row) {
 __device__ __forceinline__ int vswz(int d) { return (d >> 2) & 3; }  // 4 chunks, 4 rows per line
 
 constexpr int kPrefillWaves = 8;  // waves per workgroup
+constexpr int kStages = 8;        // K/V tiles in the LDS ring
+constexpr int kTilesPerBarrier = 2;  // tiles the ring advances per workgroup barrier
 constexpr int kRankMax = 64;       // largest batch whose sequences are ranked by work
 
 // The sequence of rank j when sequences are ordered by decreasing c * (2n - c) (chunk length c,
@@ -99,7 +101,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
   constexpr int DT = D / 32;             // PV output tiles
   constexpr int NW = kPrefillWaves;
   constexpr int NT = 64 * NW;            // threads
-  constexpr int NS = 6;                  // pipeline stages (prefetch distance NS - 1)
+  constexpr int NS = kStages;            // pipeline stages
   constexpr int KROW = 2 * D;            // bytes of one K row in LDS
   constexpr int CPR = D / 8;             // 16-byte chunks per K row
   constexpr int K_BYTES = 32 * KROW;     // K tile [32 keys][D]
@@ -109,10 +111,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
   constexpr int LPT = STAGE / 1024 / NW; // DMA instructions per wave (and per thread) per tile
   static_assert(LPT >= 1 && (STAGE / 1024) % NW == 0, "DMA work must split evenly over waves");
   static_assert(NS * STAGE >= 8 * kRankMax + 4, "the ranking scratch must fit the stages");
-  constexpr int kIdCap = 2048;           // block ids staged in LDS at a time
-  // One LDS object holds the stages and, after them, the block-id window.
-  __shared__ __attribute__((aligned(16))) unsigned char smem[NS * STAGE + 4 * kIdCap];
-  int32_t* ids = reinterpret_cast<int32_t*>(smem + NS * STAGE);
+  __shared__ __attribute__((aligned(16))) unsigned char smem[NS * STAGE];
 
   // XCD-aware numbering. Workgroup b is dispatched to XCD b % 8, and each XCD works through its
   // share in order. The (head group, sequence) pairs are dealt round-robin to the XCDs (with 8
@@ -164,7 +163,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
   const int ntiles = (kend + 31) >> 5;
   const int nblk = (n + B - 1) / B;
   const int32_t* bt = block_table + static_cast<int64_t>(s) * MB;
-  const int64_t blk_stride = static_cast<int64_t>(Hkv) * B * D;
+  const uint32_t blk_stride = static_cast<uint32_t>(Hkv) * B * D;  // < 2^32
   const uint16_t* kg = kpool + static_cast<int64_t>(g) * B * D;
   const uint16_t* vg = vpool + static_cast<int64_t>(g) * B * D;
 
@@ -181,30 +180,15 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
       qf[kk] = row_valid ? (load16(qrow + 16 * kk) ^ flip) : u32x4{0u, 0u, 0u, 0u};
   }
 
-  // Block ids are staged in LDS, a window of kIdCap logical blocks at a time, so the tile loop
-  // reads them from LDS and issues no vector load of its own (its waits count DMAs only).
-  // Tiles are issued in order; when one needs a block past the window, the window moves: the
-  // pipeline is drained, all waves pass a barrier, and the ids are reloaded.
-  int win = 0;
-  auto load_window = [&](int first) {
-    const int cnt = min(kIdCap, nblk - first);
-    int v[kIdCap / NT];
-#pragma unroll
-    for (int j = 0; j < kIdCap / NT; ++j)  // all loads in flight before any store
-      v[j] = (tid + NT * j < cnt) ? bt[first + tid + NT * j] : 0;
-#pragma unroll
-    for (int j = 0; j < kIdCap / NT; ++j)
-      if (tid + NT * j < cnt) ids[tid + NT * j] = v[j];
-    // Every load above has landed on every path out of here; otherwise the compiler carries
-    // them as pending into the tile loop and drains all DMAs when it next reuses a register.
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  };
-  load_window(0);
-  // q and the first ids must have arrived before the tile DMAs start counting in the same
-  // counter; the barrier publishes the ids.
+  // q must have arrived before the tile DMAs start counting in the same counter; the barrier
+  // keeps the first DMAs out of the ranking scratch until every wave has read its result.
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
-  auto block_id = [&](int lb) -> int64_t { return ids[min(lb, nblk - 1) - win]; };
+  // Block ids are wave-uniform: each is one scalar load (through the scalar cache; its wait
+  // counts in lgkmcnt, so the tile loop's vector-memory waits still count DMAs only).
+  auto block_id = [&](int lb) -> uint32_t {
+    return static_cast<uint32_t>(bt[__builtin_amdgcn_readfirstlane(min(lb, nblk - 1))]);
+  };
 
   // DMA of key tile t into stage t % NS: STAGE / 1 KiB instructions, LPT per wave; instruction
   // c (= LPT * wave + j) fills bytes c KiB .. of the stage. K instructions (c < KC) cover
@@ -234,20 +218,15 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
   auto issue = [&](int t) {
     unsigned char* st = smem + (t % NS) * STAGE;
     const int lb0 = (32 * t) / B;
-    if (min(lb0 + 1, nblk - 1) - win >= kIdCap) {  // uniform: every thread issues every tile
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-      __syncthreads();
-      win = lb0;
-      load_window(win);
-      __syncthreads();
-    }
-    const int64_t id0 = block_id(lb0);
-    const int64_t id1 = (B == 16) ? block_id(lb0 + 1) : id0;
+    // both candidate block offsets are wave-uniform products (ids are non-negative and the
+    // block stride fits 32 bits); a lane only selects one and adds its own offset
+    const uint64_t o0 = static_cast<uint64_t>(block_id(lb0)) * blk_stride;
+    const uint64_t o1 = (B == 16) ? static_cast<uint64_t>(block_id(lb0 + 1)) * blk_stride : o0;
     // (The source pointer is a named variable: given a conditional expression directly, the
     // builtin makes clang drop this kernel's host-side launch stub without a diagnostic.)
 #pragma unroll
     for (int j = 0; j < LPT; ++j) {
-      const uint16_t* src = (sk[j] ? kg : vg) + (ssel[j] ? id1 : id0) * blk_stride + soff[j];
+      const uint16_t* src = (sk[j] ? kg : vg) + (ssel[j] ? o1 : o0) + soff[j];
       __builtin_amdgcn_global_load_lds(src, st + (LPT * wave + j) * 1024, 16, 0, 0);
     }
   };
@@ -343,23 +322,32 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
       for (int j = 0; j < 2; ++j) acc[dt] = mfma32x32x16(va[dt][j], pb[j], acc[dt]);
   };
 
-  // Pipeline: tiles t+1 .. t+NS-2 stay in flight while tile t is waited for; one barrier per
-  // tile both publishes tile t and frees the stage that tile t+NS-1 is then loaded into.
+  // Pipeline: the ring advances TPB tiles per workgroup barrier. A wave waits for its DMAs of
+  // tiles t .. t+TPB-1, leaving the tiles issued after them in flight; the barrier publishes
+  // those tiles and frees the stages of the TPB tiles computed before it, into which tiles
+  // t+NS-TPB .. t+NS-1 are issued; then tiles t .. t+TPB-1 are computed. Fewer barriers and
+  // issue phases per tile than one per tile, with up to NS-TPB tiles in flight.
+  constexpr int TPB = kTilesPerBarrier;
+  constexpr int PRE = NS - TPB;  // tiles issued ahead of the loop
+  static_assert(PRE - TPB >= 0 && PRE - TPB <= 4, "one wait per possible depth below");
 #pragma unroll
-  for (int t = 0; t < NS - 1; ++t)
+  for (int t = 0; t < PRE; ++t)
     if (t < ntiles) issue(t);
-  for (int t = 0; t < ntiles; ++t) {
-    // wait for tile t, leaving the `ahead` tiles issued after it in flight
-    const int ahead = min(NS - 2, ntiles - 1 - t);
-    static_assert(NS - 2 <= 4, "one wait per possible depth below");
+  for (int t = 0; t < ntiles; t += TPB) {
+    // issued so far: tiles 0 .. min(t + PRE, ntiles) - 1; needed now: t .. t+TPB-1
+    const int ahead = min(t + PRE, ntiles) - min(t + TPB, ntiles);
     if (ahead >= 4) __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * LPT));
     else if (ahead == 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * LPT));
     else if (ahead == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPT));
     else if (ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPT));
     else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_barrier();
-    if (t + NS - 1 < ntiles) issue(t + NS - 1);
-    compute(t);
+#pragma unroll
+    for (int k = 0; k < TPB; ++k)
+      if (t + PRE + k < ntiles) issue(t + PRE + k);
+#pragma unroll
+    for (int k = 0; k < TPB; ++k)
+      if (t + k < ntiles) compute(t + k);
   }
 
   if (!wave_active) return;
