@@ -166,6 +166,8 @@ def run_blocks(args, w):
     def step():
         bd.kv_cache_copy_blocks(*ends, tp)
 
+    if args.calibrate_copy:
+        calibration_copies(dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -246,6 +248,17 @@ def cpu_baseline_blocks(w, src, budget_s):
             "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"oracle block copy of {done} of {len(src)} blocks in calls of 256 "
                       f"({dt:.2f} s, NumPy, one thread); bytes of the blocks copied / time"}
+
+def calibration_copies(dev):
+    """Plain device copies of known size, for scaling rocprofv3's byte counters."""
+    import torch
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
 
 def to_dev(a):
     import numpy as np
@@ -357,13 +370,7 @@ def run(args, w):
                                              max_context_len=w.max_context_len)
 
     if args.calibrate_copy:
-        # A plain device copy of known size, for scaling rocprofv3's byte counters.
-        src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copies(dev)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -673,8 +680,13 @@ def cpu_baseline(w, budget_s):
 
 # ------------------------------------------------------------------- rocprofv3 summaries
 
+# Traced runs warm up for TRACE_WARMUP steps: compute-bound kernels run slower until the GPU's
+# clocks have ramped up (the chunked prefill from about 420 down to 340 us over its first few
+# dozen launches), so the summary also averages only the dispatches after the warmup.
+TRACE_WARMUP = 100
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats -f csv -d {d} -o run -- "
-             "python3 bench.py --workload {w} --steps 20 --warmup 5 --no-cpu-baseline")
+             "python3 bench.py --workload {w} --steps 20 --warmup " + str(TRACE_WARMUP) +
+             " --no-cpu-baseline")
 PMC_CMD = ("rocprofv3 --pmc {c} -f csv -d {d} -o run -- python3 bench.py "
            "--workload {w} --steps 10 --warmup 2 --no-cpu-baseline --calibrate-copy")
 
@@ -705,16 +717,27 @@ def _rel(d):
 
 def summarize_trace(d, workload):
     rows = _csv(_find(d, "kernel_stats.csv"))
+    launches = {}
+    for r in _csv(_find(d, "kernel_trace.csv")):  # dispatch order
+        launches.setdefault(_short(r["Kernel_Name"]), []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     cmd = TRACE_CMD.format(w=workload, d=_rel(d))
     out = [f"# Kernel durations, workload {workload}", "",
            "rocprofv3 kernel trace of `bench.py` on one MI355X (gfx950).", "",
            f"Command (from the repository root): `{cmd}`", "",
-           "| kernel | calls | average us | min us | max us | share of GPU time |",
-           "|---|---|---|---|---|---|"]
+           "Columns 2-6 are rocprofv3's statistics over every dispatch; the last column averages "
+           f"the same trace's dispatches after the first {TRACE_WARMUP} of each kernel (the "
+           "bench's warmup steps).", "",
+           "| kernel | calls | average us | min us | max us | share of GPU time | "
+           "average us after warmup |",
+           "|---|---|---|---|---|---|---|"]
     for r in rows:
-        out.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} "
+        k = _short(r["Name"])
+        after = launches.get(k, [])[TRACE_WARMUP:]
+        steady = f"{sum(after) / len(after):.2f} ({len(after)})" if after else "-"
+        out.append(f"| `{k}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} "
                    f"| {float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
-                   f"{float(r['Percentage']):.1f}% |")
+                   f"{float(r['Percentage']):.1f}% | {steady} |")
     out += ["", "`__amd_rocclr_copyBuffer` is the set-up copies of the inputs to the device "
             "(not timed by the bench)."]
     path = os.path.join(ROOT, "profiles", f"kernels_{workload}.md")
