@@ -124,9 +124,9 @@ unsigned pkv_debug_found(void);
  * A pure bit copy: no rounding, NaN payloads preserved. Slots not named are left untouched.
  * T == 0 is a no-op that returns PKV_OK.
  */
-int pkv_kv_cache_write(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
-                       const int32_t* slot_mapping, int T, int num_kv_heads, int head_dim,
-                       int block_size, int num_blocks, int dtype, void* stream);
+pkv_status pkv_kv_cache_write(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                              const int32_t* slot_mapping, int T, int num_kv_heads, int head_dim,
+                              int block_size, int num_blocks, int dtype, void* stream);
 
 /*
  * pkv_kv_cache_write_fp8 -- pkv_kv_cache_write into E4M3 pools, quantising on the way.
@@ -143,10 +143,10 @@ int pkv_kv_cache_write(const void* k_new, const void* v_new, void* k_pool, void*
  * to +-448; the sign bit follows the quotient's sign; NaN stores 0x7F. Placement, skipped
  * slots and preconditions are those of pkv_kv_cache_write.
  */
-int pkv_kv_cache_write_fp8(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
-                           const int32_t* slot_mapping, int T, int num_kv_heads, int head_dim,
-                           int block_size, int num_blocks, int in_dtype, float k_scale,
-                           float v_scale, void* stream);
+pkv_status pkv_kv_cache_write_fp8(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                                  const int32_t* slot_mapping, int T, int num_kv_heads,
+                                  int head_dim, int block_size, int num_blocks, int in_dtype,
+                                  float k_scale, float v_scale, void* stream);
 
 /*
  * pkv_kv_cache_copy_blocks -- copy whole physical blocks between two pools (or inside one).
@@ -165,10 +165,10 @@ int pkv_kv_cache_write_fp8(const void* k_new, const void* v_new, void* k_pool, v
  * Preconditions (unchecked, device data): ids within their pools; destination blocks pairwise
  * distinct; within one pool, no destination is also a source. n_pairs == 0 is a no-op.
  */
-int pkv_kv_cache_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
-                             const int32_t* block_pairs, int n_pairs, int num_kv_heads,
-                             int head_dim, int block_size, int src_num_blocks,
-                             int dst_num_blocks, int dtype, void* stream);
+pkv_status pkv_kv_cache_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                                    const int32_t* block_pairs, int n_pairs, int num_kv_heads,
+                                    int head_dim, int block_size, int src_num_blocks,
+                                    int dst_num_blocks, int dtype, void* stream);
 
 /*
  * Block manager -- host-side allocator of physical blocks with reference counts, for the
@@ -196,18 +196,18 @@ int pkv_kv_cache_copy_blocks(const void* src_k, const void* src_v, void* dst_k, 
  *   pkv_bm_refcount(bm, block, &count)
  */
 typedef struct pkv_block_manager pkv_block_manager;
-int pkv_bm_create(int num_blocks, int block_size, pkv_block_manager** out);
+pkv_status pkv_bm_create(int num_blocks, int block_size, pkv_block_manager** out);
 void pkv_bm_destroy(pkv_block_manager* bm);
 int pkv_bm_num_free(const pkv_block_manager* bm);
-int pkv_bm_add(pkv_block_manager* bm, int64_t seq);
-int pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child);
-int pkv_bm_append(pkv_block_manager* bm, int64_t seq, int n_tokens, int32_t* slots,
-                  int32_t* copies, int max_copies, int* n_copies);
-int pkv_bm_free(pkv_block_manager* bm, int64_t seq);
-int pkv_bm_context_len(const pkv_block_manager* bm, int64_t seq, int* len);
-int pkv_bm_block_table(const pkv_block_manager* bm, int64_t seq, int32_t* table, int capacity,
-                       int* n_blocks);
-int pkv_bm_refcount(const pkv_block_manager* bm, int block, int* count);
+pkv_status pkv_bm_add(pkv_block_manager* bm, int64_t seq);
+pkv_status pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child);
+pkv_status pkv_bm_append(pkv_block_manager* bm, int64_t seq, int n_tokens, int32_t* slots,
+                         int32_t* copies, int max_copies, int* n_copies);
+pkv_status pkv_bm_free(pkv_block_manager* bm, int64_t seq);
+pkv_status pkv_bm_context_len(const pkv_block_manager* bm, int64_t seq, int* len);
+pkv_status pkv_bm_block_table(const pkv_block_manager* bm, int64_t seq, int32_t* table,
+                              int capacity, int* n_blocks);
+pkv_status pkv_bm_refcount(const pkv_block_manager* bm, int block, int* count);
 
 /*
  * pkv_decode_partition_size -- the fixed partition size, in tokens, that
@@ -268,13 +268,14 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads
  * out_dtype may differ from dtype (e.g. bf16 inputs with an fp32 output); the bf16 output is
  * rounded to nearest even from the fp32 result.
  */
-int pkv_paged_attention_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
-                               const int32_t* block_table, const int32_t* context_lens,
-                               int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                               int block_size, int max_blocks_per_seq, int num_blocks,
-                               float scale, int max_context_len, int partition_size,
-                               int num_waves, void* workspace, size_t workspace_bytes, int dtype,
-                               int out_dtype, void* stream);
+pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_pool,
+                                      const void* v_pool, const int32_t* block_table,
+                                      const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                      int num_kv_heads, int head_dim, int block_size,
+                                      int max_blocks_per_seq, int num_blocks, float scale,
+                                      int max_context_len, int partition_size, int num_waves,
+                                      void* workspace, size_t workspace_bytes, int dtype,
+                                      int out_dtype, void* stream);
 
 /*
  * pkv_kv_cache_write_and_decode -- pkv_kv_cache_write of each sequence's new token followed by
@@ -290,17 +291,18 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_pool, con
  *   k_pool, v_pool  read, and written at the new tokens' slots
  *   workspace     pkv_decode_workspace_size(..., partition_size = 0, PKV_BF16) bytes
  * Other arguments (num_waves included), preconditions and errors as for
- * pkv_paged_attention_decode with the balanced split. The attention takes the newest token's K/V from k_new / v_new, and
- * the wave that does so also stores them into the pool, so no kernel has to wait for the write.
+ * pkv_paged_attention_decode with the balanced split. The attention takes the newest token's
+ * K/V from k_new / v_new, and the wave that does so also stores them into the pool, so no
+ * kernel has to wait for the write.
  */
-int pkv_kv_cache_write_and_decode(void* out, const void* q, const void* k_new,
-                                  const void* v_new, const int32_t* slot_mapping, void* k_pool,
-                                  void* v_pool, const int32_t* block_table,
-                                  const int32_t* context_lens, int num_seqs, int num_q_heads,
-                                  int num_kv_heads, int head_dim, int block_size,
-                                  int max_blocks_per_seq, int num_blocks, float scale,
-                                  int max_context_len, int num_waves, void* workspace,
-                                  size_t workspace_bytes, int out_dtype, void* stream);
+pkv_status pkv_kv_cache_write_and_decode(void* out, const void* q, const void* k_new,
+                                         const void* v_new, const int32_t* slot_mapping,
+                                         void* k_pool, void* v_pool, const int32_t* block_table,
+                                         const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                         int num_kv_heads, int head_dim, int block_size,
+                                         int max_blocks_per_seq, int num_blocks, float scale,
+                                         int max_context_len, int num_waves, void* workspace,
+                                         size_t workspace_bytes, int out_dtype, void* stream);
 
 /*
  * pkv_paged_attention_decode_fp8 -- pkv_paged_attention_decode over E4M3 pools.
@@ -310,17 +312,18 @@ int pkv_kv_cache_write_and_decode(void* out, const void* q, const void* k_new,
  * v_scale (finite, > 0); K's value is code value * k_scale, V's is code value * v_scale, and
  * with those values the result is pkv_paged_attention_decode's. q is bf16; out_dtype PKV_BF16
  * or PKV_F32. The context is always split the balanced way over num_waves waves (0 = the
- * default, 1024); workspace: pkv_decode_workspace_size(..., dtype = PKV_FP8_E4M3) bytes. Other arguments, preconditions and errors as for
- * pkv_paged_attention_decode. Unwritten slots may hold any code, NaN included.
+ * default, 1024); workspace: pkv_decode_workspace_size(..., dtype = PKV_FP8_E4M3) bytes.
+ * Other arguments, preconditions and errors as for pkv_paged_attention_decode. Unwritten slots
+ * may hold any code, NaN included.
  */
-int pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_pool,
-                                   const void* v_pool, const int32_t* block_table,
-                                   const int32_t* context_lens, int num_seqs, int num_q_heads,
-                                   int num_kv_heads, int head_dim, int block_size,
-                                   int max_blocks_per_seq, int num_blocks, float scale,
-                                   float k_scale, float v_scale, int max_context_len,
-                                   int num_waves, void* workspace, size_t workspace_bytes,
-                                   int out_dtype, void* stream);
+pkv_status pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_pool,
+                                          const void* v_pool, const int32_t* block_table,
+                                          const int32_t* context_lens, int num_seqs,
+                                          int num_q_heads, int num_kv_heads, int head_dim,
+                                          int block_size, int max_blocks_per_seq, int num_blocks,
+                                          float scale, float k_scale, float v_scale,
+                                          int max_context_len, int num_waves, void* workspace,
+                                          size_t workspace_bytes, int out_dtype, void* stream);
 
 /*
  * pkv_paged_attention_decode_shared_prefix -- decode for batches whose sequences share
@@ -352,14 +355,19 @@ int pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_pool,
 size_t pkv_decode_shared_prefix_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
                                                int head_dim, int max_context_len,
                                                int max_prefix_len, int kv_dtype);
-int pkv_paged_attention_decode_shared_prefix(
-    void* out, const void* q, const void* k_pool, const void* v_pool,
-    const int32_t* block_table, const int32_t* context_lens, const int32_t* group_start,
-    const int32_t* group_prefix_len, int num_groups, int max_group_size, int max_prefix_len,
-    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-    int max_blocks_per_seq, int num_blocks, float scale, int max_context_len, int num_waves,
-    int kv_dtype, float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
-    int out_dtype, void* stream);
+pkv_status pkv_paged_attention_decode_shared_prefix(void* out, const void* q, const void* k_pool,
+                                                    const void* v_pool, const int32_t* block_table,
+                                                    const int32_t* context_lens,
+                                                    const int32_t* group_start,
+                                                    const int32_t* group_prefix_len, int num_groups,
+                                                    int max_group_size, int max_prefix_len,
+                                                    int num_seqs, int num_q_heads, int num_kv_heads,
+                                                    int head_dim, int block_size,
+                                                    int max_blocks_per_seq, int num_blocks,
+                                                    float scale, int max_context_len, int num_waves,
+                                                    int kv_dtype, float k_scale, float v_scale,
+                                                    void* workspace, size_t workspace_bytes,
+                                                    int out_dtype, void* stream);
 
 /*
  * pkv_paged_attention_prefill_chunk -- a causal chunk of query tokens against the paged cache.
@@ -381,14 +389,14 @@ int pkv_paged_attention_decode_shared_prefix(
  *   max_q_len, max_context_len  host bounds on c and n (0 = total_q and
  *                               max_blocks_per_seq*block_size)
  */
-int pkv_paged_attention_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
-                                      const int32_t* context_lens, const void* k_pool,
-                                      const void* v_pool, const int32_t* block_table,
-                                      int num_seqs, int total_q, int num_q_heads,
-                                      int num_kv_heads, int head_dim, int block_size,
-                                      int max_blocks_per_seq, int num_blocks, float scale,
-                                      int max_q_len, int max_context_len, int dtype,
-                                      int out_dtype, void* stream);
+pkv_status pkv_paged_attention_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
+                                             const int32_t* context_lens, const void* k_pool,
+                                             const void* v_pool, const int32_t* block_table,
+                                             int num_seqs, int total_q, int num_q_heads,
+                                             int num_kv_heads, int head_dim, int block_size,
+                                             int max_blocks_per_seq, int num_blocks, float scale,
+                                             int max_q_len, int max_context_len, int dtype,
+                                             int out_dtype, void* stream);
 
 /*
  * pkv_paged_attention_decode_noalloc -- pkv_paged_attention_decode (bf16 inputs, balanced
@@ -406,13 +414,13 @@ int pkv_paged_attention_prefill_chunk(void* out, const void* q, const int32_t* c
  *   contents (nothing in it has to start at zero): calls that overlap on one GPU (other streams,
  *   other threads) race and give wrong results; calls in order on one stream do not.
  */
-int pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_pool,
-                                       const void* v_pool, const int32_t* block_table,
-                                       const int32_t* context_lens, int num_seqs,
-                                       int num_q_heads, int num_kv_heads, int head_dim,
-                                       int block_size, int max_blocks_per_seq, int num_blocks,
-                                       float scale, int max_context_len, int num_waves,
-                                       int out_dtype, void* stream);
+pkv_status pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_pool,
+                                              const void* v_pool, const int32_t* block_table,
+                                              const int32_t* context_lens, int num_seqs,
+                                              int num_q_heads, int num_kv_heads, int head_dim,
+                                              int block_size, int max_blocks_per_seq,
+                                              int num_blocks, float scale, int max_context_len,
+                                              int num_waves, int out_dtype, void* stream);
 
 /*
  * pkv_decode_read_probe -- measurement only, not part of the attention path. Launches the
@@ -426,11 +434,11 @@ int pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_p
  */
 size_t pkv_decode_read_probe_sink_size(int num_seqs, int num_q_heads, int num_kv_heads,
                                        int max_context_len, int num_waves);
-int pkv_decode_read_probe(const void* k_pool, const void* v_pool, const int32_t* block_table,
-                          const int32_t* context_lens, int num_seqs, int num_q_heads,
-                          int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
-                          int num_blocks, int max_context_len, int num_waves, void* sink,
-                          size_t sink_bytes, void* stream);
+pkv_status pkv_decode_read_probe(const void* k_pool, const void* v_pool, const int32_t* block_table,
+                                 const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                 int num_kv_heads, int head_dim, int block_size,
+                                 int max_blocks_per_seq, int num_blocks, int max_context_len,
+                                 int num_waves, void* sink, size_t sink_bytes, void* stream);
 
 /*
  * Kernel timing (library plumbing, for benchmarks). For every kernel selected by the mask, the
@@ -445,9 +453,9 @@ int pkv_decode_read_probe(const void* k_pool, const void* v_pool, const int32_t*
  *   enable/reset; returns PKV_ERR_INVALID_ARG for an unknown name.
  *   pkv_profile_kernel_names(): the kernel names, comma-separated, in bit order.
  */
-int pkv_profile_enable(int kernel_mask);
-int pkv_profile_reset(void);
-int pkv_profile_read(const char* kernel_name, double* total_ms, long long* launches);
+pkv_status pkv_profile_enable(int kernel_mask);
+pkv_status pkv_profile_reset(void);
+pkv_status pkv_profile_read(const char* kernel_name, double* total_ms, long long* launches);
 const char* pkv_profile_kernel_names(void);
 
 #ifdef __cplusplus

@@ -28,7 +28,7 @@ thread_local unsigned g_debug_found = 0;  // DebugBits of this thread's last che
 constexpr bool kDebugBuild = PKV_DEBUG != 0;
 }  // namespace
 
-int pkv::fail(int status, const char* fmt, ...) {
+pkv_status pkv::fail(pkv_status status, const char* fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -42,7 +42,7 @@ namespace {
 
 using pkv::fail;
 
-int hip_status(hipError_t e, const char* what) {
+pkv_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return PKV_OK;
   return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -50,14 +50,14 @@ int hip_status(hipError_t e, const char* what) {
 // Debug builds: the call's device arrays are checked on the device first (debug.hip); a call
 // whose arrays break the documented preconditions launches nothing and returns
 // PKV_ERR_DEVICE_ARG. Release builds: nothing.
-int debug_gate(const pkv::DebugCheckArgs& d, void* stream, const char* what) {
+pkv_status debug_gate(const pkv::DebugCheckArgs& d, void* stream, const char* what) {
   if constexpr (!kDebugBuild) {
     (void)d, (void)stream, (void)what;
     return PKV_OK;
   } else {
     unsigned bits = 0;
-    if (int st = hip_status(pkv::debug_check(d, static_cast<hipStream_t>(stream), &bits), what))
-      return st;
+    const hipError_t e = pkv::debug_check(d, static_cast<hipStream_t>(stream), &bits);
+    if (pkv_status st = hip_status(e, what)) return st;
     g_debug_found = bits;
     if (!bits) return PKV_OK;
     std::string names;
@@ -226,7 +226,7 @@ BalancedPlan balanced_plan(int S, int Hq, int Hkv, int D, int max_ctx, int waves
   return pl;
 }
 
-int check_common(int Hq, int Hkv, int D, int B, int dtype, int out_dtype) {
+pkv_status check_common(int Hq, int Hkv, int D, int B, int dtype, int out_dtype) {
   if (Hq <= 0 || Hkv <= 0) return fail(PKV_ERR_INVALID_ARG, "head counts must be positive");
   if (Hq % Hkv != 0)
     return fail(PKV_ERR_UNSUPPORTED, "num_q_heads %d is not a multiple of num_kv_heads %d", Hq,
@@ -264,9 +264,9 @@ int pkv_debug_build(void) { return kDebugBuild ? 1 : 0; }
 
 unsigned pkv_debug_found(void) { return g_debug_found; }
 
-int pkv_kv_cache_write(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
-                       const int32_t* slot_mapping, int T, int num_kv_heads, int head_dim,
-                       int block_size, int num_blocks, int dtype, void* stream) {
+pkv_status pkv_kv_cache_write(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                              const int32_t* slot_mapping, int T, int num_kv_heads, int head_dim,
+                              int block_size, int num_blocks, int dtype, void* stream) {
   if (T < 0) return fail(PKV_ERR_INVALID_ARG, "T = %d is negative", T);
   if (T == 0) return PKV_OK;
   if (!k_new || !v_new || !k_pool || !v_pool || !slot_mapping)
@@ -289,14 +289,14 @@ int pkv_kv_cache_write(const void* k_new, const void* v_new, void* k_pool, void*
   d.T = T;
   d.slot_NB = num_blocks;
   d.B = block_size;
-  if (int st = debug_gate(d, stream, "kv_cache_write")) return st;
+  if (pkv_status st = debug_gate(d, stream, "kv_cache_write")) return st;
   return hip_status(pkv::launch_kv_write(a, static_cast<hipStream_t>(stream)), "kv_cache_write");
 }
 
-int pkv_kv_cache_write_fp8(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
-                           const int32_t* slot_mapping, int T, int num_kv_heads, int head_dim,
-                           int block_size, int num_blocks, int in_dtype, float k_scale,
-                           float v_scale, void* stream) {
+pkv_status pkv_kv_cache_write_fp8(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                                  const int32_t* slot_mapping, int T, int num_kv_heads,
+                                  int head_dim, int block_size, int num_blocks, int in_dtype,
+                                  float k_scale, float v_scale, void* stream) {
   if (T < 0) return fail(PKV_ERR_INVALID_ARG, "T = %d is negative", T);
   if (T == 0) return PKV_OK;
   if (!k_new || !v_new || !k_pool || !v_pool || !slot_mapping)
@@ -322,7 +322,7 @@ int pkv_kv_cache_write_fp8(const void* k_new, const void* v_new, void* k_pool, v
   d.T = T;
   d.slot_NB = num_blocks;
   d.B = block_size;
-  if (int st = debug_gate(d, stream, "kv_cache_write_fp8")) return st;
+  if (pkv_status st = debug_gate(d, stream, "kv_cache_write_fp8")) return st;
   return hip_status(pkv::launch_kv_write_fp8(a, in_dtype == PKV_BF16, k_scale, v_scale,
                                              static_cast<hipStream_t>(stream)),
                     "kv_cache_write_fp8");
@@ -332,7 +332,7 @@ namespace {
 // A pool handed to the copy kernel may be device memory or pinned host memory; anything else
 // (pageable host memory, a stale pointer) would fault in the kernel, so it is refused here.
 // Pinned memory is accepted only where the device sees it at the same address.
-int check_kernel_visible(const void* p, const char* name) {
+pkv_status check_kernel_visible(const void* p, const char* name) {
   hipPointerAttribute_t at{};
   if (hipPointerGetAttributes(&at, p) != hipSuccess) {
     (void)hipGetLastError();
@@ -347,10 +347,10 @@ int check_kernel_visible(const void* p, const char* name) {
 }
 }  // namespace
 
-int pkv_kv_cache_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
-                             const int32_t* block_pairs, int n_pairs, int num_kv_heads,
-                             int head_dim, int block_size, int src_num_blocks,
-                             int dst_num_blocks, int dtype, void* stream) {
+pkv_status pkv_kv_cache_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                                    const int32_t* block_pairs, int n_pairs, int num_kv_heads,
+                                    int head_dim, int block_size, int src_num_blocks,
+                                    int dst_num_blocks, int dtype, void* stream) {
   if (n_pairs < 0) return fail(PKV_ERR_INVALID_ARG, "n_pairs = %d is negative", n_pairs);
   if (n_pairs == 0) return PKV_OK;
   if (!src_k || !src_v || !dst_k || !dst_v || !block_pairs)
@@ -367,7 +367,7 @@ int pkv_kv_cache_copy_blocks(const void* src_k, const void* src_v, void* dst_k, 
   const void* ptrs[5] = {src_k, src_v, dst_k, dst_v, block_pairs};
   const char* names[5] = {"src_k", "src_v", "dst_k", "dst_v", "block_pairs"};
   for (int i = 0; i < 5; ++i)
-    if (int st = check_kernel_visible(ptrs[i], names[i])) return st;
+    if (pkv_status st = check_kernel_visible(ptrs[i], names[i])) return st;
   pkv::CopyBlocksArgs a{src_k, src_v, dst_k, dst_v, block_pairs, n_pairs, num_kv_heads,
                         head_dim, block_size, elem_bytes(dtype)};
   pkv::DebugCheckArgs d;
@@ -375,7 +375,7 @@ int pkv_kv_cache_copy_blocks(const void* src_k, const void* src_v, void* dst_k, 
   d.n_pairs = n_pairs;
   d.src_nb = src_num_blocks;
   d.dst_nb = dst_num_blocks;
-  if (int st = debug_gate(d, stream, "kv_cache_copy_blocks")) return st;
+  if (pkv_status st = debug_gate(d, stream, "kv_cache_copy_blocks")) return st;
   return hip_status(pkv::launch_copy_blocks(a, static_cast<hipStream_t>(stream)),
                     "kv_cache_copy_blocks");
 }
@@ -409,7 +409,7 @@ namespace {
 
 // Balanced split set-up: the plan for a's sizes, and the partial buffers carved out of the
 // caller's workspace.
-int setup_balanced(pkv::DecodeArgs& a, void* workspace, size_t workspace_bytes,
+pkv_status setup_balanced(pkv::DecodeArgs& a, void* workspace, size_t workspace_bytes,
                    int default_waves, int num_waves, int extra_slots = 0) {
   if (num_waves < 0 || num_waves > kMaxDecodeWaves)
     return fail(PKV_ERR_INVALID_ARG, "num_waves %d outside [0, %d]", num_waves, kMaxDecodeWaves);
@@ -438,14 +438,14 @@ int prefix_chunks(int max_prefix_len) {
 }
 
 // Checks shared by the decode entry points; fills the size fields of a.
-int check_decode(pkv::DecodeArgs& a, void* out, const void* q, const void* k_pool,
+pkv_status check_decode(pkv::DecodeArgs& a, void* out, const void* q, const void* k_pool,
                  const void* v_pool, const int32_t* block_table, const int32_t* context_lens,
                  int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                  int max_blocks_per_seq, int num_blocks, float scale, int max_context_len,
                  int dtype, int out_dtype) {
   if (!out || !q || !k_pool || !v_pool || !block_table || !context_lens)
     return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
-  int st = check_common(num_q_heads, num_kv_heads, head_dim, block_size, dtype, out_dtype);
+  pkv_status st = check_common(num_q_heads, num_kv_heads, head_dim, block_size, dtype, out_dtype);
   if (st != PKV_OK) return st;
   if (max_blocks_per_seq <= 0 || num_blocks <= 0)
     return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq and num_blocks must be positive");
@@ -490,18 +490,23 @@ size_t pkv_decode_shared_prefix_workspace_size(int num_seqs, int num_q_heads, in
       .bytes;
 }
 
-int pkv_paged_attention_decode_shared_prefix(
-    void* out, const void* q, const void* k_pool, const void* v_pool,
-    const int32_t* block_table, const int32_t* context_lens, const int32_t* group_start,
-    const int32_t* group_prefix_len, int num_groups, int max_group_size, int max_prefix_len,
-    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-    int max_blocks_per_seq, int num_blocks, float scale, int max_context_len, int num_waves,
-    int kv_dtype, float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
-    int out_dtype, void* stream) {
+pkv_status pkv_paged_attention_decode_shared_prefix(void* out, const void* q, const void* k_pool,
+                                                    const void* v_pool, const int32_t* block_table,
+                                                    const int32_t* context_lens,
+                                                    const int32_t* group_start,
+                                                    const int32_t* group_prefix_len, int num_groups,
+                                                    int max_group_size, int max_prefix_len,
+                                                    int num_seqs, int num_q_heads, int num_kv_heads,
+                                                    int head_dim, int block_size,
+                                                    int max_blocks_per_seq, int num_blocks,
+                                                    float scale, int max_context_len, int num_waves,
+                                                    int kv_dtype, float k_scale, float v_scale,
+                                                    void* workspace, size_t workspace_bytes,
+                                                    int out_dtype, void* stream) {
   if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs = %d is negative", num_seqs);
   if (num_seqs == 0) return PKV_OK;
   pkv::DecodeArgs a{};
-  int st = check_decode(a, out, q, k_pool, v_pool, block_table, context_lens, num_seqs,
+  pkv_status st = check_decode(a, out, q, k_pool, v_pool, block_table, context_lens, num_seqs,
                         num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                         num_blocks, scale, max_context_len, PKV_BF16, out_dtype);
   if (st != PKV_OK) return st;
@@ -553,25 +558,25 @@ int pkv_paged_attention_decode_shared_prefix(
   d.group_prefix_len = group_prefix_len;
   d.NG = num_groups;
   d.max_prefix = max_prefix_len;
-  if (int dst = debug_gate(d, stream, "paged_attention_decode_shared_prefix")) return dst;
+  if (pkv_status dst = debug_gate(d, stream, "paged_attention_decode_shared_prefix")) return dst;
   return hip_status(pkv::launch_decode(a, static_cast<hipStream_t>(stream)),
                     "paged_attention_decode_shared_prefix");
 }
 
-int pkv_kv_cache_write_and_decode(void* out, const void* q, const void* k_new,
-                                  const void* v_new, const int32_t* slot_mapping, void* k_pool,
-                                  void* v_pool, const int32_t* block_table,
-                                  const int32_t* context_lens, int num_seqs, int num_q_heads,
-                                  int num_kv_heads, int head_dim, int block_size,
-                                  int max_blocks_per_seq, int num_blocks, float scale,
-                                  int max_context_len, int num_waves, void* workspace,
-                                  size_t workspace_bytes, int out_dtype, void* stream) {
+pkv_status pkv_kv_cache_write_and_decode(void* out, const void* q, const void* k_new,
+                                         const void* v_new, const int32_t* slot_mapping,
+                                         void* k_pool, void* v_pool, const int32_t* block_table,
+                                         const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                         int num_kv_heads, int head_dim, int block_size,
+                                         int max_blocks_per_seq, int num_blocks, float scale,
+                                         int max_context_len, int num_waves, void* workspace,
+                                         size_t workspace_bytes, int out_dtype, void* stream) {
   if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs = %d is negative", num_seqs);
   if (num_seqs == 0) return PKV_OK;
   if (!k_new || !v_new || !slot_mapping)
     return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
   pkv::DecodeArgs a{};
-  int st = check_decode(a, out, q, k_pool, v_pool, block_table, context_lens, num_seqs,
+  pkv_status st = check_decode(a, out, q, k_pool, v_pool, block_table, context_lens, num_seqs,
                         num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                         num_blocks, scale, max_context_len, PKV_BF16, out_dtype);
   if (st != PKV_OK) return st;
@@ -589,23 +594,23 @@ int pkv_kv_cache_write_and_decode(void* out, const void* q, const void* k_new,
   d.slots = slot_mapping;
   d.T = num_seqs;
   d.slot_NB = num_blocks;
-  if (int dst = debug_gate(d, stream, "kv_cache_write_and_decode")) return dst;
+  if (pkv_status dst = debug_gate(d, stream, "kv_cache_write_and_decode")) return dst;
   return hip_status(pkv::launch_decode(a, static_cast<hipStream_t>(stream)),
                     "kv_cache_write_and_decode");
 }
 
-int pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_pool,
-                                   const void* v_pool, const int32_t* block_table,
-                                   const int32_t* context_lens, int num_seqs, int num_q_heads,
-                                   int num_kv_heads, int head_dim, int block_size,
-                                   int max_blocks_per_seq, int num_blocks, float scale,
-                                   float k_scale, float v_scale, int max_context_len,
-                                   int num_waves, void* workspace, size_t workspace_bytes,
-                                   int out_dtype, void* stream) {
+pkv_status pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_pool,
+                                          const void* v_pool, const int32_t* block_table,
+                                          const int32_t* context_lens, int num_seqs,
+                                          int num_q_heads, int num_kv_heads, int head_dim,
+                                          int block_size, int max_blocks_per_seq, int num_blocks,
+                                          float scale, float k_scale, float v_scale,
+                                          int max_context_len, int num_waves, void* workspace,
+                                          size_t workspace_bytes, int out_dtype, void* stream) {
   if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs = %d is negative", num_seqs);
   if (num_seqs == 0) return PKV_OK;
   pkv::DecodeArgs a{};
-  int st = check_decode(a, out, q, k_pool, v_pool, block_table, context_lens, num_seqs,
+  pkv_status st = check_decode(a, out, q, k_pool, v_pool, block_table, context_lens, num_seqs,
                         num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                         num_blocks, scale, max_context_len, PKV_BF16, out_dtype);
   if (st != PKV_OK) return st;
@@ -620,24 +625,25 @@ int pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_pool,
   a.v_scale = v_scale;
   a.bf16_in = 1;
   a.bf16_out = out_dtype == PKV_BF16;
-  if (int dst = debug_gate(tables_check(block_table, context_lens, a.S, a.MB, a.B, a.NB,
+  if (pkv_status dst = debug_gate(tables_check(block_table, context_lens, a.S, a.MB, a.B, a.NB,
                                         a.max_ctx), stream, "paged_attention_decode_fp8"))
     return dst;
   return hip_status(pkv::launch_decode(a, static_cast<hipStream_t>(stream)),
                     "paged_attention_decode_fp8");
 }
 
-int pkv_paged_attention_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
-                               const int32_t* block_table, const int32_t* context_lens,
-                               int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                               int block_size, int max_blocks_per_seq, int num_blocks,
-                               float scale, int max_context_len, int partition_size,
-                               int num_waves, void* workspace, size_t workspace_bytes, int dtype,
-                               int out_dtype, void* stream) {
+pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_pool,
+                                      const void* v_pool, const int32_t* block_table,
+                                      const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                      int num_kv_heads, int head_dim, int block_size,
+                                      int max_blocks_per_seq, int num_blocks, float scale,
+                                      int max_context_len, int partition_size, int num_waves,
+                                      void* workspace, size_t workspace_bytes, int dtype,
+                                      int out_dtype, void* stream) {
   if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs = %d is negative", num_seqs);
   if (num_seqs == 0) return PKV_OK;
   pkv::DecodeArgs a{};
-  int st = check_decode(a, out, q, k_pool, v_pool, block_table, context_lens, num_seqs,
+  pkv_status st = check_decode(a, out, q, k_pool, v_pool, block_table, context_lens, num_seqs,
                         num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                         num_blocks, scale, max_context_len, dtype, out_dtype);
   if (st != PKV_OK) return st;
@@ -670,7 +676,7 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_pool, con
   }
   a.bf16_in = dtype == PKV_BF16;
   a.bf16_out = out_dtype == PKV_BF16;
-  if (int dst = debug_gate(tables_check(block_table, context_lens, a.S, a.MB, a.B, a.NB,
+  if (pkv_status dst = debug_gate(tables_check(block_table, context_lens, a.S, a.MB, a.B, a.NB,
                                         a.max_ctx), stream, "paged_attention_decode"))
     return dst;
   return hip_status(pkv::launch_decode(a, static_cast<hipStream_t>(stream)),
@@ -691,17 +697,17 @@ size_t probe_sink_bytes(int waves) {
 
 extern "C" {
 
-int pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_pool,
-                                       const void* v_pool, const int32_t* block_table,
-                                       const int32_t* context_lens, int num_seqs,
-                                       int num_q_heads, int num_kv_heads, int head_dim,
-                                       int block_size, int max_blocks_per_seq, int num_blocks,
-                                       float scale, int max_context_len, int num_waves,
-                                       int out_dtype, void* stream) {
+pkv_status pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_pool,
+                                              const void* v_pool, const int32_t* block_table,
+                                              const int32_t* context_lens, int num_seqs,
+                                              int num_q_heads, int num_kv_heads, int head_dim,
+                                              int block_size, int max_blocks_per_seq,
+                                              int num_blocks, float scale, int max_context_len,
+                                              int num_waves, int out_dtype, void* stream) {
   if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs = %d is negative", num_seqs);
   if (num_seqs == 0) return PKV_OK;
   pkv::DecodeArgs a{};
-  int st = check_decode(a, out, q, k_pool, v_pool, block_table, context_lens, num_seqs,
+  pkv_status st = check_decode(a, out, q, k_pool, v_pool, block_table, context_lens, num_seqs,
                         num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                         num_blocks, scale, max_context_len, PKV_BF16, out_dtype);
   if (st != PKV_OK) return st;
@@ -718,13 +724,13 @@ int pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_p
                 need, pkv::kNoAllocScratchBytes);
   void* ws = nullptr;
   size_t ws_bytes = 0;
-  if (int hs = hip_status(pkv::noalloc_scratch(&ws, &ws_bytes), "decode_noalloc scratch"))
+  if (pkv_status hs = hip_status(pkv::noalloc_scratch(&ws, &ws_bytes), "decode_noalloc scratch"))
     return hs;
   st = setup_balanced(a, ws, ws_bytes, kDefaultDecodeWaves, num_waves);
   if (st != PKV_OK) return st;
   a.bf16_in = 1;
   a.bf16_out = out_dtype == PKV_BF16;
-  if (int dst = debug_gate(tables_check(block_table, context_lens, a.S, a.MB, a.B, a.NB,
+  if (pkv_status dst = debug_gate(tables_check(block_table, context_lens, a.S, a.MB, a.B, a.NB,
                                         a.max_ctx), stream, "paged_attention_decode_noalloc"))
     return dst;
   return hip_status(pkv::launch_decode(a, static_cast<hipStream_t>(stream)),
@@ -742,15 +748,15 @@ size_t pkv_decode_read_probe_sink_size(int num_seqs, int num_q_heads, int num_kv
   return probe_sink_bytes(pl.waves);
 }
 
-int pkv_decode_read_probe(const void* k_pool, const void* v_pool, const int32_t* block_table,
-                          const int32_t* context_lens, int num_seqs, int num_q_heads,
-                          int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
-                          int num_blocks, int max_context_len, int num_waves, void* sink,
-                          size_t sink_bytes, void* stream) {
+pkv_status pkv_decode_read_probe(const void* k_pool, const void* v_pool, const int32_t* block_table,
+                                 const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                 int num_kv_heads, int head_dim, int block_size,
+                                 int max_blocks_per_seq, int num_blocks, int max_context_len,
+                                 int num_waves, void* sink, size_t sink_bytes, void* stream) {
   if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs = %d is negative", num_seqs);
   if (num_seqs == 0) return PKV_OK;
   pkv::DecodeArgs a{};
-  int st = check_decode(a, sink, sink, k_pool, v_pool, block_table, context_lens, num_seqs,
+  pkv_status st = check_decode(a, sink, sink, k_pool, v_pool, block_table, context_lens, num_seqs,
                         num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                         num_blocks, 1.0f, max_context_len, PKV_BF16, PKV_BF16);
   if (st != PKV_OK) return st;
@@ -763,27 +769,27 @@ int pkv_decode_read_probe(const void* k_pool, const void* v_pool, const int32_t*
     return fail(PKV_ERR_WORKSPACE, "sink of %zu bytes needed, %zu given", need, sink_bytes);
   pkv::ReadProbeArgs r{static_cast<uint32_t*>(sink), k_pool, v_pool, block_table, context_lens,
                        a.S, a.Hq, a.Hkv, a.D, a.B, a.MB, pl.waves, kMinTilesPerWave};
-  if (int dst = debug_gate(tables_check(block_table, context_lens, a.S, a.MB, a.B, a.NB,
+  if (pkv_status dst = debug_gate(tables_check(block_table, context_lens, a.S, a.MB, a.B, a.NB,
                                         a.max_ctx), stream, "decode_read_probe"))
     return dst;
   return hip_status(pkv::launch_read_probe(r, static_cast<hipStream_t>(stream)),
                     "decode_read_probe");
 }
 
-int pkv_paged_attention_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
-                                      const int32_t* context_lens, const void* k_pool,
-                                      const void* v_pool, const int32_t* block_table,
-                                      int num_seqs, int total_q, int num_q_heads,
-                                      int num_kv_heads, int head_dim, int block_size,
-                                      int max_blocks_per_seq, int num_blocks, float scale,
-                                      int max_q_len, int max_context_len, int dtype,
-                                      int out_dtype, void* stream) {
+pkv_status pkv_paged_attention_prefill_chunk(void* out, const void* q, const int32_t* cu_q_lens,
+                                             const int32_t* context_lens, const void* k_pool,
+                                             const void* v_pool, const int32_t* block_table,
+                                             int num_seqs, int total_q, int num_q_heads,
+                                             int num_kv_heads, int head_dim, int block_size,
+                                             int max_blocks_per_seq, int num_blocks, float scale,
+                                             int max_q_len, int max_context_len, int dtype,
+                                             int out_dtype, void* stream) {
   if (num_seqs < 0 || total_q < 0)
     return fail(PKV_ERR_INVALID_ARG, "num_seqs and total_q must be non-negative");
   if (num_seqs == 0 || total_q == 0) return PKV_OK;
   if (!out || !q || !cu_q_lens || !context_lens || !k_pool || !v_pool || !block_table)
     return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
-  int st = check_common(num_q_heads, num_kv_heads, head_dim, block_size, dtype, out_dtype);
+  pkv_status st = check_common(num_q_heads, num_kv_heads, head_dim, block_size, dtype, out_dtype);
   if (st != PKV_OK) return st;
   if (max_blocks_per_seq <= 0 || num_blocks <= 0)
     return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq and num_blocks must be positive");
@@ -823,12 +829,12 @@ int pkv_paged_attention_prefill_chunk(void* out, const void* q, const int32_t* c
   pkv::DebugCheckArgs d = tables_check(block_table, context_lens, a.S, a.MB, a.B, a.NB, a.max_ctx);
   d.cu_q_lens = cu_q_lens;
   d.total_q = total_q;
-  if (int dst = debug_gate(d, stream, "paged_attention_prefill_chunk")) return dst;
+  if (pkv_status dst = debug_gate(d, stream, "paged_attention_prefill_chunk")) return dst;
   return hip_status(pkv::launch_prefill(a, static_cast<hipStream_t>(stream)),
                     "paged_attention_prefill_chunk");
 }
 
-int pkv_profile_enable(int kernel_mask) {
+pkv_status pkv_profile_enable(int kernel_mask) {
   std::lock_guard<std::mutex> lk(g_timing_mu);
   drain_locked();
   for (int i = 0; i < pkv::K_COUNT; ++i) {
@@ -839,7 +845,7 @@ int pkv_profile_enable(int kernel_mask) {
   return PKV_OK;
 }
 
-int pkv_profile_reset(void) {
+pkv_status pkv_profile_reset(void) {
   std::lock_guard<std::mutex> lk(g_timing_mu);
   drain_locked();
   for (int i = 0; i < pkv::K_COUNT; ++i) {
@@ -849,7 +855,7 @@ int pkv_profile_reset(void) {
   return PKV_OK;
 }
 
-int pkv_profile_read(const char* kernel_name, double* total_ms, long long* launches) {
+pkv_status pkv_profile_read(const char* kernel_name, double* total_ms, long long* launches) {
   if (!kernel_name) return fail(PKV_ERR_INVALID_ARG, "null kernel name");
   std::lock_guard<std::mutex> lk(g_timing_mu);
   drain_locked();

@@ -38,7 +38,7 @@ struct pkv_block_manager {
 
 extern "C" {
 
-int pkv_bm_create(int num_blocks, int block_size, pkv_block_manager** out) {
+pkv_status pkv_bm_create(int num_blocks, int block_size, pkv_block_manager** out) {
   if (!out || num_blocks <= 0 || block_size <= 0)
     return fail(PKV_ERR_INVALID_ARG, "bm_create: num_blocks %d, block_size %d", num_blocks,
                 block_size);
@@ -57,7 +57,7 @@ int pkv_bm_num_free(const pkv_block_manager* bm) {
   return bm ? static_cast<int>(bm->free_list.size()) : -1;
 }
 
-int pkv_bm_add(pkv_block_manager* bm, int64_t seq) {
+pkv_status pkv_bm_add(pkv_block_manager* bm, int64_t seq) {
   if (!bm) return fail(PKV_ERR_INVALID_ARG, "bm_add: null manager");
   if (bm->seqs.count(seq)) return fail(PKV_ERR_INVALID_ARG, "bm_add: sequence %lld exists",
                                        static_cast<long long>(seq));
@@ -65,7 +65,7 @@ int pkv_bm_add(pkv_block_manager* bm, int64_t seq) {
   return PKV_OK;
 }
 
-int pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child) {
+pkv_status pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child) {
   if (!bm || !bm->seqs.count(parent) || bm->seqs.count(child))
     return fail(PKV_ERR_INVALID_ARG, "bm_fork: parent %lld must exist and child %lld must not",
                 static_cast<long long>(parent), static_cast<long long>(child));
@@ -75,8 +75,8 @@ int pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child) {
   return PKV_OK;
 }
 
-int pkv_bm_append(pkv_block_manager* bm, int64_t seq, int n_tokens, int32_t* slots,
-                  int32_t* copies, int max_copies, int* n_copies) {
+pkv_status pkv_bm_append(pkv_block_manager* bm, int64_t seq, int n_tokens, int32_t* slots,
+                         int32_t* copies, int max_copies, int* n_copies) {
   if (!bm || !n_copies || n_tokens < 0 || !bm->seqs.count(seq))
     return fail(PKV_ERR_INVALID_ARG, "bm_append: bad arguments for sequence %lld",
                 static_cast<long long>(seq));
@@ -112,7 +112,7 @@ int pkv_bm_append(pkv_block_manager* bm, int64_t seq, int n_tokens, int32_t* slo
   return PKV_OK;
 }
 
-int pkv_bm_free(pkv_block_manager* bm, int64_t seq) {
+pkv_status pkv_bm_free(pkv_block_manager* bm, int64_t seq) {
   if (!bm || !bm->seqs.count(seq))
     return fail(PKV_ERR_INVALID_ARG, "bm_free: unknown sequence %lld", static_cast<long long>(seq));
   for (int32_t b : bm->seqs.at(seq).blocks) bm->drop(b);
@@ -120,7 +120,7 @@ int pkv_bm_free(pkv_block_manager* bm, int64_t seq) {
   return PKV_OK;
 }
 
-int pkv_bm_context_len(const pkv_block_manager* bm, int64_t seq, int* len) {
+pkv_status pkv_bm_context_len(const pkv_block_manager* bm, int64_t seq, int* len) {
   if (!bm || !len || !bm->seqs.count(seq))
     return fail(PKV_ERR_INVALID_ARG, "bm_context_len: unknown sequence %lld",
                 static_cast<long long>(seq));
@@ -128,8 +128,8 @@ int pkv_bm_context_len(const pkv_block_manager* bm, int64_t seq, int* len) {
   return PKV_OK;
 }
 
-int pkv_bm_block_table(const pkv_block_manager* bm, int64_t seq, int32_t* table, int capacity,
-                       int* n_blocks) {
+pkv_status pkv_bm_block_table(const pkv_block_manager* bm, int64_t seq, int32_t* table,
+                              int capacity, int* n_blocks) {
   if (!bm || !n_blocks || capacity < 0 || !bm->seqs.count(seq))
     return fail(PKV_ERR_INVALID_ARG, "bm_block_table: unknown sequence %lld",
                 static_cast<long long>(seq));
@@ -140,7 +140,7 @@ int pkv_bm_block_table(const pkv_block_manager* bm, int64_t seq, int32_t* table,
   return PKV_OK;
 }
 
-int pkv_bm_refcount(const pkv_block_manager* bm, int block, int* count) {
+pkv_status pkv_bm_refcount(const pkv_block_manager* bm, int block, int* count) {
   if (!bm || !count || block < 0 || block >= bm->num_blocks)
     return fail(PKV_ERR_INVALID_ARG, "bm_refcount: block %d out of range", block);
   *count = bm->refcount[block];

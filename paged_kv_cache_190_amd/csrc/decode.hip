@@ -251,7 +251,8 @@ struct TileWalk {
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        T.k[hf][kk] = STREAM ? load16_stream(kb + koff[hf] + 32 * kk) : load16(kb + koff[hf] + 32 * kk);
+        T.k[hf][kk] = STREAM ? load16_stream(kb + koff[hf] + 32 * kk)
+                             : load16(kb + koff[hf] + 32 * kk);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
       T.v[dt] = STREAM ? load16_stream(vb + voff + 16 * dt * B) : load16(vb + voff + 16 * dt * B);
@@ -459,7 +460,8 @@ __device__ __forceinline__ void attend_tiles_fp8(WaveAttn<D>& st, const u32x4 (&
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int j = 0; j < KL; ++j)
-        T.k[hf][j] = STREAM ? load16_stream(kb + koff[hf] + 16 * j) : load16(kb + koff[hf] + 16 * j);
+        T.k[hf][j] = STREAM ? load16_stream(kb + koff[hf] + 16 * j)
+                            : load16(kb + koff[hf] + 16 * j);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
       T.v[dt] = STREAM ? load8_stream(vb + voff + 16 * dt * B) : load8(vb + voff + 16 * dt * B);
@@ -1363,27 +1365,29 @@ static hipError_t launch_bf16(const DecodeArgs& a, hipStream_t st) {
   const int groups = (a.waves + kBalancedWavesPerGroup - 1) / kBalancedWavesPerGroup;
   if (a.fp8_kv) {
     return launch_kernel(K_DECODE_PARTITION, decode_balanced_kernel<D, B, OutT, uint8_t>,
-        dim3(groups), dim3(64 * kBalancedWavesPerGroup), st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l,
-        a.seg_count, static_cast<const uint16_t*>(a.q), static_cast<const uint8_t*>(a.k_pool),
-        static_cast<const uint8_t*>(a.v_pool), a.block_table, a.context_lens, a.S, a.Hq, a.Hkv, G,
-        HG, a.MB, a.KMAX, a.min_tiles, a.scale * a.k_scale * kLog2e, a.v_scale);
+        dim3(groups), dim3(64 * kBalancedWavesPerGroup), st, static_cast<OutT*>(a.out), a.part_o,
+        a.part_m, a.part_l, a.seg_count, static_cast<const uint16_t*>(a.q),
+        static_cast<const uint8_t*>(a.k_pool), static_cast<const uint8_t*>(a.v_pool),
+        a.block_table, a.context_lens, a.S, a.Hq, a.Hkv, G, HG, a.MB, a.KMAX, a.min_tiles,
+        a.scale * a.k_scale * kLog2e, a.v_scale);
   }
   if (a.balanced) {
     return launch_kernel(K_DECODE_PARTITION, decode_balanced_kernel<D, B, OutT, uint16_t>,
-        dim3(groups), dim3(64 * kBalancedWavesPerGroup), st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l,
-        a.seg_count, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
-        static_cast<const uint16_t*>(a.v_pool), a.block_table, a.context_lens, a.S, a.Hq, a.Hkv, G,
-        HG, a.MB, a.KMAX, a.min_tiles, a.scale * kLog2e, 1.0f);
+        dim3(groups), dim3(64 * kBalancedWavesPerGroup), st, static_cast<OutT*>(a.out), a.part_o,
+        a.part_m, a.part_l, a.seg_count, static_cast<const uint16_t*>(a.q),
+        static_cast<const uint16_t*>(a.k_pool), static_cast<const uint16_t*>(a.v_pool),
+        a.block_table, a.context_lens, a.S, a.Hq, a.Hkv, G, HG, a.MB, a.KMAX, a.min_tiles,
+        a.scale * kLog2e, 1.0f);
   }
   dim3 grid(a.Hkv * HG, a.S, a.NP);
   if (a.NP > 1)
-    return launch_kernel(K_DECODE_PARTITION, decode_fixed_kernel<D, B, true, OutT>, dim3(grid), dim3(64),
-        st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l,
+    return launch_kernel(K_DECODE_PARTITION, decode_fixed_kernel<D, B, true, OutT>, dim3(grid),
+        dim3(64), st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l,
         static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
         static_cast<const uint16_t*>(a.v_pool), a.block_table, a.context_lens, a.Hq, a.Hkv, G, HG,
         a.MB, a.P, a.NP, a.scale * kLog2e);
-  return launch_kernel(K_DECODE_PARTITION, decode_fixed_kernel<D, B, false, OutT>, dim3(grid), dim3(64),
-        st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l,
+  return launch_kernel(K_DECODE_PARTITION, decode_fixed_kernel<D, B, false, OutT>, dim3(grid),
+        dim3(64), st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l,
         static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_pool),
         static_cast<const uint16_t*>(a.v_pool), a.block_table, a.context_lens, a.Hq, a.Hkv, G, HG,
         a.MB, a.P, a.NP, a.scale * kLog2e);
@@ -1409,7 +1413,8 @@ static hipError_t launch_step_t(const DecodeArgs& a, hipStream_t st) {
   const int HG = (G + 15) / 16;
   return launch_kernel(K_DECODE_PARTITION, decode_step_kernel<D, B, OutT>,
       dim3((a.waves + kBalancedWavesPerGroup - 1) / kBalancedWavesPerGroup),
-      dim3(64 * kBalancedWavesPerGroup), st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l, a.seg_count,
+      dim3(64 * kBalancedWavesPerGroup), st, static_cast<OutT*>(a.out), a.part_o, a.part_m,
+      a.part_l, a.seg_count,
       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k_new),
       static_cast<const uint16_t*>(a.v_new), a.slot_mapping,
       static_cast<uint16_t*>(const_cast<void*>(a.k_pool)),
@@ -1420,7 +1425,8 @@ static hipError_t launch_step_t(const DecodeArgs& a, hipStream_t st) {
 template <int D, int B, bool SPLIT, typename OutT>
 static hipError_t launch_f32(const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.S, a.Hq, a.NP);
-  return launch_kernel(K_DECODE_PARTITION, attn_f32_kernel<D, B, SPLIT, false, OutT>, dim3(grid), dim3(64),
+  return launch_kernel(K_DECODE_PARTITION, attn_f32_kernel<D, B, SPLIT, false, OutT>, dim3(grid),
+                       dim3(64),
       st, static_cast<OutT*>(a.out), a.part_o, a.part_m, a.part_l, static_cast<const float*>(a.q),
       static_cast<const float*>(a.k_pool), static_cast<const float*>(a.v_pool), a.block_table,
       a.context_lens, nullptr, a.S, a.Hq, a.Hkv, a.MB, a.P, a.NP, a.scale * kLog2e);
@@ -1486,7 +1492,8 @@ static hipError_t launch_probe_t(const ReadProbeArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_read_probe(const ReadProbeArgs& a, hipStream_t st) {
-  if (a.D == 128) return a.B == 16 ? launch_probe_t<128, 16>(a, st) : launch_probe_t<128, 32>(a, st);
+  if (a.D == 128)
+    return a.B == 16 ? launch_probe_t<128, 16>(a, st) : launch_probe_t<128, 32>(a, st);
   return a.B == 16 ? launch_probe_t<64, 16>(a, st) : launch_probe_t<64, 32>(a, st);
 }
 
@@ -1497,7 +1504,8 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st);
 template <int D, int B, typename OutT>
 static hipError_t launch_prefill_f32_t(const PrefillArgs& a, hipStream_t st) {
   dim3 grid(a.total_q, a.Hq, 1);
-  return launch_kernel(K_PREFILL, attn_f32_kernel<D, B, false, true, OutT>, dim3(grid), dim3(64), st,
+  return launch_kernel(K_PREFILL, attn_f32_kernel<D, B, false, true, OutT>, dim3(grid), dim3(64),
+                       st,
       static_cast<OutT*>(a.out), nullptr, nullptr, nullptr, static_cast<const float*>(a.q),
       static_cast<const float*>(a.k_pool), static_cast<const float*>(a.v_pool), a.block_table,
       a.context_lens, a.cu_q_lens, a.S, a.Hq, a.Hkv, a.MB, 1 << 30, 1, a.scale * kLog2e);
@@ -1510,7 +1518,8 @@ static hipError_t prefill_f32_out(const PrefillArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st) {
-  if (a.D == 128) return a.B == 16 ? prefill_f32_out<128, 16>(a, st) : prefill_f32_out<128, 32>(a, st);
+  if (a.D == 128)
+    return a.B == 16 ? prefill_f32_out<128, 16>(a, st) : prefill_f32_out<128, 32>(a, st);
   return a.B == 16 ? prefill_f32_out<64, 16>(a, st) : prefill_f32_out<64, 32>(a, st);
 }
 

@@ -2,6 +2,8 @@
 // (per thread) and return the status code.
 #pragma once
 
+#include "../../include/pkv.h"
+
 namespace pkv {
-int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+pkv_status fail(pkv_status status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 }  // namespace pkv

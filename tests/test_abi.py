@@ -4,6 +4,7 @@ HIP call, so none of these launches anything; pointers here are fake non-null ad
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -26,6 +27,28 @@ def test_every_declared_symbol_is_exported():
     assert len(names) >= 10
     missing = [n for n in names if not hasattr(L, n)]
     assert not missing, missing
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """A C99 caller compiles against the header with warnings as errors, takes the address of
+    every declared call, links against the library and runs (no GPU call is made)."""
+    names = declared_symbols()
+    src = tmp_path / "caller.c"
+    src.write_text('#include "pkv.h"\n#include <stdio.h>\nint main(void) {\n'
+                   '  void (*calls[])(void) = {'
+                   + ", ".join("(void (*)(void))&" + n for n in names)
+                   + '};\n  pkv_status st = PKV_OK;\n'
+                   '  printf("%d %zu\\n", (int)st, sizeof calls / sizeof calls[0]);\n'
+                   '  return 0;\n}\n')
+    libdir = os.path.dirname(bd.LIB_PATH)
+    exe = tmp_path / "caller"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    "-I", os.path.dirname(HEADER), str(src), "-o", str(exe),
+                    "-L", libdir, "-l:" + os.path.basename(bd.LIB_PATH),
+                    "-Wl,-rpath," + libdir, "-Wl,--allow-shlib-undefined"],
+                   check=True, capture_output=True, text=True)
+    run = subprocess.run([str(exe)], check=True, capture_output=True, text=True, timeout=60)
+    assert run.stdout.split() == ["0", str(len(names))]
 
 
 def test_version_and_strings():
