@@ -215,13 +215,17 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
       ssel[j] = B == 16 && chunk >= 2;
     }
   }
-  auto issue = [&](int t) {
-    unsigned char* st = smem + (t % NS) * STAGE;
+  // The physical block ids of key tile t (two when B = 16: the tile spans two blocks).
+  struct Ids { uint32_t a, b; };
+  auto ids_of = [&](int t) -> Ids {
     const int lb0 = (32 * t) / B;
-    // both candidate block offsets are wave-uniform products (ids are non-negative and the
-    // block stride fits 32 bits); a lane only selects one and adds its own offset
-    const uint64_t o0 = static_cast<uint64_t>(block_id(lb0)) * blk_stride;
-    const uint64_t o1 = (B == 16) ? static_cast<uint64_t>(block_id(lb0 + 1)) * blk_stride : o0;
+    const uint32_t a = block_id(lb0);
+    return Ids{a, B == 16 ? block_id(lb0 + 1) : a};
+  };
+  auto issue_ids = [&](int t, Ids id) {
+    unsigned char* st = smem + (t % NS) * STAGE;
+    const uint64_t o0 = static_cast<uint64_t>(id.a) * blk_stride;
+    const uint64_t o1 = (B == 16) ? static_cast<uint64_t>(id.b) * blk_stride : o0;
     // (The source pointer is a named variable: given a conditional expression directly, the
     // builtin makes clang drop this kernel's host-side launch stub without a diagnostic.)
 #pragma unroll
@@ -230,6 +234,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
       __builtin_amdgcn_global_load_lds(src, st + (LPT * wave + j) * 1024, 16, 0, 0);
     }
   };
+  auto issue = [&](int t) { issue_ids(t, ids_of(t)); };
 
   f32x16 acc[DT];
 #pragma unroll
@@ -325,8 +330,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
   // Pipeline: the ring advances TPB tiles per workgroup barrier. A wave waits for its DMAs of
   // tiles t .. t+TPB-1, leaving the tiles issued after them in flight; the barrier publishes
   // those tiles and frees the stages of the TPB tiles computed before it, into which tiles
-  // t+NS-TPB .. t+NS-1 are issued; then tiles t .. t+TPB-1 are computed. Fewer barriers and
-  // issue phases per tile than one per tile, with up to NS-TPB tiles in flight.
+  // t+NS-TPB .. t+NS-1 are issued, each just before one of the tiles t .. t+TPB-1 is computed
+  // (so the waves' DMA issues spread over the iteration instead of all following the barrier).
+  // Fewer barriers per tile than one per tile, with up to NS-TPB tiles in flight. The block ids
+  // of the tiles to issue are loaded before the wait, so their scalar loads overlap it.
   constexpr int TPB = kTilesPerBarrier;
   constexpr int PRE = NS - TPB;  // tiles issued ahead of the loop
   static_assert(PRE - TPB >= 0 && PRE - TPB <= 4, "one wait per possible depth below");
@@ -334,6 +341,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
   for (int t = 0; t < PRE; ++t)
     if (t < ntiles) issue(t);
   for (int t = 0; t < ntiles; t += TPB) {
+    Ids nid[TPB];  // (ids_of clamps past the context, so this is safe for any t)
+#pragma unroll
+    for (int k = 0; k < TPB; ++k) nid[k] = ids_of(t + PRE + k);
     // issued so far: tiles 0 .. min(t + PRE, ntiles) - 1; needed now: t .. t+TPB-1
     const int ahead = min(t + PRE, ntiles) - min(t + TPB, ntiles);
     if (ahead >= 4) __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * LPT));
@@ -343,11 +353,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
     else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int k = 0; k < TPB; ++k)
-      if (t + PRE + k < ntiles) issue(t + PRE + k);
-#pragma unroll
-    for (int k = 0; k < TPB; ++k)
+    for (int k = 0; k < TPB; ++k) {
+      if (t + PRE + k < ntiles) issue_ids(t + PRE + k, nid[k]);
       if (t + k < ntiles) compute(t + k);
+    }
   }
 
   if (!wave_active) return;
