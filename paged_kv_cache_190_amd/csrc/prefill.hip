@@ -222,8 +222,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
     const uint32_t a = block_id(lb0);
     return Ids{a, B == 16 ? block_id(lb0 + 1) : a};
   };
-  auto issue_ids = [&](int t, Ids id) {
-    unsigned char* st = smem + (t % NS) * STAGE;
+  auto issue_ids = [&](int t, int stage, Ids id) {
+    unsigned char* st = smem + stage * STAGE;
     const uint64_t o0 = static_cast<uint64_t>(id.a) * blk_stride;
     const uint64_t o1 = (B == 16) ? static_cast<uint64_t>(id.b) * blk_stride : o0;
     // (The source pointer is a named variable: given a conditional expression directly, the
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
       __builtin_amdgcn_global_load_lds(src, st + (LPT * wave + j) * 1024, 16, 0, 0);
     }
   };
-  auto issue = [&](int t) { issue_ids(t, ids_of(t)); };
+  auto issue = [&](int t) { issue_ids(t, t % NS, ids_of(t)); };
 
   f32x16 acc[DT];
 #pragma unroll
@@ -242,6 +242,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
   float m = -INFINITY;
+  float m_grow = -INFINITY;  // m + 8: the row max past which the reference max moves
   float l = 0.f;
   const int qpos = r + my_i;           // this lane's query position
   const int wq_lo = r + w_tok0;        // the wave's first query position
@@ -252,10 +253,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
   const int kx = kswz<D>(krow);
   const int vx = vswz(col);
 
-  auto compute = [&](int t) {
+  auto compute = [&](int t, int stage) {
     const int key0 = 32 * t;
     if (!wave_active || key0 > wq_lo + 31) return;  // wholly above the diagonal
-    const unsigned char* st = smem + (t % NS) * STAGE;
+    const unsigned char* st = smem + stage * STAGE;
     f32x16 sacc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
@@ -273,22 +274,31 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
       for (int i = 0; i < 16; ++i)
         if (key0 + 16 * hb + i > klim) sacc[i] = -INFINITY;
     }
+    // (IEEE maximum: a NaN score makes the row NaN either way, and this form needs no
+    // canonicalising of the MFMA results before the three-input max instructions)
     float rmax = sacc[0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) rmax = fmaxf(rmax, sacc[i]);
-    rmax = xor32_max(rmax) * scale_log2;
+    for (int i = 1; i < 16; ++i) rmax = __builtin_elementwise_maximum(rmax, sacc[i]);
+    {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmax),
+                                                      __float_as_uint(rmax), false, false);
+      rmax = __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    rmax *= scale_log2;
     // Lazy rescaling: keep the old reference max unless the row's max grows by more than 2^8,
     // so exponentials stay <= 256 and the output is rescaled only rarely.
-    const bool grow = rmax > m + 8.0f;
+    const bool grow = rmax > m_grow;
     if (__builtin_amdgcn_ballot_w64(grow)) {
       const float mnew = grow ? rmax : m;
       const float alpha = fast_exp2(m - mnew);
       m = mnew;
+      m_grow = mnew + 8.0f;
       l *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
     }
-    float psum = 0.f;
+    // The row sum takes the bf16-rounded weights that the P.V product uses, two per dot2.
+    float psum[2] = {0.f, 0.f};
     u32x4 pb[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -296,10 +306,11 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
       for (int w = 0; w < 4; ++w) {
         const float p0 = fast_exp2(__builtin_fmaf(sacc[8 * j + 2 * w], scale_log2, -m));
         const float p1 = fast_exp2(__builtin_fmaf(sacc[8 * j + 2 * w + 1], scale_log2, -m));
-        psum += p0 + p1;
-        pb[j][w] = pack_bf16x2(p0, p1);
+        const bf16x2 pp = __builtin_convertvector((f32x2{p0, p1}), bf16x2);
+        pb[j][w] = __builtin_bit_cast(uint32_t, pp);
+        psum[j] = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{1.0f, 1.0f}, psum[j], false);
       }
-    l += psum;
+    l += psum[0] + psum[1];
     u32x4 va[DT][2];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -340,22 +351,31 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
 #pragma unroll
   for (int t = 0; t < PRE; ++t)
     if (t < ntiles) issue(t);
-  for (int t = 0; t < ntiles; t += TPB) {
-    Ids nid[TPB];  // (ids_of clamps past the context, so this is safe for any t)
+  // The loop runs once around the ring per outer iteration, unrolled, so that every tile's stage
+  // is a compile-time constant: the LDS reads then take the stage as an immediate offset instead
+  // of an address add per read.
+  static_assert(NS % TPB == 0, "the unrolled ring visits every stage");
+  for (int t0 = 0; t0 < ntiles; t0 += NS) {
 #pragma unroll
-    for (int k = 0; k < TPB; ++k) nid[k] = ids_of(t + PRE + k);
-    // issued so far: tiles 0 .. min(t + PRE, ntiles) - 1; needed now: t .. t+TPB-1
-    const int ahead = min(t + PRE, ntiles) - min(t + TPB, ntiles);
-    if (ahead >= 4) __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * LPT));
-    else if (ahead == 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * LPT));
-    else if (ahead == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPT));
-    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPT));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    __builtin_amdgcn_s_barrier();
+    for (int kb = 0; kb < NS; kb += TPB) {
+      const int t = t0 + kb;
+      if (t >= ntiles) break;
+      Ids nid[TPB];  // (ids_of clamps past the context, so this is safe for any t)
 #pragma unroll
-    for (int k = 0; k < TPB; ++k) {
-      if (t + PRE + k < ntiles) issue_ids(t + PRE + k, nid[k]);
-      if (t + k < ntiles) compute(t + k);
+      for (int k = 0; k < TPB; ++k) nid[k] = ids_of(t + PRE + k);
+      // issued so far: tiles 0 .. min(t + PRE, ntiles) - 1; needed now: t .. t+TPB-1
+      const int ahead = min(t + PRE, ntiles) - min(t + TPB, ntiles);
+      if (ahead >= 4) __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * LPT));
+      else if (ahead == 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * LPT));
+      else if (ahead == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPT));
+      else if (ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPT));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int k = 0; k < TPB; ++k) {
+        if (t + PRE + k < ntiles) issue_ids(t + PRE + k, (kb + PRE + k) % NS, nid[k]);
+        if (t + k < ntiles) compute(t + k, kb + k);
+      }
     }
   }
 
