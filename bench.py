@@ -533,22 +533,29 @@ def traffic_from_profile(workload, algorithmic):
     text = open(path).read()
     m = re.search(r"kernel_sources_sha256:\s*([0-9a-f]{64})", text)
     t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m or not t or m.group(1) != kernel_sources_sha():
+    if not m or not t or m.group(1) != kernel_sources_sha(workload):
         return None
     return float(t.group(1))
 
 
-def kernel_sources_sha():
-    """SHA-256 of the device sources' code: comments dropped and whitespace collapsed, so that
-    editing a comment does not disown counters taken on the same code."""
+def kernel_sources(workload):
+    """The device sources the workload's dominant kernel is compiled from."""
+    main = ("prefill.hip" if workload == "prefill-chunk" else
+            "blocks.hip" if workload in BLOCK_WORKLOADS else "decode.hip")
+    return [main, "common.hpp", "launch.hpp"]
+
+
+def kernel_sources_sha(workload):
+    """SHA-256 of the code of the sources the workload's dominant kernel is built from: comments
+    dropped and whitespace collapsed, so that editing a comment does not disown counters taken
+    on the same code."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_190_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp")):
-            text = open(os.path.join(csrc, f)).read()
-            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-            text = re.sub(r"//[^\n]*", " ", text)
-            h.update(f.encode() + b"\0" + " ".join(text.split()).encode())
+    for f in sorted(kernel_sources(workload)):
+        text = open(os.path.join(csrc, f)).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(f.encode() + b"\0" + " ".join(text.split()).encode())
     return h.hexdigest()
 
 
@@ -787,7 +794,7 @@ def summarize_pmc(fetch_dir, write_dir, workload, dominant):
     out += ["", "(`__amd_rocclr_copyBuffer` rows mix the input set-up copies and the calibration "
             "copies.)", "", f"dominant kernel: `{dom}`",
             f"traffic_bytes_per_launch: {avg[dom]:.6g}",
-            f"kernel_sources_sha256: {kernel_sources_sha()}"]
+            f"kernel_sources_sha256: {kernel_sources_sha(workload)}"]
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
     open(path, "w").write("\n".join(out) + "\n")
     return path
