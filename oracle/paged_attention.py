@@ -1,6 +1,6 @@
 """CPU oracle for paged attention -- TEST INFRASTRUCTURE ONLY.
 
-Only the tests, the graft smoke check and the bench's CPU-baseline leg may import this module.
+Only the tests, `__graft_entry__.smoke()` and the bench's CPU-baseline leg may import this module.
 The library's product path never calls it, and it shares no code with the HIP kernels, their
 host code or their binding.
 
