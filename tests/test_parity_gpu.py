@@ -276,6 +276,14 @@ PREFILL_CASES = [
     # more sequences than the kernel ranks (64): batch order
     ("past_rank_limit", 210, 70, 4, 2, 64, 16, [(7 * i) % 50 for i in range(70)],
      [1 + i % 5 for i in range(70)], "bf16"),
+    # key-tile counts 1 .. 24 (every position of the tile ring, both halves of a two-tile step,
+    # ragged last tiles): sequence s ends at 32 (s + 1) - s % 5 with a chunk of 1-3 rows
+    ("ring_lengths", 211, 24, 8, 2, 128, 16,
+     [32 * (i + 1) - i % 5 - (1 + i % 3) for i in range(24)], [1 + i % 3 for i in range(24)],
+     "bf16"),
+    ("ring_lengths_b32", 212, 20, 4, 1, 64, 32,
+     [32 * (i + 1) - (3 * i) % 7 - (2 + i % 4) for i in range(20)], [2 + i % 4 for i in range(20)],
+     "bf16"),
 ]
 
 
