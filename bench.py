@@ -539,16 +539,16 @@ def traffic_from_profile(workload, algorithmic):
 
 
 def kernel_sources(workload):
-    """The device sources the workload's dominant kernel is compiled from."""
+    """The sources that decide what the workload's dominant kernel does: the kernel's own file,
+    the shared device headers, and the host code that plans its launch (api.cpp)."""
     main = ("prefill.hip" if workload == "prefill-chunk" else
             "blocks.hip" if workload in BLOCK_WORKLOADS else "decode.hip")
-    return [main, "common.hpp", "launch.hpp"]
+    return [main, "common.hpp", "launch.hpp", "api.cpp"]
 
 
 def kernel_sources_sha(workload):
-    """SHA-256 of the code of the sources the workload's dominant kernel is built from: comments
-    dropped and whitespace collapsed, so that editing a comment does not disown counters taken
-    on the same code."""
+    """SHA-256 of the code of kernel_sources(workload): comments dropped and whitespace
+    collapsed, so that editing a comment does not disown counters taken on the same code."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_190_amd", "csrc")
     for f in sorted(kernel_sources(workload)):

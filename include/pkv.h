@@ -347,7 +347,8 @@ pkv_status pkv_paged_attention_decode_fp8(void* out, const void* q, const void* 
  *                     ignored for bf16); q is bf16; out_dtype PKV_BF16 or PKV_F32
  *   workspace         pkv_decode_shared_prefix_workspace_size(...) bytes
  * Other arguments as for pkv_paged_attention_decode (num_waves: waves of the balanced split of
- * the private suffixes, 0 = the default). Each shared prefix is split into chunks
+ * the private suffixes, 0 = the default; fewer are used when the suffixes have under 4 tiles
+ * per wave). Each shared prefix is split into chunks
  * of 256 tokens; a chunk is attended for 32 (member, query head) rows at a time over bf16
  * pools and 16 over E4M3 pools, and the private rest of every context goes through the
  * balanced split; a reduce kernel merges the pieces by log-sum-exp.
