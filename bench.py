@@ -220,7 +220,8 @@ def run_blocks(args, w):
         achieved = hbm / (kern_us * 1e-6) / 1e9
         result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1),
                               "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                              "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                              "frac": round(achieved / HBM_PEAK_GBS, 4),
+                              "traffic": traffic_from_profile(args.workload, hbm),
                               "kernel": "copy_blocks", "avg_us": round(kern_us, 2),
                               "algorithmic_bytes_per_launch": hbm}
         result.update(metric=f"{args.workload}: KV block copy HBM GB/s (read + write)",
