@@ -242,7 +242,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
   float m = -INFINITY;
-  float m_grow = -INFINITY;  // m + 8: the row max past which the reference max moves
+  // (m + 8) / scale_log2: the raw score past which the reference max moves
+  float m_grow_raw = -INFINITY;
+  const float inv_scale_log2 = 1.0f / scale_log2;
   float l = 0.f;
   const int qpos = r + my_i;           // this lane's query position
   const int wq_lo = r + w_tok0;        // the wave's first query position
@@ -279,20 +281,20 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
     float rmax = sacc[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) rmax = __builtin_elementwise_maximum(rmax, sacc[i]);
-    {
+    // Lazy rescaling: keep the old reference max unless the row's max grows by more than 2^8,
+    // so exponentials stay <= 256 and the output is rescaled only rarely. Each lane half tests
+    // its own 16 keys in raw units (a row grows exactly when one of its halves does); only
+    // then are the halves combined and scaled.
+    if (__builtin_amdgcn_ballot_w64(rmax > m_grow_raw)) {
       const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmax),
                                                       __float_as_uint(rmax), false, false);
-      rmax = __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
-    }
-    rmax *= scale_log2;
-    // Lazy rescaling: keep the old reference max unless the row's max grows by more than 2^8,
-    // so exponentials stay <= 256 and the output is rescaled only rarely.
-    const bool grow = rmax > m_grow;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float mnew = grow ? rmax : m;
+      const float row_raw =
+          __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+      const bool grow = row_raw > m_grow_raw;
+      const float mnew = grow ? row_raw * scale_log2 : m;
       const float alpha = fast_exp2(m - mnew);
       m = mnew;
-      m_grow = mnew + 8.0f;
+      m_grow_raw = (mnew + 8.0f) * inv_scale_log2;
       l *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
