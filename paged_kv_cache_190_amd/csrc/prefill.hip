@@ -245,7 +245,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
   // (m + 8) / scale_log2: the raw score past which the reference max moves
   float m_grow_raw = -INFINITY;
   const float inv_scale_log2 = 1.0f / scale_log2;
-  float l = 0.f;
+  float l[2] = {0.f, 0.f};  // row sum, in two halves that the dot2 chains extend
   const int qpos = r + my_i;           // this lane's query position
   const int wq_lo = r + w_tok0;        // the wave's first query position
   const int klim = min(qpos, n - 1);   // last visible key of this row
@@ -295,12 +295,14 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
       const float alpha = fast_exp2(m - mnew);
       m = mnew;
       m_grow_raw = (mnew + 8.0f) * inv_scale_log2;
-      l *= alpha;
+      l[0] *= alpha;
+      l[1] *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
     }
-    // The row sum takes the bf16-rounded weights that the P.V product uses, two per dot2.
-    float psum[2] = {0.f, 0.f};
+    // The row sum takes the bf16-rounded weights that the P.V product uses, two per dot2; the
+    // dot2 chains extend the two halves of the running sum directly.
+    float* psum = l;
     u32x4 pb[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -312,7 +314,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
         pb[j][w] = __builtin_bit_cast(uint32_t, pp);
         psum[j] = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{1.0f, 1.0f}, psum[j], false);
       }
-    l += psum[0] + psum[1];
+
     u32x4 va[DT][2];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -382,9 +384,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
   }
 
   if (!wave_active) return;
-  l = xor32_sum(l);
+  const float lsum = xor32_sum(l[0] + l[1]);
   if (!row_valid) return;
-  const float inv = 1.0f / l;
+  const float inv = 1.0f / lsum;
   OutT* o = out + (static_cast<int64_t>(q0 + my_i) * Hq + head) * D + 4 * hb;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
