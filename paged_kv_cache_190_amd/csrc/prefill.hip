@@ -196,22 +196,20 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
   // wave-uniform per tile (two candidates when B = 16); a lane's offset inside the block tile
   // does not change from tile to tile (tiles start at multiples of 32, which B divides or
   // equals), so it is computed once. Each wave's instructions are all K or all V.
-  int soff[LPT];
+  const char* lsrc[LPT];  // the lane's 16 bytes inside block 0 of the pool it copies from
   bool ssel[LPT];
-  bool sk[LPT];
 #pragma unroll
   for (int j = 0; j < LPT; ++j) {
     const int c = LPT * wave + j;
-    sk[j] = c < KC;
     if (c < KC) {
       const int prow = c * (64 / CPR) + lane / CPR;
       const int chunk = (lane % CPR) ^ kswz<D>(prow);
-      soff[j] = (prow % B) * D + 8 * chunk;
+      lsrc[j] = reinterpret_cast<const char*>(kg + (prow % B) * D + 8 * chunk);
       ssel[j] = B == 16 && prow >= 16;
     } else {
       const int d = (c - KC) * 16 + lane / 4;
       const int chunk = (lane & 3) ^ vswz(d);  // keys 8*chunk .. 8*chunk+7
-      soff[j] = d * B + (8 * chunk) % B;
+      lsrc[j] = reinterpret_cast<const char*>(vg + d * B + (8 * chunk) % B);
       ssel[j] = B == 16 && chunk >= 2;
     }
   }
@@ -222,15 +220,17 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
     const uint32_t a = block_id(lb0);
     return Ids{a, B == 16 ? block_id(lb0 + 1) : a};
   };
+  // A block of a pool is 2 * blk_stride bytes, which fits 32 bits (num_q_heads <= 65535 bounds
+  // the KV heads), so a lane's address is one 32 x 32 -> 64-bit multiply-add.
+  const uint32_t blk_bytes = 2u * blk_stride;
   auto issue_ids = [&](int t, int stage, Ids id) {
     unsigned char* st = smem + stage * STAGE;
-    const uint64_t o0 = static_cast<uint64_t>(id.a) * blk_stride;
-    const uint64_t o1 = (B == 16) ? static_cast<uint64_t>(id.b) * blk_stride : o0;
     // (The source pointer is a named variable: given a conditional expression directly, the
     // builtin makes clang drop this kernel's host-side launch stub without a diagnostic.)
 #pragma unroll
     for (int j = 0; j < LPT; ++j) {
-      const uint16_t* src = (sk[j] ? kg : vg) + (ssel[j] ? o1 : o0) + soff[j];
+      const uint32_t bid = (B == 16 && ssel[j]) ? id.b : id.a;
+      const char* src = lsrc[j] + static_cast<uint64_t>(bid) * blk_bytes;
       __builtin_amdgcn_global_load_lds(src, st + (LPT * wave + j) * 1024, 16, 0, 0);
     }
   };
