@@ -270,6 +270,15 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
     for (int kk = 0; kk < KK; ++kk) sacc = mfma32x32x16(ka[kk], qf[kk], sacc);
     // Scores stay in raw units until the exponential: the row max is taken on the raw values
     // (scale_log2 >= 0 keeps the order) and p = 2^(raw * scale_log2 - m) is one fma.
+    // The V operands are read from LDS now, while the score products finish.
+    u32x4 va[DT][2];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const unsigned char* vrow = st + K_BYTES + (32 * dt + col) * 64;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        va[dt][j] = *reinterpret_cast<const u32x4*>(vrow + 16 * ((2 * hb + j) ^ vx));
+    }
     const bool edge = key0 + 31 > wq_lo || key0 + 31 >= n;  // diagonal or past the context
     if (edge) {
 #pragma unroll
@@ -315,14 +324,6 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(
         psum[j] = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{1.0f, 1.0f}, psum[j], false);
       }
 
-    u32x4 va[DT][2];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const unsigned char* vrow = st + K_BYTES + (32 * dt + col) * 64;
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        va[dt][j] = *reinterpret_cast<const u32x4*>(vrow + 16 * ((2 * hb + j) ^ vx));
-    }
     const int vlim = n - key0;  // keys at or past n may hold stale words: clear their V
     if (vlim < 32) {
 #pragma unroll
