@@ -833,6 +833,70 @@ def summarize_mfma(d, workload):
     return path
 
 
+# Instruction and stall counters of the dominant kernel, one rocprofv3 pass per set (each set
+# within one pass's hardware limits).
+COUNTER_SETS = (
+    "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS "
+    "SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_ANY",
+    "SQ_LDS_IDX_ACTIVE SQ_LDS_DATA_FIFO_FULL SQ_LDS_CMD_FIFO_FULL SQ_LDS_BANK_CONFLICT "
+    "SQ_INSTS_LDS_LOAD_BANDWIDTH SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES "
+    "SQ_INST_LEVEL_LDS GRBM_GUI_ACTIVE",
+    "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU SQ_INSTS_VALU_TRANS_F32 "
+    "SQ_ACTIVE_INST_MISC SQ_ACTIVE_INST_SCA SQ_WAVES GRBM_GUI_ACTIVE",
+)
+COUNTERS_CMD = ("rocprofv3 --pmc {c} -f csv -d {d} -o run -- python3 bench.py --workload {w} "
+                "--steps 10 --warmup 60 --no-cpu-baseline")
+
+
+def summarize_counters(dirs, workload, dominant):
+    """Per-dispatch averages of the COUNTER_SETS passes for the dominant kernel, with the ratios
+    they give (shares of wave cycles, MFMA busy and co-issue shares, instructions per MFMA)."""
+    vals = {}
+    kernel = None
+    for d in dirs:
+        per = {}
+        for r in _csv(_find(d, "counter_collection.csv")):
+            k = _short(r["Kernel_Name"])
+            if k.startswith(dominant):
+                kernel = k
+                per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        for c, v in per.items():
+            vals.setdefault(c, sum(v) / len(v))
+    out = [f"# Instruction and stall counters, workload {workload}", "",
+           "Commands (from the repository root), one pass per counter set:", ""]
+    for c, d in zip(COUNTER_SETS, dirs):
+        out.append(f"- `{COUNTERS_CMD.format(c=c, d=_rel(d), w=workload)}`")
+    out += ["", f"Kernel: `{kernel}`; per-dispatch averages (each counter summed over the GPU).",
+            "", "| counter | per dispatch |", "|---|---|"]
+    for c in sorted(vals):
+        out.append(f"| {c} | {vals[c]:.4g} |")
+    def ratio(a, b):
+        return vals[a] / vals[b] if a in vals and b in vals and vals[b] else float("nan")
+    gui = vals.get("GRBM_GUI_ACTIVE", float("nan"))
+    derived = [
+        ("wave cycles issuing any instruction", ratio("SQ_ACTIVE_INST_ANY", "SQ_WAVE_CYCLES")),
+        ("wave cycles issuing VALU", ratio("SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES")),
+        ("wave cycles waiting (any)", ratio("SQ_WAIT_ANY", "SQ_WAVE_CYCLES")),
+        ("wave cycles waiting on LDS", ratio("SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES")),
+        ("MFMA busy (of 1024 SIMDs x GUI-active cycles of one XCD)",
+         vals.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / (gui / 8 * 1024)),
+        ("MFMA-busy cycles co-issuing VALU",
+         ratio("SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES")),
+        ("VALU instructions per MFMA instruction (as counted)",
+         ratio("SQ_INSTS_VALU", "SQ_INSTS_MFMA")),
+        ("transcendental per MFMA", ratio("SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_MFMA")),
+        ("SALU per MFMA", ratio("SQ_INSTS_SALU", "SQ_INSTS_MFMA")),
+        ("LDS instructions per MFMA", ratio("SQ_INSTS_LDS", "SQ_INSTS_MFMA")),
+        ("LDS bank conflicts per LDS-active cycle",
+         ratio("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE")),
+    ]
+    out += ["", "| derived | value |", "|---|---|"]
+    out += [f"| {name} | {v:.3f} |" for name, v in derived]
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.md")
+    open(path, "w").write("\n".join(out) + "\n")
+    return path
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -855,9 +919,15 @@ def main():
                     help="write profiles/traffic_<workload>.md from FETCH_SIZE / WRITE_SIZE runs")
     ap.add_argument("--summarize-mfma", metavar="DIR",
                     help="write profiles/mfma_<workload>.md from an MFMA counter run")
+    ap.add_argument("--summarize-counters", nargs=len(COUNTER_SETS), metavar="DIR",
+                    help="write profiles/counters_<workload>.md from the COUNTER_SETS passes")
     args = ap.parse_args()
     if args.summarize_mfma:
         print(summarize_mfma(args.summarize_mfma, args.workload))
+    if args.summarize_counters:
+        dom = "prefill" if args.workload == "prefill-chunk" else "decode"
+        print(summarize_counters(args.summarize_counters, args.workload, dom))
+        return
     if args.summarize_trace or args.summarize_pmc:
         if args.summarize_trace:
             print(summarize_trace(args.summarize_trace, args.workload))
