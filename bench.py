@@ -542,9 +542,10 @@ def traffic_from_profile(workload, algorithmic):
 def kernel_sources(workload):
     """The sources that decide what the workload's dominant kernel does: the kernel's own file,
     the shared device headers, and the host code that plans its launch (api.cpp)."""
-    main = ("prefill.hip" if workload == "prefill-chunk" else
-            "blocks.hip" if workload in BLOCK_WORKLOADS else "decode.hip")
-    return [main, "common.hpp", "launch.hpp", "api.cpp"]
+    if workload in BLOCK_WORKLOADS:
+        return ["blocks.hip", "common.hpp", "launch.hpp", "api.cpp"]
+    main = "prefill.hip" if workload == "prefill-chunk" else "decode.hip"
+    return [main, "common.hpp", "lds_tile.hpp", "launch.hpp", "api.cpp"]
 
 
 def kernel_sources_sha(workload):

@@ -190,10 +190,12 @@ size_t fixed_workspace_bytes(int S, int Hq, int D, int NP) {
 
 // Balanced split (bf16 inputs, partition_size == 0).
 constexpr int kMinTilesPerWave = 8;     // 256 tokens
-// The prefix-aware decode's suffix waves: its suffixes are short and its prefix units carry the
-// rest of the work, so more, shorter suffix pieces pay there (27.9-28.0 against 28.4-28.8 us on
-// the shared-prefix batch).
-constexpr int kMinTilesPerWavePrefix = 4;
+// The prefix-aware decode's suffix waves: its suffixes are short and its prefix chunks carry the
+// rest of the work, so more, shorter suffix pieces pay there. On the shared-prefix batch: over
+// E4M3 pools 4 against 8 tiles gave 20.6-20.8 against 21.0-21.2 us; over bf16 pools (suffix
+// waves filling the CUs beside the prefix workgroups) 3 gave 24.0-24.6 us, 4 24.7-25.1 and 2
+// 24.4-24.8.
+int prefix_min_tiles(int kv_dtype) { return kv_dtype == PKV_FP8_E4M3 ? 4 : 3; }
 constexpr int kDefaultDecodeWaves = 1024;
 // E4M3 pools: the same count measured best (768 - 2048 tried; their tile loop keeps three
 // tiles in flight instead).
@@ -492,7 +494,7 @@ size_t pkv_decode_shared_prefix_workspace_size(int num_seqs, int num_q_heads, in
     return 0;
   return balanced_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                        kv_dtype == PKV_FP8_E4M3 ? kDefaultDecodeWavesFp8 : kDefaultDecodeWaves,
-                       prefix_chunks(max_prefix_len), kMinTilesPerWavePrefix)
+                       prefix_chunks(max_prefix_len), prefix_min_tiles(kv_dtype))
       .bytes;
 }
 
@@ -536,17 +538,35 @@ pkv_status pkv_paged_attention_decode_shared_prefix(void* out, const void* q, co
                 max_prefix_len);
   const int G = num_q_heads / num_kv_heads;
   const int nch = prefix_chunks(max_prefix_len);
-  // column units: 16 (sequence, query head) columns each over E4M3 pools, 32 over bf16 pools
-  const int cols_per_unit = kv_dtype == PKV_FP8_E4M3 ? 16 : 32;
+  // column units: 16 (sequence, query head) columns each over E4M3 pools (one wave); over bf16
+  // pools a workgroup of kPrefixWgWaves waves takes kPrefixWgColumns
+  const int cols_per_unit = kv_dtype == PKV_FP8_E4M3 ? 16 : pkv::kPrefixWgColumns;
   const long long col_tiles =
       (static_cast<long long>(max_group_size) * G + cols_per_unit - 1) / cols_per_unit;
   const long long units = static_cast<long long>(num_groups) * num_kv_heads * nch * col_tiles;
-  const long long waves_p = (units + 7) / 8 * 8;
-  const int default_waves =
-      kv_dtype == PKV_FP8_E4M3 ? kDefaultDecodeWavesFp8 : kDefaultDecodeWaves;
-  st = setup_balanced(a, workspace, workspace_bytes, default_waves, num_waves, nch,
-                      kMinTilesPerWavePrefix);
+  const long long waves_p = (units + 7) / 8 * 8;  // prefix waves (E4M3) or workgroups (bf16)
+  const int min_tiles = prefix_min_tiles(kv_dtype);
+  st = setup_balanced(a, workspace, workspace_bytes,
+                      kv_dtype == PKV_FP8_E4M3 ? kDefaultDecodeWavesFp8 : kDefaultDecodeWaves,
+                      num_waves, nch, min_tiles);
   if (st != PKV_OK) return st;
+  if (kv_dtype != PKV_FP8_E4M3 && num_waves == 0) {
+    // Over bf16 pools every workgroup takes one CU (the prefix chunks' LDS): by default the
+    // suffix waves fill the CUs that the prefix workgroups leave, all resident from the start
+    // (more waves, dispatched as CUs free up, measured 31 against 24 us on the shared-prefix
+    // batch).
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      return fail(PKV_ERR_HIP, "cannot read the device's compute unit count");
+    const long long free_cus = std::max<long long>(cus - waves_p, cus / 4);
+    st = setup_balanced(a, workspace, workspace_bytes,
+                        static_cast<int>(std::min<long long>(free_cus * pkv::kPrefixWgWaves,
+                                                             kMaxDecodeWaves)),
+                        0, nch, min_tiles);
+    if (st != PKV_OK) return st;
+  }
   if (waves_p + a.waves > 0x7fffffffLL)
     return fail(PKV_ERR_UNSUPPORTED, "too many prefix units (%lld)", units);
   a.num_groups = num_groups;

@@ -41,6 +41,7 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "lds_tile.hpp"
 
 namespace pkv {
 
@@ -298,36 +299,6 @@ __device__ __forceinline__ void attend_tiles(WaveAttn<D>& st, const u32x4 (&qf)[
       compute(tb, t + 1);
     } else {
       compute(ta, t);
-    }
-  }
-}
-
-// attend_tiles for two 16-column tiles at once (the prefix units): each K/V tile is loaded once
-// and feeds both column tiles' products; both column tiles see the same tokens. One register
-// set (the prefix kernel is held to 256 VGPRs): a tile's loads, mostly L2 hits, are waited for
-// at once, and the suffix wave that shares the SIMD runs meanwhile.
-template <int D, int B>
-__device__ __forceinline__ void attend_tiles2(WaveAttn<D> (&st)[2],
-                                              const u32x4 (&qf)[2][D / 32],
-                                              const uint16_t* __restrict__ kpool,
-                                              const uint16_t* __restrict__ vpool,
-                                              const int32_t* __restrict__ bt, int n, int g,
-                                              int Hkv, int tok_begin, int tok_end,
-                                              float scale_log2, const bool (&col_used)[2]) {
-  const int lg = (threadIdx.x & 63) >> 4;
-  const int ntiles = (tok_end - tok_begin + 31) >> 5;
-  TileWalk<D, B> wk(kpool, vpool, n, g, Hkv, tok_begin);
-  KvTile<D, B> ta;
-  for (int c0 = 0; c0 < ntiles; c0 += TileWalk<D, B>::kChunkTiles) {
-    const int c1 = min(ntiles, c0 + TileWalk<D, B>::kChunkTiles);
-    wk.begin_chunk(bt, c0);
-    for (int t = c0; t < c1; ++t) {
-      wk.template load<false>(ta, t);
-      const int tok0 = tok_begin + 32 * t;
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-        tile_update<D>(st[c], ta.k, ta.v, qf[c], tok_end - tok0, n - tok0, scale_log2, lg,
-                       col_used[c]);
     }
   }
 }
@@ -687,11 +658,13 @@ __device__ __forceinline__ int wave_incl_scan_i(int v) {
 // Shared prefixes (the prefix-aware decode): sequences come in groups of consecutive ones,
 // group i being sequences group_start[i] .. group_start[i+1]-1, whose first group_prefix_len[i]
 // tokens (a multiple of B) are the same physical blocks. Such a prefix is attended once per
-// group: a prefix unit is one wave for (group, KV head, 16 query columns, one chunk of kPrefixChunk
-// prefix tokens), the 16 columns being (member sequence, query head) pairs -- the K/V tile is
-// then shared by 16 useful query rows instead of one sequence's G heads. The private rest of each
-// context goes through the balanced split as usual. A row's partials: the prefix chunks at slots
-// 0 .. pc-1 (pc = ceil(prefix / kPrefixChunk)), then its suffix pieces.
+// group, in units of (group, KV head, chunk of kPrefixChunk prefix tokens, block of query
+// columns), the columns being (member sequence, query head) pairs: a chunk's K/V is then shared
+// by every member's query heads instead of one sequence's G heads. Over bf16 pools a unit is a
+// workgroup of kPrefixWgWaves waves and kPrefixWgColumns columns (prefix_wg); over E4M3 pools it
+// is one wave and 16 columns (prefix_unit). The private rest of each context goes through the
+// balanced split as usual. A row's partials: the prefix chunks at slots 0 .. pc-1
+// (pc = ceil(prefix / kPrefixChunk)), then its suffix pieces.
 constexpr int kPrefixChunk = kPrefixChunkTokens;
 
 struct PrefixInfo {
@@ -830,8 +803,8 @@ __device__ __forceinline__ void balanced_body(
     const int32_t* bt = block_table + static_cast<int64_t>(s) * MB;
     const int tb = pre + 32 * t_begin;
     const int te = min(pre + 32 * t_end, n);
-    // the prefix kernel's suffix waves run beside prefix units re-reading their tiles from
-    // cache: cacheable loads there (measured faster than streamed ones)
+    // the prefix kernels' suffix waves: cacheable loads (measured faster than streamed ones,
+    // 24.4 against 26.1 us on the shared-prefix batch over bf16 pools)
     const bool stream = !PREFIX && !shares_first_block(block_table, s, S, MB);
     if constexpr (PROBE) {
       probe_acc ^= stream ? probe_tiles<D, B, true>(kpool, vpool, bt, n, g, Hkv, tb, te)
@@ -958,17 +931,17 @@ __global__ __launch_bounds__(64 * kBalancedWavesPerGroup) void decode_read_probe
       PrefixInfo{nullptr, nullptr, 0}, StepInfo{}, sink);
 }
 
-// One prefix unit (see PrefixInfo). Units are numbered (group, KV head, chunk, column tile),
-// column tile fastest; `unit` is that number.
-template <int D, int B, typename OutT, typename KvT>
+// One prefix unit over E4M3 pools (see PrefixInfo): one wave for (group, KV head, chunk, 16
+// query columns). Units are numbered (group, KV head, chunk, column tile), column tile fastest;
+// `unit` is that number.
+template <int D, int B, typename OutT>
 __device__ __forceinline__ void prefix_unit(
     int64_t unit, OutT* __restrict__ out, float* __restrict__ part_o,
     float* __restrict__ part_m, float* __restrict__ part_l, const uint16_t* __restrict__ q,
-    const KvT* __restrict__ kpool, const KvT* __restrict__ vpool,
+    const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ context_lens, int Hq,
     int Hkv, int G, int MB, int KSTRIDE, int CT, int NCH, float scale_log2, float out_scale,
     PrefixInfo pf) {
-  constexpr bool kFp8 = sizeof(KvT) == 1;
   const int lane = threadIdx.x;
   const int lg = lane >> 4;
   const int ct = static_cast<int>(unit % CT);
@@ -982,59 +955,312 @@ __device__ __forceinline__ void prefix_unit(
   const int members = pf.group_start[gi + 1] - s0;
   const int pre = pf.group_prefix_len[gi];
   const int tok0 = ch * kPrefixChunk;
-  constexpr int NCW = kFp8 ? 1 : 2;  // column tiles per unit
-  if (tok0 >= pre || ct * 16 * NCW >= members * G) return;
+  if (tok0 >= pre || ct * 16 >= members * G) return;
   const int32_t* bt = block_table + static_cast<int64_t>(s0) * MB;  // the shared blocks
   const int te = min(pre, tok0 + kPrefixChunk);
   const int pc = (pre + kPrefixChunk - 1) / kPrefixChunk;
-  const float osc = kFp8 ? out_scale : 1.0f;
-  bool valid[NCW];
-  int seq[NCW];
-  int64_t row[NCW];
-  u32x4 qf[NCW][D / 32];
-  WaveAttn<D> st[NCW];
-#pragma unroll
-  for (int k = 0; k < NCW; ++k) {
-    const int c = (ct * NCW + k) * 16 + (lane & 15);
-    valid[k] = c < members * G;
-    const int m = valid[k] ? c / G : 0;
-    seq[k] = s0 + m;
-    const int h = g * G + (valid[k] ? c - m * G : 0);
-    row[k] = static_cast<int64_t>(seq[k]) * Hq + h;
-    attn_init(st[k]);
-    if constexpr (kFp8) load_q_fp8<D>(qf[k], q + row[k] * D, valid[k], lg);
-    else load_q<D>(qf[k], q + row[k] * D, valid[k], lg);
-  }
-  if constexpr (kFp8)
-    attend_tiles_fp8<D, B, 2, false>(st[0], qf[0], kpool, vpool, bt, pre, g, Hkv, tok0, te,
-                                     scale_log2);
+  const int c = ct * 16 + (lane & 15);
+  const bool valid = c < members * G;
+  const int m = valid ? c / G : 0;
+  const int seq = s0 + m;
+  const int64_t row = static_cast<int64_t>(seq) * Hq + g * G + (valid ? c - m * G : 0);
+  u32x4 qf[D / 32];
+  WaveAttn<D> st;
+  attn_init(st);
+  load_q_fp8<D>(qf, q + row * D, valid, lg);
+  attend_tiles_fp8<D, B, 2, false>(st, qf, kpool, vpool, bt, pre, g, Hkv, tok0, te, scale_log2);
+  // Each lane's column is its own row: reduce l over the 4 row groups only (lanes ^16, ^32).
+  const float l_total = xor32_sum(xor16_sum(st.l));
+  if (!valid) return;
+  if (pc == 1 && context_lens[seq] == pre)
+    write_final<D>(out + row * D, st, l_total, lg, out_scale);
   else
-    attend_tiles2<D, B>(st, qf, kpool, vpool, bt, pre, g, Hkv, tok0, te, scale_log2, valid);
-#pragma unroll
-  for (int k = 0; k < NCW; ++k) {
-    // Each lane's column is its own row: reduce l over the 4 row groups only (lanes ^16, ^32).
-    const float l_total = xor32_sum(xor16_sum(st[k].l));
-    if (!valid[k]) continue;
-    if (pc == 1 && context_lens[seq[k]] == pre)
-      write_final<D>(out + row[k] * D, st[k], l_total, lg, osc);
-    else
-      write_partial<D>(part_o, part_m, part_l, row[k] * KSTRIDE + ch, st[k], l_total, lg, osc);
-  }
+    write_partial<D>(part_o, part_m, part_l, row * KSTRIDE + ch, st, l_total, lg, out_scale);
 }
 
-// Prefix-aware decode: Wp prefix-unit waves and Ws = gridDim.x - Wp waves of the balanced split
-// of the suffixes. The two kinds alternate in runs of 8 workgroups (while both last), so that
-// prefix work, which mostly hits in L2, runs beside suffix work, which streams from HBM.
-// Workgroups go to the 8 XCDs round-robin; prefix units are numbered so that the column tiles of
-// one (group, KV head, chunk), which read the same K/V, land on the same XCD. At most 256
-// VGPRs, so that two waves share each SIMD (both kinds of work run side by side).
-template <int D, int B, typename OutT, typename KvT>
+// Prefix chunks over bf16 pools, one workgroup of kPrefixWgWaves waves per (group, KV head,
+// chunk, block of 32 * kPrefixWgWaves query columns): the columns are (member sequence, query
+// head) pairs, 32 per wave. The chunk's K/V tiles (kPrefixChunk tokens of the shared blocks) are
+// copied into LDS once, all of them at the start (global_load_lds; no LDS stage is reused), and
+// every wave computes its columns against each tile as the chunked prefill does against its
+// rows, without a causal mask (every member's query follows the whole prefix):
+//   S^T[32 keys][32 columns] = K_tile . Q^T,  online softmax per column,
+//   O^T[D][32 columns] += V_tile^T . P^T      (32x32x16 MFMAs)
+// Each column leaves one partial (m, l, O / l) at its row's slot for the chunk, or its final
+// output when the prefix is one chunk and the whole context.
+constexpr int kPrefixWgCols = kPrefixWgColumns;
+
+// f(std::integral_constant<int, i>{}) for i = 0 .. N-1, in order (i usable as a constant).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for_from(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_from<I + 1, N>(f);
+  }
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) { static_for_from<0, N>(f); }
+constexpr int kPrefixChunkTiles = kPrefixChunk / 32;
+
+template <int D>
+constexpr int prefix_stage_bytes() { return 32 * 2 * D + D * 64; }  // K tile + V tile
+
+template <int D, int B, typename OutT>
+__device__ __forceinline__ void prefix_wg(
+    int64_t unit, unsigned char* __restrict__ smem, OutT* __restrict__ out,
+    float* __restrict__ part_o, float* __restrict__ part_m, float* __restrict__ part_l,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kpool,
+    const uint16_t* __restrict__ vpool, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ context_lens, int Hq, int Hkv, int G, int MB, int KSTRIDE, int CB,
+    int NCH, float scale_log2, int neg_scale, PrefixInfo pf) {
+  constexpr int KK = D / 16;              // QK MFMA steps
+  constexpr int DT = D / 32;              // PV output tiles
+  constexpr int NW = kPrefixWgWaves;
+  constexpr int NCT = kPrefixChunkTiles;  // tiles per chunk, one LDS stage each
+  constexpr int KROW = 2 * D;             // bytes of one K row in LDS
+  constexpr int CPR = D / 8;              // 16-byte chunks per K row
+  constexpr int K_BYTES = 32 * KROW;
+  constexpr int STAGE = prefix_stage_bytes<D>();
+  constexpr int KC = K_BYTES / 1024;      // 1 KiB DMA instructions for K (V follows at KC)
+  constexpr int LPT = STAGE / 1024 / NW;  // DMA instructions per wave per tile
+  static_assert(LPT >= 1 && (STAGE / 1024) % NW == 0, "DMA work must split evenly over waves");
+  static_assert(NCT * LPT <= 63, "every DMA of the chunk fits the vmcnt counter");
+
+  const int cb = static_cast<int>(unit % CB);
+  int64_t r = unit / CB;
+  const int ch = static_cast<int>(r % NCH);
+  r /= NCH;
+  const int g = static_cast<int>(r % Hkv);
+  const int gi = static_cast<int>(r / Hkv);
+  // (all of these are uniform over the workgroup, so whole workgroups leave together)
+  if (gi >= pf.NG) return;
+  const int s0 = pf.group_start[gi];
+  const int ncols = (pf.group_start[gi + 1] - s0) * G;
+  const int pre = pf.group_prefix_len[gi];
+  const int tok0 = ch * kPrefixChunk;
+  if (tok0 >= pre || cb * kPrefixWgCols >= ncols) return;
+  const int te = min(pre, tok0 + kPrefixChunk);
+  const int pblk = pre / B;  // the prefix's blocks (pre is a multiple of B)
+  const int32_t* bt = block_table + static_cast<int64_t>(s0) * MB;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 31;
+  const int hb = lane >> 5;
+  const int c = cb * kPrefixWgCols + 32 * wave + col;
+  const bool valid = c < ncols;
+  const bool wave_active = cb * kPrefixWgCols + 32 * wave < ncols;
+  const int mi = valid ? c / G : 0;
+  const int64_t row = static_cast<int64_t>(s0 + mi) * Hq + g * G + (valid ? c - mi * G : 0);
+
+  u32x4 qf[KK];
+  {
+    // A negative scale is applied as |scale| on -q (bf16 negation flips the sign bits), so the
+    // maximum can be taken on the raw scores. A column past the group reads the group's first
+    // query (its results are never stored), so that every load is unconditional and none has
+    // to be waited for before the DMAs are issued.
+    const uint16_t* qrow = q + row * D + 8 * hb;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qf[kk] = load16(qrow + 16 * kk);
+  }
+
+  // DMA: instruction j of wave w fills KiB (LPT * w + j) of a stage. K instructions cover
+  // 64 / CPR key rows each, V instructions 16 dims x 32 keys; a lane's offset inside its block
+  // is the same for every tile, so its source is a fixed address inside block 0 of the pool
+  // plus the tile's block id times the block's bytes.
+  const uint16_t* kg = kpool + static_cast<int64_t>(g) * B * D;
+  const uint16_t* vg = vpool + static_cast<int64_t>(g) * B * D;
+  const char* lsrc[LPT];
+  bool ssel[LPT];
+#pragma unroll
+  for (int j = 0; j < LPT; ++j) {
+    const int ci = LPT * wave + j;
+    if (ci < KC) {
+      const int prow = ci * (64 / CPR) + lane / CPR;
+      const int chunk = (lane % CPR) ^ kswz<D>(prow);
+      lsrc[j] = reinterpret_cast<const char*>(kg + (prow % B) * D + 8 * chunk);
+      ssel[j] = B == 16 && prow >= 16;
+    } else {
+      const int d = (ci - KC) * 16 + lane / 4;
+      const int chunk = (lane & 3) ^ vswz(d);  // keys 8*chunk .. 8*chunk+7
+      lsrc[j] = reinterpret_cast<const char*>(vg + d * B + (8 * chunk) % B);
+      ssel[j] = B == 16 && chunk >= 2;
+    }
+  }
+  const uint32_t blk_bytes = 2u * static_cast<uint32_t>(Hkv) * B * D;  // < 2^32
+  // Every stage is filled, also past the chunk's last tile (those repeat the prefix's last
+  // blocks and are never computed), so that the count of DMAs, and each wait below, is fixed.
+  // The chunk's block ids first (uniform indexes: scalar loads, which do not count in vmcnt),
+  // so that their loads overlap.
+  constexpr int NID = NCT * 32 / B;
+  uint32_t ids[NID];
+#pragma unroll
+  for (int i = 0; i < NID; ++i)
+    ids[i] = static_cast<uint32_t>(
+        bt[__builtin_amdgcn_readfirstlane(min(tok0 / B + i, pblk - 1))]);
+  // q has arrived before the DMAs start counting in the same counter (its loads overlap the
+  // block ids' loads); the tile waits below then count DMAs only.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  {
+    const uint32_t flip = neg_scale ? 0x80008000u : 0u;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qf[kk] ^= flip;
+  }
+#pragma unroll
+  for (int t = 0; t < NCT; ++t) {
+    const uint32_t ida = ids[t * 32 / B];
+    const uint32_t idb = B == 16 ? ids[t * 32 / B + 1] : ida;
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const uint32_t bid = (B == 16 && ssel[j]) ? idb : ida;
+      const char* src = lsrc[j] + static_cast<uint64_t>(bid) * blk_bytes;
+      __builtin_amdgcn_global_load_lds(src, smem + t * STAGE + (LPT * wave + j) * 1024, 16, 0, 0);
+    }
+  }
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+  float m = -INFINITY;
+  float m_grow_raw = -INFINITY;  // (m + 8) / scale_log2: the raw score past which m moves
+  const float inv_scale_log2 = 1.0f / scale_log2;
+  float l[2] = {0.f, 0.f};
+  // MFMA row of the K operand -> key within the tile: lane half hb gets keys 16*hb + i.
+  const int krow = 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3);
+  const int kbase = krow * KROW;
+  const int kx = kswz<D>(krow);
+  const int vx = vswz(col);
+
+  auto compute = [&](int t) {
+    const int key0 = tok0 + 32 * t;
+    const unsigned char* st = smem + t * STAGE;
+    f32x16 sacc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+    u32x4 ka[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      ka[kk] = *reinterpret_cast<const u32x4*>(st + kbase + 16 * ((2 * kk + hb) ^ kx));
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) sacc = mfma32x32x16(ka[kk], qf[kk], sacc);
+    u32x4 va[DT][2];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const unsigned char* vrow = st + K_BYTES + (32 * dt + col) * 64;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        va[dt][j] = *reinterpret_cast<const u32x4*>(vrow + 16 * ((2 * hb + j) ^ vx));
+    }
+    const int vlim = te - key0;  // keys of the tile inside the chunk
+    if (vlim < 32) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (16 * hb + i >= vlim) sacc[i] = -INFINITY;
+    }
+    float rmax = sacc[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) rmax = __builtin_elementwise_maximum(rmax, sacc[i]);
+    // Lazy rescaling as in the chunked prefill: the reference max moves only when a column's
+    // max grows past it by more than 2^8; each lane half tests its own keys in raw units.
+    if (__builtin_amdgcn_ballot_w64(rmax > m_grow_raw)) {
+      const auto rr = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmax),
+                                                       __float_as_uint(rmax), false, false);
+      const float col_raw =
+          __builtin_elementwise_maximum(__uint_as_float(rr[0]), __uint_as_float(rr[1]));
+      const bool grow = col_raw > m_grow_raw;
+      const float mnew = grow ? col_raw * scale_log2 : m;
+      const float alpha = fast_exp2(m - mnew);
+      m = mnew;
+      m_grow_raw = (mnew + 8.0f) * inv_scale_log2;
+      l[0] *= alpha;
+      l[1] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+    }
+    u32x4 pb[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float p0 = fast_exp2(__builtin_fmaf(sacc[8 * j + 2 * w], scale_log2, -m));
+        const float p1 = fast_exp2(__builtin_fmaf(sacc[8 * j + 2 * w + 1], scale_log2, -m));
+        const bf16x2 pp = __builtin_convertvector((f32x2{p0, p1}), bf16x2);
+        pb[j][w] = __builtin_bit_cast(uint32_t, pp);
+        l[j] = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{1.0f, 1.0f}, l[j], false);
+      }
+    if (vlim < 32) {  // words past the chunk may hold anything: clear their V
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int k0 = 16 * hb + 8 * j + 2 * w;
+          const uint32_t keep =
+              (k0 < vlim ? 0x0000ffffu : 0u) | (k0 + 1 < vlim ? 0xffff0000u : 0u);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) va[dt][j][w] &= keep;
+        }
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[dt] = mfma32x32x16(va[dt][j], pb[j], acc[dt]);
+  };
+
+  const int ntiles = (te - tok0 + 31) >> 5;
+  // Tile t: this wave's DMAs of it are done once at most (NCT - 1 - t) * LPT remain (the q loads
+  // were issued first); the barrier then covers every wave's.
+  static_for<NCT>([&](auto tc) {
+    constexpr int t = decltype(tc)::value;
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NCT - 1 - t) * LPT));
+    __builtin_amdgcn_s_barrier();
+    if (t < ntiles && wave_active) compute(t);
+  });
+
+  if (!wave_active) return;
+  const float lsum = xor32_sum(l[0] + l[1]);
+  if (!valid) return;
+  const int pc = (pre + kPrefixChunk - 1) / kPrefixChunk;
+  const int seq = s0 + mi;
+  const float inv = 1.0f / lsum;
+  if (pc == 1 && context_lens[seq] == pre) {
+    OutT* o = out + row * D + 4 * hb;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        store_out(o + 32 * dt + 8 * (i >> 2) + (i & 3), acc[dt][i] * inv);
+    return;
+  }
+  const int64_t idx = row * KSTRIDE + ch;
+  if (hb == 0) {
+    part_m[idx] = m;
+    part_l[idx] = lsum;
+  }
+  float* o = part_o + idx * D + 4 * hb;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4)
+      *reinterpret_cast<f32x4*>(o + 32 * dt + 8 * i4) =
+          f32x4{acc[dt][4 * i4], acc[dt][4 * i4 + 1], acc[dt][4 * i4 + 2], acc[dt][4 * i4 + 3]} *
+          inv;
+}
+
+// Prefix-aware decode over E4M3 pools: Wp prefix-unit waves and Ws = gridDim.x - Wp waves of the
+// balanced split of the suffixes. The two kinds alternate in runs of 8 workgroups (while both
+// last), so that prefix work, which mostly hits in L2, runs beside suffix work, which streams
+// from HBM. Workgroups go to the 8 XCDs round-robin; prefix units are numbered so that the
+// column tiles of one (group, KV head, chunk), which read the same K/V, land on the same XCD. At
+// most 256 VGPRs, so that two waves share each SIMD (both kinds of work run side by side).
+template <int D, int B, typename OutT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void
 decode_prefix_kernel(
     OutT* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_m,
     float* __restrict__ part_l, int32_t* __restrict__ seg_count,
-    const uint16_t* __restrict__ q, const KvT* __restrict__ kpool,
-    const KvT* __restrict__ vpool, const int32_t* __restrict__ block_table,
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ kpool,
+    const uint8_t* __restrict__ vpool, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ group_start,
     const int32_t* __restrict__ group_prefix_len, int NG, int S, int Hq, int Hkv, int G, int HG,
     int MB, int KSTRIDE, int min_tiles, int Wp, int CT, int NCH, float scale_log2,
@@ -1058,14 +1284,49 @@ decode_prefix_kernel(
   if (is_prefix) {
     const int per_xcd = Wp >> 3;
     const int64_t unit = static_cast<int64_t>(idx & 7) * per_xcd + (idx >> 3);
-    prefix_unit<D, B, OutT, KvT>(unit, out, part_o, part_m, part_l, q, kpool, vpool,
-                                 block_table, context_lens, Hq, Hkv, G, MB, KSTRIDE, CT, NCH,
-                                 scale_log2, out_scale, pf);
+    prefix_unit<D, B, OutT>(unit, out, part_o, part_m, part_l, q, kpool, vpool, block_table,
+                            context_lens, Hq, Hkv, G, MB, KSTRIDE, CT, NCH, scale_log2,
+                            out_scale, pf);
     return;
   }
-  balanced_body<D, B, OutT, KvT, true>(idx, Ws, out, part_o, part_m, part_l, seg_count, q,
+  balanced_body<D, B, OutT, uint8_t, true>(idx, Ws, out, part_o, part_m, part_l, seg_count, q,
                                        kpool, vpool, block_table, context_lens, S, Hq, Hkv, G,
                                        HG, MB, KSTRIDE, min_tiles, scale_log2, out_scale, pf);
+}
+
+// Prefix-aware decode over bf16 pools: WGp workgroups of prefix chunks (prefix_wg), then
+// workgroups of kPrefixWgWaves suffix waves of the balanced split (Ws waves in all). The prefix
+// workgroups come first, so that they are dispatched with the first suffix workgroups and run
+// beside them (the chunks' products on the matrix cores, the suffixes streaming from HBM).
+// Prefix workgroups are numbered so that the column blocks of one (group, KV head, chunk), which
+// read the same K/V, land on the same XCD. The LDS that the prefix chunks take (8 stages)
+// leaves one workgroup per CU.
+template <int D, int B, typename OutT>
+__global__ __launch_bounds__(64 * kPrefixWgWaves) void decode_prefix_wg_kernel(
+    OutT* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_m,
+    float* __restrict__ part_l, int32_t* __restrict__ seg_count,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kpool,
+    const uint16_t* __restrict__ vpool, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ group_start,
+    const int32_t* __restrict__ group_prefix_len, int NG, int S, int Hq, int Hkv, int G, int HG,
+    int MB, int KSTRIDE, int min_tiles, int WGp, int Ws, int CB, int NCH, float scale_log2,
+    float pscale_log2, int neg_scale) {
+  __shared__ __attribute__((aligned(16))) unsigned char
+      smem[kPrefixChunkTiles * prefix_stage_bytes<D>()];
+  const PrefixInfo pf{group_start, group_prefix_len, NG};
+  const int b = blockIdx.x;
+  if (b < WGp) {
+    const int64_t unit = static_cast<int64_t>(b & 7) * (WGp >> 3) + (b >> 3);
+    prefix_wg<D, B, OutT>(unit, smem, out, part_o, part_m, part_l, q, kpool, vpool, block_table,
+                          context_lens, Hq, Hkv, G, MB, KSTRIDE, CB, NCH, pscale_log2, neg_scale,
+                          pf);
+    return;
+  }
+  const int w = (b - WGp) * kPrefixWgWaves + (threadIdx.x >> 6);
+  if (w >= Ws) return;
+  balanced_body<D, B, OutT, uint16_t, true>(w, Ws, out, part_o, part_m, part_l, seg_count, q,
+                                            kpool, vpool, block_table, context_lens, S, Hq, Hkv,
+                                            G, HG, MB, KSTRIDE, min_tiles, scale_log2, 1.0f, pf);
 }
 
 // fp32 path. `rows` are decode sequences (PREFILL = false) or prefill query tokens.
@@ -1393,18 +1654,34 @@ static hipError_t launch_bf16(const DecodeArgs& a, hipStream_t st) {
         a.MB, a.P, a.NP, a.scale * kLog2e);
 }
 
-template <int D, int B, typename OutT, typename KvT>
-static hipError_t launch_prefix_t(const DecodeArgs& a, hipStream_t st) {
+// Prefix-aware decode over bf16 pools. The prefix workgroups take a positive scale (see
+// prefix_wg; zero becomes a tiny one, which gives the uniform softmax of a zero scale).
+template <int D, int B, typename OutT>
+static hipError_t launch_prefix_bf16_t(const DecodeArgs& a, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   const int HG = (G + 15) / 16;
-  const float sl = a.scale * (a.fp8_kv ? a.k_scale : 1.0f) * kLog2e;
-  return launch_kernel(K_DECODE_PARTITION, decode_prefix_kernel<D, B, OutT, KvT>,
+  const float sl = a.scale * kLog2e;
+  const int wgs = (a.waves + kPrefixWgWaves - 1) / kPrefixWgWaves;
+  return launch_kernel(K_DECODE_PARTITION, decode_prefix_wg_kernel<D, B, OutT>,
+      dim3(a.prefix_waves + wgs), dim3(64 * kPrefixWgWaves), st, static_cast<OutT*>(a.out),
+      a.part_o, a.part_m, a.part_l, a.seg_count, static_cast<const uint16_t*>(a.q),
+      static_cast<const uint16_t*>(a.k_pool), static_cast<const uint16_t*>(a.v_pool),
+      a.block_table, a.context_lens, a.group_start, a.group_prefix_len, a.num_groups, a.S, a.Hq,
+      a.Hkv, G, HG, a.MB, a.KMAX, a.min_tiles, a.prefix_waves, a.waves, a.prefix_col_tiles,
+      a.prefix_chunks, sl, fmaxf(fabsf(sl), 1e-30f), a.scale < 0.f ? 1 : 0);
+}
+
+template <int D, int B, typename OutT>
+static hipError_t launch_prefix_fp8_t(const DecodeArgs& a, hipStream_t st) {
+  const int G = a.Hq / a.Hkv;
+  const int HG = (G + 15) / 16;
+  return launch_kernel(K_DECODE_PARTITION, decode_prefix_kernel<D, B, OutT>,
       dim3(a.prefix_waves + a.waves), dim3(64), st, static_cast<OutT*>(a.out), a.part_o,
       a.part_m, a.part_l, a.seg_count, static_cast<const uint16_t*>(a.q),
-      static_cast<const KvT*>(a.k_pool), static_cast<const KvT*>(a.v_pool), a.block_table,
+      static_cast<const uint8_t*>(a.k_pool), static_cast<const uint8_t*>(a.v_pool), a.block_table,
       a.context_lens, a.group_start, a.group_prefix_len, a.num_groups, a.S, a.Hq, a.Hkv, G, HG,
-      a.MB, a.KMAX, a.min_tiles, a.prefix_waves, a.prefix_col_tiles, a.prefix_chunks, sl,
-      a.fp8_kv ? a.v_scale : 1.0f);
+      a.MB, a.KMAX, a.min_tiles, a.prefix_waves, a.prefix_col_tiles, a.prefix_chunks,
+      a.scale * a.k_scale * kLog2e, a.v_scale);
 }
 
 template <int D, int B, typename OutT>
@@ -1436,8 +1713,8 @@ template <int D, int B, typename OutT>
 static hipError_t dispatch_out_t(const DecodeArgs& a, hipStream_t st) {
   if (a.step) return launch_step_t<D, B, OutT>(a, st);
   if (a.num_groups > 0)
-    return a.fp8_kv ? launch_prefix_t<D, B, OutT, uint8_t>(a, st)
-                    : launch_prefix_t<D, B, OutT, uint16_t>(a, st);
+    return a.fp8_kv ? launch_prefix_fp8_t<D, B, OutT>(a, st)
+                    : launch_prefix_bf16_t<D, B, OutT>(a, st);
   if (a.bf16_in || a.fp8_kv) return launch_bf16<D, B, OutT>(a, st);
   return a.NP > 1 ? launch_f32<D, B, true, OutT>(a, st) : launch_f32<D, B, false, OutT>(a, st);
 }

@@ -110,8 +110,9 @@ struct DecodeArgs {
   float v_scale;
   // Shared prefixes (num_groups > 0; balanced): group i is sequences group_start[i] ..
   // group_start[i+1]-1 sharing their first group_prefix_len[i] tokens. prefix_waves units of
-  // (group, KV head, chunk, 16-column tile) run before the `waves` suffix waves; KMAX is then
-  // the row stride of the partials (prefix chunks first).
+  // (group, KV head, chunk, block of query columns; prefix_col_tiles blocks per chunk) run beside
+  // the `waves` suffix waves: workgroups of kPrefixWgWaves waves over bf16 pools, single waves
+  // over E4M3 pools. KMAX is then the row stride of the partials (prefix chunks first).
   int num_groups;
   const int32_t* group_start;
   const int32_t* group_prefix_len;
@@ -125,7 +126,11 @@ struct DecodeArgs {
   const void* v_new;
   const int32_t* slot_mapping;
 };
-constexpr int kPrefixChunkTokens = 256;  // tokens of the shared prefix per prefix unit
+constexpr int kPrefixChunkTokens = 256;  // tokens of the shared prefix per prefix chunk
+// Prefix-aware decode over bf16 pools: waves per workgroup, and the (member, query head) columns
+// one prefix workgroup computes (32 per wave).
+constexpr int kPrefixWgWaves = 8;
+constexpr int kPrefixWgColumns = 32 * kPrefixWgWaves;
 // Waves per workgroup of the balanced split's kernels; a launch of W waves runs
 // kBalancedWavesPerGroup * ceil(W / kBalancedWavesPerGroup) of them.
 constexpr int kBalancedWavesPerGroup = 4;

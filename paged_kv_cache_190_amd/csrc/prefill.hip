@@ -29,6 +29,7 @@
 // fp32 prefill runs on the vector kernel in decode.hip.
 #include "common.hpp"
 #include "launch.hpp"
+#include "lds_tile.hpp"
 
 namespace pkv {
 
@@ -39,23 +40,6 @@ constexpr float kLog2eP = 1.4426950408889634f;
 __device__ __forceinline__ u32x4 lds16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
-
-// s_waitcnt immediate that waits until at most n vector-memory operations are outstanding and
-// leaves the other counters alone (gfx9 encoding: vmcnt split over bits 3:0 and 15:14).
-constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
-
-// XOR swizzles of the 16-byte chunks of the LDS tiles. The DMA writes each wave's 64 lanes to
-// 1 KiB of consecutive LDS, so rows cannot be padded; instead a row's chunks are permuted so
-// that the sixteen lanes a 128-bit LDS read serves together (64 banks x 4 bytes) hit sixteen
-// different 16-byte bank groups. K rows are read in the order krow(col) below, i.e. rows
-// {0..3, 16..19, 4..7, 20..23} for lanes 0..15 and {8..11, 24..27, 12..15, 28..31} for lanes
-// 16..31; V rows d in order.
-template <int D>
-__device__ __forceinline__ int kswz(int row) {
-  if constexpr (D == 128) return (row & 7) | ((row >> 1) & 8);       // 16 chunks per row
-  else return ((row >> 1) & 3) | ((row >> 2) & 4);                   // 8 chunks, 2 rows per line
-}
-__device__ __forceinline__ int vswz(int d) { return (d >> 2) & 3; }  // 4 chunks, 4 rows per line
 
 constexpr int kPrefillWaves = 8;  // waves per workgroup
 constexpr int kStages = 8;        // K/V tiles in the LDS ring

@@ -23,13 +23,15 @@ def test_sources_per_workload():
     assert bench.kernel_sources("block-copy")[0] == "blocks.hip"
     for w in ("decode-8b", "prefill-chunk", "block-copy"):
         assert "api.cpp" in bench.kernel_sources(w)
+    assert "lds_tile.hpp" in bench.kernel_sources("prefill-chunk")
+    assert "lds_tile.hpp" in bench.kernel_sources("decode-8b")
     assert bench.kernel_sources_sha("decode-8b") != bench.kernel_sources_sha("prefill-chunk")
 
 
 def test_hash_ignores_comments_and_whitespace(tmp_path, monkeypatch):
     csrc = tmp_path / "paged_kv_cache_190_amd" / "csrc"
     csrc.mkdir(parents=True)
-    for f in ("decode.hip", "common.hpp", "launch.hpp", "api.cpp"):
+    for f in ("decode.hip", "common.hpp", "lds_tile.hpp", "launch.hpp", "api.cpp"):
         (csrc / f).write_text("int f(int x) { return x + 1; }\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     h0 = bench.kernel_sources_sha("decode-8b")
@@ -44,7 +46,7 @@ def test_traffic_counts_only_on_matching_sources(tmp_path, monkeypatch):
     csrc.mkdir(parents=True)
     prof = tmp_path / "profiles"
     prof.mkdir()
-    for f in ("decode.hip", "common.hpp", "launch.hpp", "api.cpp"):
+    for f in ("decode.hip", "common.hpp", "lds_tile.hpp", "launch.hpp", "api.cpp"):
         (csrc / f).write_text("int f(int x) { return x; }\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     sha = bench.kernel_sources_sha("decode-8b")

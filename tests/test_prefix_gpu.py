@@ -63,6 +63,8 @@ GROUPED = [
      ""),
     ("g20", 303, [(48, [50, 300, 49]), (272, [272, 600])], 40, 2, 64, 16, ""),
     ("g8_b32", 304, [(1024, [1030, 1500, 1024, 2000])], 64, 8, 128, 32, ""),
+    # 80 members x 4 query heads = 320 columns: more than one prefix workgroup's 256 columns
+    ("wide_group", 306, [(320, [330] * 40 + [321] * 40), (16, [20, 40])], 32, 8, 128, 16, ""),
     ("mixed_fp8", 305, [(64, [64, 100, 200]), (0, [5]), (512, [512, 700]), (256, [300] * 9)],
      32, 8, 128, 16, "fp8"),
 ]
@@ -109,3 +111,14 @@ def test_shared_prefix_config4(kv_dtype):
     ref = _oracle(w)
     got = _run(w, [0, w.num_seqs], [w.prefix_tokens], "f32")
     assert_close(got, ref, TOL_BF16, f"config 4 shared prefix {kv_dtype or 'bf16'}")
+
+
+@pytest.mark.parametrize("name", ["mixed", "b32_d64_g1"])
+def test_shared_prefix_negative_scale(name):
+    """A negative softmax scale: the prefix chunks take it as |scale| on -q."""
+    import dataclasses
+    w0, _ = _grouped(name)
+    w = dataclasses.replace(w0, scale=-w0.scale)
+    log(f"shared-prefix decode {name} scale={w.scale}")
+    got = _run(w, w.meta["group_start"], w.meta["group_prefix_len"], "f32")
+    assert_close(got, _oracle(w), TOL_BF16, f"shared prefix {name} negative scale")
