@@ -113,12 +113,14 @@ def test_shared_prefix_config4(kv_dtype):
     assert_close(got, ref, TOL_BF16, f"config 4 shared prefix {kv_dtype or 'bf16'}")
 
 
-@pytest.mark.parametrize("name", ["mixed", "b32_d64_g1"])
-def test_shared_prefix_negative_scale(name):
-    """A negative softmax scale: the prefix chunks take it as |scale| on -q."""
+@pytest.mark.parametrize("name,scale", [("mixed", -0.3), ("mixed", 0.0), ("mixed", 1.7),
+                                        ("b32_d64_g1", -0.125), ("wide_group", 0.0)])
+def test_shared_prefix_scale_variants(name, scale):
+    """Any finite scale: negative (the prefix chunks take it as |scale| on -q), zero (uniform
+    weights over each context) and a large one."""
     import dataclasses
     w0, _ = _grouped(name)
-    w = dataclasses.replace(w0, scale=-w0.scale)
+    w = dataclasses.replace(w0, scale=scale)
     log(f"shared-prefix decode {name} scale={w.scale}")
     got = _run(w, w.meta["group_start"], w.meta["group_prefix_len"], "f32")
-    assert_close(got, _oracle(w), TOL_BF16, f"shared prefix {name} negative scale")
+    assert_close(got, _oracle(w), TOL_BF16, f"shared prefix {name} scale={scale}")
