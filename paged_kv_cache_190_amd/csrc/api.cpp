@@ -440,6 +440,27 @@ pkv_status setup_balanced(pkv::DecodeArgs& a, void* workspace, size_t workspace_
   return PKV_OK;
 }
 
+// Compute units of the current device, read once per device.
+hipError_t device_cu_count(int* cus) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static int per_device[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (per_device[dev] <= 0) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (n <= 0) return hipErrorInvalidDevice;
+    per_device[dev] = n;
+  }
+  *cus = per_device[dev];
+  return hipSuccess;
+}
+
 // Partial slots per row taken by the prefix chunks.
 int prefix_chunks(int max_prefix_len) {
   return (max_prefix_len + pkv::kPrefixChunkTokens - 1) / pkv::kPrefixChunkTokens;
@@ -555,11 +576,8 @@ pkv_status pkv_paged_attention_decode_shared_prefix(void* out, const void* q, co
     // suffix waves fill the CUs that the prefix workgroups leave, all resident from the start
     // (more waves, dispatched as CUs free up, measured 31 against 24 us on the shared-prefix
     // batch).
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      return fail(PKV_ERR_HIP, "cannot read the device's compute unit count");
+    int cus = 0;
+    if (pkv_status hs = hip_status(device_cu_count(&cus), "compute unit count")) return hs;
     const long long free_cus = std::max<long long>(cus - waves_p, cus / 4);
     st = setup_balanced(a, workspace, workspace_bytes,
                         static_cast<int>(std::min<long long>(free_cus * pkv::kPrefixWgWaves,
