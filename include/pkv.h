@@ -347,13 +347,12 @@ pkv_status pkv_paged_attention_decode_fp8(void* out, const void* q, const void* 
  *                     ignored for bf16); q is bf16; out_dtype PKV_BF16 or PKV_F32
  *   workspace         pkv_decode_shared_prefix_workspace_size(...) bytes
  * Other arguments as for pkv_paged_attention_decode (num_waves: waves of the balanced split of
- * the private suffixes, 0 = the default: over bf16 pools, as many as fill the compute units
- * that the prefix workgroups leave, eight per unit; over E4M3 pools 1024; fewer are used when
- * the suffixes have under 3 (bf16) or 4 (E4M3) tiles of 32 tokens per wave). Each shared
- * prefix is split into chunks of 256 tokens. Over bf16 pools one workgroup of eight waves
- * stages a chunk's K/V in LDS and attends it for up to 256 (member, query head) rows; over E4M3
- * pools one wave attends a chunk for 16 such rows. The private rest of every context goes
- * through the balanced split, and a reduce kernel merges the pieces by log-sum-exp.
+ * the private suffixes, 0 = the default: as many as fill the compute units that the prefix
+ * workgroups leave, eight per unit; fewer are used when the suffixes have under 3 (bf16) or 4
+ * (E4M3) tiles of 32 tokens per wave). Each shared prefix is split into chunks of 256 tokens;
+ * one workgroup of eight waves stages a chunk's K/V in LDS as bf16 (E4M3 codes widened exactly)
+ * and attends it for up to 256 (member, query head) rows. The private rest of every context
+ * goes through the balanced split, and a reduce kernel merges the pieces by log-sum-exp.
  */
 size_t pkv_decode_shared_prefix_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
                                                int head_dim, int max_context_len,

@@ -559,39 +559,37 @@ pkv_status pkv_paged_attention_decode_shared_prefix(void* out, const void* q, co
                 max_prefix_len);
   const int G = num_q_heads / num_kv_heads;
   const int nch = prefix_chunks(max_prefix_len);
-  // column units: 16 (sequence, query head) columns each over E4M3 pools (one wave); over bf16
-  // pools a workgroup of kPrefixWgWaves waves takes kPrefixWgColumns
-  const int cols_per_unit = kv_dtype == PKV_FP8_E4M3 ? 16 : pkv::kPrefixWgColumns;
-  const long long col_tiles =
+  // column units: a workgroup of kPrefixWgWaves waves takes kPrefixWgColumns (sequence, query
+  // head) columns of a chunk
+  const int cols_per_unit = pkv::kPrefixWgColumns;
+  const long long col_blocks =
       (static_cast<long long>(max_group_size) * G + cols_per_unit - 1) / cols_per_unit;
-  const long long units = static_cast<long long>(num_groups) * num_kv_heads * nch * col_tiles;
-  const long long waves_p = (units + 7) / 8 * 8;  // prefix waves (E4M3) or workgroups (bf16)
+  const long long units = static_cast<long long>(num_groups) * num_kv_heads * nch * col_blocks;
+  const long long units_p = (units + 7) / 8 * 8;  // prefix workgroups, a multiple of 8
   const int min_tiles = prefix_min_tiles(kv_dtype);
-  st = setup_balanced(a, workspace, workspace_bytes,
-                      kv_dtype == PKV_FP8_E4M3 ? kDefaultDecodeWavesFp8 : kDefaultDecodeWaves,
-                      num_waves, nch, min_tiles);
+  st = setup_balanced(a, workspace, workspace_bytes, kDefaultDecodeWaves, num_waves, nch,
+                      min_tiles);
   if (st != PKV_OK) return st;
-  if (kv_dtype != PKV_FP8_E4M3 && num_waves == 0) {
-    // Over bf16 pools every workgroup takes one CU (the prefix chunks' LDS): by default the
-    // suffix waves fill the CUs that the prefix workgroups leave, all resident from the start
-    // (more waves, dispatched as CUs free up, measured 31 against 24 us on the shared-prefix
-    // batch).
+  if (num_waves == 0) {
+    // Every workgroup takes one CU (the prefix chunks' LDS): by default the suffix waves fill
+    // the CUs that the prefix workgroups leave, all resident from the start (more waves,
+    // dispatched as CUs free up, measured 31 against 24 us on the shared-prefix batch).
     int cus = 0;
     if (pkv_status hs = hip_status(device_cu_count(&cus), "compute unit count")) return hs;
-    const long long free_cus = std::max<long long>(cus - waves_p, cus / 4);
+    const long long free_cus = std::max<long long>(cus - units_p, cus / 4);
     st = setup_balanced(a, workspace, workspace_bytes,
                         static_cast<int>(std::min<long long>(free_cus * pkv::kPrefixWgWaves,
                                                              kMaxDecodeWaves)),
                         0, nch, min_tiles);
     if (st != PKV_OK) return st;
   }
-  if (waves_p + a.waves > 0x7fffffffLL)
+  if (units_p + a.waves > 0x7fffffffLL)
     return fail(PKV_ERR_UNSUPPORTED, "too many prefix units (%lld)", units);
   a.num_groups = num_groups;
   a.group_start = group_start;
   a.group_prefix_len = group_prefix_len;
-  a.prefix_waves = static_cast<int>(waves_p);
-  a.prefix_col_tiles = static_cast<int>(col_tiles);
+  a.prefix_units = static_cast<int>(units_p);
+  a.prefix_col_blocks = static_cast<int>(col_blocks);
   a.prefix_chunks = nch;
   a.fp8_kv = kv_dtype == PKV_FP8_E4M3;
   a.k_scale = a.fp8_kv ? k_scale : 1.0f;

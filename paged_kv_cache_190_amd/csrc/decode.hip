@@ -658,13 +658,12 @@ __device__ __forceinline__ int wave_incl_scan_i(int v) {
 // Shared prefixes (the prefix-aware decode): sequences come in groups of consecutive ones,
 // group i being sequences group_start[i] .. group_start[i+1]-1, whose first group_prefix_len[i]
 // tokens (a multiple of B) are the same physical blocks. Such a prefix is attended once per
-// group, in units of (group, KV head, chunk of kPrefixChunk prefix tokens, block of query
-// columns), the columns being (member sequence, query head) pairs: a chunk's K/V is then shared
-// by every member's query heads instead of one sequence's G heads. Over bf16 pools a unit is a
-// workgroup of kPrefixWgWaves waves and kPrefixWgColumns columns (prefix_wg); over E4M3 pools it
-// is one wave and 16 columns (prefix_unit). The private rest of each context goes through the
-// balanced split as usual. A row's partials: the prefix chunks at slots 0 .. pc-1
-// (pc = ceil(prefix / kPrefixChunk)), then its suffix pieces.
+// group, in units of (group, KV head, chunk of kPrefixChunk prefix tokens, block of
+// kPrefixWgColumns query columns), the columns being (member sequence, query head) pairs: a
+// chunk's K/V is then read once for every member's query heads instead of once per sequence.
+// A unit is a workgroup of kPrefixWgWaves waves (prefix_wg). The private rest of each context
+// goes through the balanced split as usual. A row's partials: the prefix chunks at slots
+// 0 .. pc-1 (pc = ceil(prefix / kPrefixChunk)), then its suffix pieces.
 constexpr int kPrefixChunk = kPrefixChunkTokens;
 
 struct PrefixInfo {
@@ -931,59 +930,12 @@ __global__ __launch_bounds__(64 * kBalancedWavesPerGroup) void decode_read_probe
       PrefixInfo{nullptr, nullptr, 0}, StepInfo{}, sink);
 }
 
-// One prefix unit over E4M3 pools (see PrefixInfo): one wave for (group, KV head, chunk, 16
-// query columns). Units are numbered (group, KV head, chunk, column tile), column tile fastest;
-// `unit` is that number.
-template <int D, int B, typename OutT>
-__device__ __forceinline__ void prefix_unit(
-    int64_t unit, OutT* __restrict__ out, float* __restrict__ part_o,
-    float* __restrict__ part_m, float* __restrict__ part_l, const uint16_t* __restrict__ q,
-    const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool,
-    const int32_t* __restrict__ block_table, const int32_t* __restrict__ context_lens, int Hq,
-    int Hkv, int G, int MB, int KSTRIDE, int CT, int NCH, float scale_log2, float out_scale,
-    PrefixInfo pf) {
-  const int lane = threadIdx.x;
-  const int lg = lane >> 4;
-  const int ct = static_cast<int>(unit % CT);
-  int64_t r = unit / CT;
-  const int ch = static_cast<int>(r % NCH);
-  r /= NCH;
-  const int g = static_cast<int>(r % Hkv);
-  const int gi = static_cast<int>(r / Hkv);
-  if (gi >= pf.NG) return;
-  const int s0 = pf.group_start[gi];
-  const int members = pf.group_start[gi + 1] - s0;
-  const int pre = pf.group_prefix_len[gi];
-  const int tok0 = ch * kPrefixChunk;
-  if (tok0 >= pre || ct * 16 >= members * G) return;
-  const int32_t* bt = block_table + static_cast<int64_t>(s0) * MB;  // the shared blocks
-  const int te = min(pre, tok0 + kPrefixChunk);
-  const int pc = (pre + kPrefixChunk - 1) / kPrefixChunk;
-  const int c = ct * 16 + (lane & 15);
-  const bool valid = c < members * G;
-  const int m = valid ? c / G : 0;
-  const int seq = s0 + m;
-  const int64_t row = static_cast<int64_t>(seq) * Hq + g * G + (valid ? c - m * G : 0);
-  u32x4 qf[D / 32];
-  WaveAttn<D> st;
-  attn_init(st);
-  load_q_fp8<D>(qf, q + row * D, valid, lg);
-  attend_tiles_fp8<D, B, 2, false>(st, qf, kpool, vpool, bt, pre, g, Hkv, tok0, te, scale_log2);
-  // Each lane's column is its own row: reduce l over the 4 row groups only (lanes ^16, ^32).
-  const float l_total = xor32_sum(xor16_sum(st.l));
-  if (!valid) return;
-  if (pc == 1 && context_lens[seq] == pre)
-    write_final<D>(out + row * D, st, l_total, lg, out_scale);
-  else
-    write_partial<D>(part_o, part_m, part_l, row * KSTRIDE + ch, st, l_total, lg, out_scale);
-}
-
-// Prefix chunks over bf16 pools, one workgroup of kPrefixWgWaves waves per (group, KV head,
-// chunk, block of 32 * kPrefixWgWaves query columns): the columns are (member sequence, query
-// head) pairs, 32 per wave. The chunk's K/V tiles (kPrefixChunk tokens of the shared blocks) are
-// copied into LDS once, all of them at the start (global_load_lds; no LDS stage is reused), and
-// every wave computes its columns against each tile as the chunked prefill does against its
-// rows, without a causal mask (every member's query follows the whole prefix):
+// Prefix chunks, one workgroup of kPrefixWgWaves waves per (group, KV head, chunk, block of
+// 32 * kPrefixWgWaves query columns): the columns are (member sequence, query head) pairs, 32
+// per wave. The chunk's K/V tiles (kPrefixChunk tokens of the shared blocks) are staged in LDS
+// as bf16 once, all of them at the start (no LDS stage is reused), and every wave computes its
+// columns against each tile as the chunked prefill does against its rows, without a causal
+// mask (every member's query follows the whole prefix):
 //   S^T[32 keys][32 columns] = K_tile . Q^T,  online softmax per column,
 //   O^T[D][32 columns] += V_tile^T . P^T      (32x32x16 MFMAs)
 // Each column leaves one partial (m, l, O / l) at its row's slot for the chunk, or its final
@@ -1005,14 +957,15 @@ constexpr int kPrefixChunkTiles = kPrefixChunk / 32;
 template <int D>
 constexpr int prefix_stage_bytes() { return 32 * 2 * D + D * 64; }  // K tile + V tile
 
-template <int D, int B, typename OutT>
+template <int D, int B, typename OutT, typename KvT>
 __device__ __forceinline__ void prefix_wg(
     int64_t unit, unsigned char* __restrict__ smem, OutT* __restrict__ out,
     float* __restrict__ part_o, float* __restrict__ part_m, float* __restrict__ part_l,
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kpool,
-    const uint16_t* __restrict__ vpool, const int32_t* __restrict__ block_table,
+    const uint16_t* __restrict__ q, const KvT* __restrict__ kpool,
+    const KvT* __restrict__ vpool, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ context_lens, int Hq, int Hkv, int G, int MB, int KSTRIDE, int CB,
-    int NCH, float scale_log2, int neg_scale, PrefixInfo pf) {
+    int NCH, float scale_log2, int neg_scale, float out_scale, PrefixInfo pf) {
+  constexpr bool kFp8 = sizeof(KvT) == 1;
   constexpr int KK = D / 16;              // QK MFMA steps
   constexpr int DT = D / 32;              // PV output tiles
   constexpr int NW = kPrefixWgWaves;
@@ -1064,12 +1017,15 @@ __device__ __forceinline__ void prefix_wg(
     for (int kk = 0; kk < KK; ++kk) qf[kk] = load16(qrow + 16 * kk);
   }
 
-  // DMA: instruction j of wave w fills KiB (LPT * w + j) of a stage. K instructions cover
-  // 64 / CPR key rows each, V instructions 16 dims x 32 keys; a lane's offset inside its block
-  // is the same for every tile, so its source is a fixed address inside block 0 of the pool
-  // plus the tile's block id times the block's bytes.
-  const uint16_t* kg = kpool + static_cast<int64_t>(g) * B * D;
-  const uint16_t* vg = vpool + static_cast<int64_t>(g) * B * D;
+  // Staging: piece j of wave w fills KiB (LPT * w + j) of a stage, 16 bytes (8 bf16 values)
+  // per lane. K pieces cover 64 / CPR key rows each, V pieces 16 dims x 32 keys; a lane's offset
+  // inside its block is the same for every tile, so its source is a fixed address inside block
+  // 0 of the pool plus the tile's block id times the block's bytes. bf16 pools: each piece is
+  // one DMA (global_load_lds). E4M3 pools: each lane loads its 8 codes (8 bytes) into registers,
+  // widens them to bf16 exactly and writes the 16 bytes to the same LDS place, so the tiles in
+  // LDS, and everything that reads them, are the same for both pool types.
+  const KvT* kg = kpool + static_cast<int64_t>(g) * B * D;
+  const KvT* vg = vpool + static_cast<int64_t>(g) * B * D;
   const char* lsrc[LPT];
   bool ssel[LPT];
 #pragma unroll
@@ -1087,7 +1043,7 @@ __device__ __forceinline__ void prefix_wg(
       ssel[j] = B == 16 && chunk >= 2;
     }
   }
-  const uint32_t blk_bytes = 2u * static_cast<uint32_t>(Hkv) * B * D;  // < 2^32
+  const uint32_t blk_bytes = static_cast<uint32_t>(sizeof(KvT) * Hkv * B * D);  // < 2^32
   // Every stage is filled, also past the chunk's last tile (those repeat the prefix's last
   // blocks and are never computed), so that the count of DMAs, and each wait below, is fixed.
   // The chunk's block ids first (uniform indexes: scalar loads, which do not count in vmcnt),
@@ -1098,14 +1054,15 @@ __device__ __forceinline__ void prefix_wg(
   for (int i = 0; i < NID; ++i)
     ids[i] = static_cast<uint32_t>(
         bt[__builtin_amdgcn_readfirstlane(min(tok0 / B + i, pblk - 1))]);
-  // q has arrived before the DMAs start counting in the same counter (its loads overlap the
-  // block ids' loads); the tile waits below then count DMAs only.
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  // bf16: q has arrived before the DMAs start counting in the same counter (its loads overlap
+  // the block ids' loads); the tile waits below then count DMAs only.
+  if constexpr (!kFp8) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   {
     const uint32_t flip = neg_scale ? 0x80008000u : 0u;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) qf[kk] ^= flip;
   }
+  [[maybe_unused]] u32x2 raw[kFp8 ? NCT : 1][LPT];  // E4M3 codes of every piece of the chunk
 #pragma unroll
   for (int t = 0; t < NCT; ++t) {
     const uint32_t ida = ids[t * 32 / B];
@@ -1114,7 +1071,11 @@ __device__ __forceinline__ void prefix_wg(
     for (int j = 0; j < LPT; ++j) {
       const uint32_t bid = (B == 16 && ssel[j]) ? idb : ida;
       const char* src = lsrc[j] + static_cast<uint64_t>(bid) * blk_bytes;
-      __builtin_amdgcn_global_load_lds(src, smem + t * STAGE + (LPT * wave + j) * 1024, 16, 0, 0);
+      if constexpr (kFp8)
+        raw[t][j] = load8(src);
+      else
+        __builtin_amdgcn_global_load_lds(src, smem + t * STAGE + (LPT * wave + j) * 1024, 16, 0,
+                                         0);
     }
   }
 
@@ -1213,7 +1174,17 @@ __device__ __forceinline__ void prefix_wg(
   // were issued first); the barrier then covers every wave's.
   static_for<NCT>([&](auto tc) {
     constexpr int t = decltype(tc)::value;
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NCT - 1 - t) * LPT));
+    if constexpr (kFp8) {
+      // (the compiler waits for exactly this tile's codes; the LDS writes are waited for
+      // before the barrier that publishes them)
+#pragma unroll
+      for (int j = 0; j < LPT; ++j)
+        *reinterpret_cast<u32x4*>(smem + t * STAGE + (LPT * wave + j) * 1024 + 16 * lane) =
+            e4m3x8_to_bf16x8(raw[t][j][0], raw[t][j][1]);
+      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm((NCT - 1 - t) * LPT));
+    }
     __builtin_amdgcn_s_barrier();
     if (t < ntiles && wave_active) compute(t);
   });
@@ -1223,7 +1194,7 @@ __device__ __forceinline__ void prefix_wg(
   if (!valid) return;
   const int pc = (pre + kPrefixChunk - 1) / kPrefixChunk;
   const int seq = s0 + mi;
-  const float inv = 1.0f / lsum;
+  const float inv = out_scale / lsum;  // (E4M3 pools: the V scale is folded in here)
   if (pc == 1 && context_lens[seq] == pre) {
     OutT* o = out + row * D + 4 * hb;
 #pragma unroll
@@ -1248,85 +1219,39 @@ __device__ __forceinline__ void prefix_wg(
           inv;
 }
 
-// Prefix-aware decode over E4M3 pools: Wp prefix-unit waves and Ws = gridDim.x - Wp waves of the
-// balanced split of the suffixes. The two kinds alternate in runs of 8 workgroups (while both
-// last), so that prefix work, which mostly hits in L2, runs beside suffix work, which streams
-// from HBM. Workgroups go to the 8 XCDs round-robin; prefix units are numbered so that the
-// column tiles of one (group, KV head, chunk), which read the same K/V, land on the same XCD. At
-// most 256 VGPRs, so that two waves share each SIMD (both kinds of work run side by side).
-template <int D, int B, typename OutT>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void
-decode_prefix_kernel(
-    OutT* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_m,
-    float* __restrict__ part_l, int32_t* __restrict__ seg_count,
-    const uint16_t* __restrict__ q, const uint8_t* __restrict__ kpool,
-    const uint8_t* __restrict__ vpool, const int32_t* __restrict__ block_table,
-    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ group_start,
-    const int32_t* __restrict__ group_prefix_len, int NG, int S, int Hq, int Hkv, int G, int HG,
-    int MB, int KSTRIDE, int min_tiles, int Wp, int CT, int NCH, float scale_log2,
-    float out_scale) {
-  const PrefixInfo pf{group_start, group_prefix_len, NG};
-  const int b = blockIdx.x;
-  const int Ws = gridDim.x - Wp;
-  const int m = min(Wp, Ws & ~7);  // Wp is a multiple of 8
-  bool is_prefix;
-  int idx;
-  if (b < 2 * m) {  // alternating runs of 8; idx keeps b's XCD (idx % 8 == b % 8)
-    is_prefix = ((b >> 3) & 1) == 0;
-    idx = 8 * (b >> 4) + (b & 7);
-  } else if (b < m + Wp) {
-    is_prefix = true;
-    idx = b - m;
-  } else {
-    is_prefix = false;
-    idx = b - Wp;
-  }
-  if (is_prefix) {
-    const int per_xcd = Wp >> 3;
-    const int64_t unit = static_cast<int64_t>(idx & 7) * per_xcd + (idx >> 3);
-    prefix_unit<D, B, OutT>(unit, out, part_o, part_m, part_l, q, kpool, vpool, block_table,
-                            context_lens, Hq, Hkv, G, MB, KSTRIDE, CT, NCH, scale_log2,
-                            out_scale, pf);
-    return;
-  }
-  balanced_body<D, B, OutT, uint8_t, true>(idx, Ws, out, part_o, part_m, part_l, seg_count, q,
-                                       kpool, vpool, block_table, context_lens, S, Hq, Hkv, G,
-                                       HG, MB, KSTRIDE, min_tiles, scale_log2, out_scale, pf);
-}
-
-// Prefix-aware decode over bf16 pools: WGp workgroups of prefix chunks (prefix_wg), then
-// workgroups of kPrefixWgWaves suffix waves of the balanced split (Ws waves in all). The prefix
-// workgroups come first, so that they are dispatched with the first suffix workgroups and run
-// beside them (the chunks' products on the matrix cores, the suffixes streaming from HBM).
-// Prefix workgroups are numbered so that the column blocks of one (group, KV head, chunk), which
-// read the same K/V, land on the same XCD. The LDS that the prefix chunks take (8 stages)
-// leaves one workgroup per CU.
-template <int D, int B, typename OutT>
+// Prefix-aware decode: WGp workgroups of prefix chunks (prefix_wg), then workgroups of
+// kPrefixWgWaves suffix waves of the balanced split (Ws waves in all). The prefix workgroups come
+// first, so that they are dispatched with the first suffix workgroups and run beside them (the
+// chunks' products on the matrix cores, the suffixes streaming from HBM). Prefix workgroups are
+// numbered so that the column blocks of one (group, KV head, chunk), which read the same K/V,
+// land on the same XCD. The LDS that the prefix chunks take (8 stages) leaves one workgroup per
+// CU. KvT: uint16_t for bf16 pools, uint8_t for E4M3 pools (out_scale = the V scale).
+template <int D, int B, typename OutT, typename KvT>
 __global__ __launch_bounds__(64 * kPrefixWgWaves) void decode_prefix_wg_kernel(
     OutT* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_m,
     float* __restrict__ part_l, int32_t* __restrict__ seg_count,
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kpool,
-    const uint16_t* __restrict__ vpool, const int32_t* __restrict__ block_table,
+    const uint16_t* __restrict__ q, const KvT* __restrict__ kpool,
+    const KvT* __restrict__ vpool, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ group_start,
     const int32_t* __restrict__ group_prefix_len, int NG, int S, int Hq, int Hkv, int G, int HG,
     int MB, int KSTRIDE, int min_tiles, int WGp, int Ws, int CB, int NCH, float scale_log2,
-    float pscale_log2, int neg_scale) {
+    float pscale_log2, int neg_scale, float out_scale) {
   __shared__ __attribute__((aligned(16))) unsigned char
       smem[kPrefixChunkTiles * prefix_stage_bytes<D>()];
   const PrefixInfo pf{group_start, group_prefix_len, NG};
   const int b = blockIdx.x;
   if (b < WGp) {
     const int64_t unit = static_cast<int64_t>(b & 7) * (WGp >> 3) + (b >> 3);
-    prefix_wg<D, B, OutT>(unit, smem, out, part_o, part_m, part_l, q, kpool, vpool, block_table,
-                          context_lens, Hq, Hkv, G, MB, KSTRIDE, CB, NCH, pscale_log2, neg_scale,
-                          pf);
+    prefix_wg<D, B, OutT, KvT>(unit, smem, out, part_o, part_m, part_l, q, kpool, vpool,
+                               block_table, context_lens, Hq, Hkv, G, MB, KSTRIDE, CB, NCH,
+                               pscale_log2, neg_scale, out_scale, pf);
     return;
   }
   const int w = (b - WGp) * kPrefixWgWaves + (threadIdx.x >> 6);
   if (w >= Ws) return;
-  balanced_body<D, B, OutT, uint16_t, true>(w, Ws, out, part_o, part_m, part_l, seg_count, q,
-                                            kpool, vpool, block_table, context_lens, S, Hq, Hkv,
-                                            G, HG, MB, KSTRIDE, min_tiles, scale_log2, 1.0f, pf);
+  balanced_body<D, B, OutT, KvT, true>(w, Ws, out, part_o, part_m, part_l, seg_count, q, kpool,
+                                       vpool, block_table, context_lens, S, Hq, Hkv, G, HG, MB,
+                                       KSTRIDE, min_tiles, scale_log2, out_scale, pf);
 }
 
 // fp32 path. `rows` are decode sequences (PREFILL = false) or prefill query tokens.
@@ -1654,34 +1579,22 @@ static hipError_t launch_bf16(const DecodeArgs& a, hipStream_t st) {
         a.MB, a.P, a.NP, a.scale * kLog2e);
 }
 
-// Prefix-aware decode over bf16 pools. The prefix workgroups take a positive scale (see
-// prefix_wg; zero becomes a tiny one, which gives the uniform softmax of a zero scale).
-template <int D, int B, typename OutT>
-static hipError_t launch_prefix_bf16_t(const DecodeArgs& a, hipStream_t st) {
+// Prefix-aware decode. The prefix workgroups take a positive scale (see prefix_wg; zero becomes
+// a tiny one, which gives the uniform softmax of a zero scale).
+template <int D, int B, typename OutT, typename KvT>
+static hipError_t launch_prefix_wg_t(const DecodeArgs& a, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   const int HG = (G + 15) / 16;
-  const float sl = a.scale * kLog2e;
+  const float sl = a.scale * (a.fp8_kv ? a.k_scale : 1.0f) * kLog2e;
   const int wgs = (a.waves + kPrefixWgWaves - 1) / kPrefixWgWaves;
-  return launch_kernel(K_DECODE_PARTITION, decode_prefix_wg_kernel<D, B, OutT>,
-      dim3(a.prefix_waves + wgs), dim3(64 * kPrefixWgWaves), st, static_cast<OutT*>(a.out),
+  return launch_kernel(K_DECODE_PARTITION, decode_prefix_wg_kernel<D, B, OutT, KvT>,
+      dim3(a.prefix_units + wgs), dim3(64 * kPrefixWgWaves), st, static_cast<OutT*>(a.out),
       a.part_o, a.part_m, a.part_l, a.seg_count, static_cast<const uint16_t*>(a.q),
-      static_cast<const uint16_t*>(a.k_pool), static_cast<const uint16_t*>(a.v_pool),
-      a.block_table, a.context_lens, a.group_start, a.group_prefix_len, a.num_groups, a.S, a.Hq,
-      a.Hkv, G, HG, a.MB, a.KMAX, a.min_tiles, a.prefix_waves, a.waves, a.prefix_col_tiles,
-      a.prefix_chunks, sl, fmaxf(fabsf(sl), 1e-30f), a.scale < 0.f ? 1 : 0);
-}
-
-template <int D, int B, typename OutT>
-static hipError_t launch_prefix_fp8_t(const DecodeArgs& a, hipStream_t st) {
-  const int G = a.Hq / a.Hkv;
-  const int HG = (G + 15) / 16;
-  return launch_kernel(K_DECODE_PARTITION, decode_prefix_kernel<D, B, OutT>,
-      dim3(a.prefix_waves + a.waves), dim3(64), st, static_cast<OutT*>(a.out), a.part_o,
-      a.part_m, a.part_l, a.seg_count, static_cast<const uint16_t*>(a.q),
-      static_cast<const uint8_t*>(a.k_pool), static_cast<const uint8_t*>(a.v_pool), a.block_table,
+      static_cast<const KvT*>(a.k_pool), static_cast<const KvT*>(a.v_pool), a.block_table,
       a.context_lens, a.group_start, a.group_prefix_len, a.num_groups, a.S, a.Hq, a.Hkv, G, HG,
-      a.MB, a.KMAX, a.min_tiles, a.prefix_waves, a.prefix_col_tiles, a.prefix_chunks,
-      a.scale * a.k_scale * kLog2e, a.v_scale);
+      a.MB, a.KMAX, a.min_tiles, a.prefix_units, a.waves, a.prefix_col_blocks,
+      a.prefix_chunks, sl, fmaxf(fabsf(sl), 1e-30f), a.scale < 0.f ? 1 : 0,
+      a.fp8_kv ? a.v_scale : 1.0f);
 }
 
 template <int D, int B, typename OutT>
@@ -1713,8 +1626,8 @@ template <int D, int B, typename OutT>
 static hipError_t dispatch_out_t(const DecodeArgs& a, hipStream_t st) {
   if (a.step) return launch_step_t<D, B, OutT>(a, st);
   if (a.num_groups > 0)
-    return a.fp8_kv ? launch_prefix_fp8_t<D, B, OutT>(a, st)
-                    : launch_prefix_bf16_t<D, B, OutT>(a, st);
+    return a.fp8_kv ? launch_prefix_wg_t<D, B, OutT, uint8_t>(a, st)
+                    : launch_prefix_wg_t<D, B, OutT, uint16_t>(a, st);
   if (a.bf16_in || a.fp8_kv) return launch_bf16<D, B, OutT>(a, st);
   return a.NP > 1 ? launch_f32<D, B, true, OutT>(a, st) : launch_f32<D, B, false, OutT>(a, st);
 }

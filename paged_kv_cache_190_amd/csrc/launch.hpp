@@ -109,15 +109,15 @@ struct DecodeArgs {
   float k_scale;
   float v_scale;
   // Shared prefixes (num_groups > 0; balanced): group i is sequences group_start[i] ..
-  // group_start[i+1]-1 sharing their first group_prefix_len[i] tokens. prefix_waves units of
-  // (group, KV head, chunk, block of query columns; prefix_col_tiles blocks per chunk) run beside
-  // the `waves` suffix waves: workgroups of kPrefixWgWaves waves over bf16 pools, single waves
-  // over E4M3 pools. KMAX is then the row stride of the partials (prefix chunks first).
+  // group_start[i+1]-1 sharing their first group_prefix_len[i] tokens. prefix_units units
+  // (group, KV head, chunk, block of query columns; prefix_col_blocks blocks per chunk), each a
+  // workgroup of kPrefixWgWaves waves, run beside the `waves` suffix waves. KMAX is then the row
+  // stride of the partials (prefix chunks first).
   int num_groups;
   const int32_t* group_start;
   const int32_t* group_prefix_len;
-  int prefix_waves;
-  int prefix_col_tiles;
+  int prefix_units;
+  int prefix_col_blocks;
   int prefix_chunks;
   // Fused write + decode (bf16, balanced): token s's newest K/V come from k_new / v_new when
   // slot_mapping[s] >= 0, and the same launch stores them into the pool.
@@ -127,8 +127,8 @@ struct DecodeArgs {
   const int32_t* slot_mapping;
 };
 constexpr int kPrefixChunkTokens = 256;  // tokens of the shared prefix per prefix chunk
-// Prefix-aware decode over bf16 pools: waves per workgroup, and the (member, query head) columns
-// one prefix workgroup computes (32 per wave).
+// Prefix-aware decode: waves per workgroup, and the (member, query head) columns one prefix
+// workgroup computes (32 per wave).
 constexpr int kPrefixWgWaves = 8;
 constexpr int kPrefixWgColumns = 32 * kPrefixWgWaves;
 // Waves per workgroup of the balanced split's kernels; a launch of W waves runs

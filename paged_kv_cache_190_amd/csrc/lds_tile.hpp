@@ -11,6 +11,9 @@ namespace pkv {
 // s_waitcnt immediate that waits until at most n vector-memory operations are outstanding and
 // leaves the other counters alone (gfx9 encoding: vmcnt split over bits 3:0 and 15:14).
 constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+// s_waitcnt immediate that waits for every LDS (and scalar-memory) operation and leaves the
+// vector-memory and export counters alone.
+constexpr int waitcnt_lgkm0() { return 0xF | (0x3 << 14) | (0x7 << 4); }
 
 // XOR swizzles of the 16-byte chunks of the LDS tiles, chosen so that the sixteen lanes a
 // 128-bit LDS read serves together (64 banks x 4 bytes) hit sixteen different 16-byte bank
