@@ -487,9 +487,10 @@ __device__ __forceinline__ void attend_tiles_fp8(WaveAttn<D>& st, const u32x4 (&
     for (int dt = 0; dt < DT; ++dt) st.acc[dt] = mfma16x16x32(vv[dt], pb, st.acc[dt]);
   };
 
-  // Three register sets: two tiles' loads stay in flight during each compute (an E4M3 tile is
-  // half the bytes of a bf16 one, so the bf16 loop's two-deep pipeline would keep half the
-  // bytes in flight).
+  // DEPTH register sets. With three (the plain decode), two tiles' loads stay in flight during
+  // each compute (an E4M3 tile is half the bytes of a bf16 one, so the bf16 loop's two-deep
+  // pipeline would keep half the bytes in flight); the prefix-aware kernel, held to 256 VGPRs
+  // by its eight-wave workgroups, uses two.
   constexpr int kChunkTiles = 64 * B / 32;
   if constexpr (DEPTH == 2) {
     KvTile8<D, B> ta, tb;
@@ -810,7 +811,7 @@ __device__ __forceinline__ void balanced_body(
                           : probe_tiles<D, B, false>(kpool, vpool, bt, n, g, Hkv, tb, te);
     } else if constexpr (kFp8) {
       load_q_fp8<D>(qf, q + row * D, hvalid, lg);
-      // the prefix kernel is held to 256 VGPRs: two register sets there
+      // the prefix-aware kernel is held to 256 VGPRs: two register sets there
       if constexpr (PREFIX)
         attend_tiles_fp8<D, B, 2, false>(st, qf, kpool, vpool, bt, n, g, Hkv, tb, te,
                                          scale_log2);
