@@ -67,6 +67,10 @@ GROUPED = [
     ("wide_group", 306, [(320, [330] * 40 + [321] * 40), (16, [20, 40])], 32, 8, 128, 16, ""),
     ("mixed_fp8", 305, [(64, [64, 100, 200]), (0, [5]), (512, [512, 700]), (256, [300] * 9)],
      32, 8, 128, 16, "fp8"),
+    ("b32_d64_fp8", 307, [(96, [96, 97, 400]), (0, [1, 63]), (320, [330, 900])], 16, 16, 64, 32,
+     "fp8"),
+    ("wide_group_fp8", 308, [(320, [330] * 40 + [321] * 40), (48, [50, 60])], 32, 8, 128, 16,
+     "fp8"),
 ]
 
 
