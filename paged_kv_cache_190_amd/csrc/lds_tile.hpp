@@ -20,11 +20,12 @@ constexpr int waitcnt_lgkm0() { return 0xF | (0x3 << 14) | (0x7 << 4); }
 // groups. K tiles are [32 keys][D]; their rows are read in the order krow(col) of the kernels,
 // i.e. rows {0..3, 16..19, 4..7, 20..23} for lanes 0..15 and {8..11, 24..27, 12..15, 28..31}
 // for lanes 16..31. V tiles are [D][32 keys], rows d read in order.
+// (constexpr: also callable on the host, where a test checks the layout)
 template <int D>
-__device__ __forceinline__ int kswz(int row) {
+constexpr int kswz(int row) {
   if constexpr (D == 128) return (row & 7) | ((row >> 1) & 8);       // 16 chunks per row
   else return ((row >> 1) & 3) | ((row >> 2) & 4);                   // 8 chunks, 2 rows per line
 }
-__device__ __forceinline__ int vswz(int d) { return (d >> 2) & 3; }  // 4 chunks, 4 rows per line
+constexpr int vswz(int d) { return (d >> 2) & 3; }  // 4 chunks, 4 rows per line
 
 }  // namespace pkv
